@@ -1,0 +1,125 @@
+"""Python face of the CPU oracle (``dg_oracle.c``): plain float64 reference results.
+
+TEST INFRASTRUCTURE ONLY. Only the test-suite, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package. It imports nothing from the HIP
+library package and the library imports nothing from here.
+
+Every function takes numpy arrays in the layouts of ``workloads`` (e4m3 as uint8 bits,
+FP32 scales with the A scales MN-major) and returns float64 results; rows the method does
+not compute are NaN in the returned array.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dg_oracle.c")
+_LIB = os.path.join(_HERE, "libdg_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math: IEEE float64 as written)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.dgo_e4m3_table.argtypes = [p]
+    lib.dgo_num_threads.restype = ctypes.c_int
+    lib.dgo_block_partials.argtypes = [p, p, p, i64, i64, i64]
+    lib.dgo_fp8_gemm_nt.argtypes = [p, p, i64, p, p, p, p, i64, i64, i64]
+    lib.dgo_fp8_gemm_nt.restype = ctypes.c_int
+    lib.dgo_m_grouped_fp8_gemm_nt_contiguous.argtypes = [p, p, i64, p, p, p, p, i64, i64, i64, i64]
+    lib.dgo_m_grouped_fp8_gemm_nt_contiguous.restype = ctypes.c_int
+    lib.dgo_m_grouped_fp8_gemm_nt_masked.argtypes = [p, p, i64, p, p, p, p, i64, i64, i64, i64]
+    lib.dgo_m_grouped_fp8_gemm_nt_masked.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(x: Optional[np.ndarray]):
+    return None if x is None else x.ctypes.data
+
+
+def _c(x, dtype):
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().dgo_num_threads())
+
+
+def e4m3_table() -> np.ndarray:
+    """The 256 e4m3 (OCP E4M3FN) values indexed by bit pattern, as float64."""
+    out = np.empty(256, dtype=np.float64)
+    _load().dgo_e4m3_table(out.ctypes.data)
+    return out
+
+
+def block_partials(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """P[m, n, kb] = sum over the 128-deep block kb of dec(A[m,k]) * dec(B[n,k]) (no scales)."""
+    a, b = _c(a, np.uint8), _c(b, np.uint8)
+    m, k = a.shape
+    n = b.shape[0]
+    out = np.empty((m, n, k // 128), dtype=np.float64)
+    _load().dgo_block_partials(a.ctypes.data, b.ctypes.data, out.ctypes.data, m, n, k)
+    return out
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, c=None) -> np.ndarray:
+    """D = C + A @ B.T with 1x128 A scales (MN-major ``sfa`` [K/128, ld]) and 128x128 B scales."""
+    a, sfa, b, sfb = _c(a, np.uint8), _c(sfa, np.float32), _c(b, np.uint8), _c(sfb, np.float32)
+    m, k = a.shape
+    n = b.shape[0]
+    c = None if c is None else _c(c, np.float32)
+    d = np.full((m, n), np.nan, dtype=np.float64)
+    rc = _load().dgo_fp8_gemm_nt(_ptr(a), _ptr(sfa), sfa.shape[1], _ptr(b), _ptr(sfb), _ptr(c),
+                                 _ptr(d), m, n, k)
+    if rc != 0:
+        raise ValueError("oracle: unsupported dense shape")
+    return d
+
+
+def m_grouped_contiguous(a, sfa, b, sfb, m_indices) -> np.ndarray:
+    a, sfa, b, sfb = _c(a, np.uint8), _c(sfa, np.float32), _c(b, np.uint8), _c(sfb, np.float32)
+    m_indices = _c(m_indices, np.int32)
+    m_total, k = a.shape
+    g, n, _ = b.shape
+    d = np.full((m_total, n), np.nan, dtype=np.float64)
+    rc = _load().dgo_m_grouped_fp8_gemm_nt_contiguous(_ptr(a), _ptr(sfa), sfa.shape[1], _ptr(b),
+                                                      _ptr(sfb), _ptr(d), _ptr(m_indices),
+                                                      m_total, n, k, g)
+    if rc != 0:
+        raise ValueError("oracle: unsupported contiguous shape")
+    return d
+
+
+def m_grouped_masked(a, sfa, b, sfb, masked_m) -> np.ndarray:
+    a, sfa, b, sfb = _c(a, np.uint8), _c(sfa, np.float32), _c(b, np.uint8), _c(sfb, np.float32)
+    masked_m = _c(masked_m, np.int32)
+    g, m_max, k = a.shape
+    n = b.shape[1]
+    d = np.full((g, m_max, n), np.nan, dtype=np.float64)
+    rc = _load().dgo_m_grouped_fp8_gemm_nt_masked(_ptr(a), _ptr(sfa), sfa.shape[2], _ptr(b),
+                                                  _ptr(sfb), _ptr(d), _ptr(masked_m), g, m_max,
+                                                  n, k)
+    if rc != 0:
+        raise ValueError("oracle: unsupported masked shape")
+    return d

@@ -1,0 +1,270 @@
+"""Seeded synthetic inputs for the fine-grained-scaled FP8 GEMM and its M-grouped forms.
+
+This module is shared by the CPU oracle's tests and by the HIP path's tests and bench.
+It holds none of the GEMM's arithmetic: only random draws (numpy ``default_rng``), the
+per-segment amax/448 FP8 cast that the DeepGEMM pages leave to the caller (pt.news.hada.io
+page, "Interface GEMM e restrições de layout": casting to FP8 and transposition are the
+user's job), and the assembly of the documented memory layouts.
+
+Layouts produced (all row-major numpy arrays, bytes for e4m3):
+  A    uint8 [M, K]            e4m3 bits, K contiguous ("not transposed")
+  sfa  float32 [K/128, ld]     one FP32 scale per 1x128 row segment, stored MN-major
+                               ("transposed" LHS scale), ld = ceil(M/4)*4
+  B    uint8 [N, K]            e4m3 bits (B.T is column-major)
+  sfb  float32 [ceil(N/128), K/128]   one FP32 scale per 128x128 block
+  C    float32 [M, N] or None
+Grouped forms add a leading group axis to B/sfb (and to A/sfa for the masked layout).
+
+Quantisation recipe (input preparation, not a parity question: both sides read the same
+bytes): scale = max(amax, 1e-4) / 448 over the segment/block, q = clip(x / scale, +-448)
+rounded to nearest-even e4m3 (OCP E4M3FN) by torch's float8_e4m3fn cast.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_NAN = 0x7F            # OCP E4M3FN NaN bit pattern (S.1111.111)
+BF16_SENTINEL = 0x7FC1     # a bf16 NaN payload never produced by a rounding; marks "untouched"
+BLOCK = 128                # K block / B block edge / contiguous-layout M alignment
+AMAX_FLOOR = 1e-4
+
+
+def sf_aligned(m: int) -> int:
+    """Leading dimension of the MN-major A-scale array: rows padded to 4 floats (16 bytes)."""
+    return (m + 3) // 4 * 4
+
+
+def to_e4m3_bits(y: np.ndarray) -> np.ndarray:
+    """Round float32 values already inside [-448, 448] to e4m3 bit patterns (uint8)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _cast(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    y = np.clip(x / scale, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return to_e4m3_bits(y)
+
+
+def quantize_rows(x: np.ndarray, seg_mult: Optional[np.ndarray] = None):
+    """1x128 row-segment cast. x: float32 [M, K] -> (bits uint8 [M, K], scales float32 [M, K/128]).
+
+    ``seg_mult`` (float32 [M, K/128]) multiplies each segment before the cast (stress inputs).
+    """
+    m, k = x.shape
+    assert k % BLOCK == 0
+    kb = k // BLOCK
+    xs = x.reshape(m, kb, BLOCK)
+    if seg_mult is not None:
+        xs = xs * seg_mult[:, :, None].astype(np.float32)
+    amax = np.abs(xs).max(axis=2)
+    scale = (np.maximum(amax, AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+    bits = _cast(xs, scale[:, :, None]).reshape(m, k)
+    return bits, scale
+
+
+def quantize_blocks(x: np.ndarray, blk_mult: Optional[np.ndarray] = None):
+    """128x128 block cast. x: float32 [N, K] -> (bits uint8 [N, K], scales float32 [ceil(N/128), K/128]).
+
+    The last block row may be partial (N % 128 != 0): its amax is over the rows that exist.
+    """
+    n, k = x.shape
+    assert k % BLOCK == 0
+    kb = k // BLOCK
+    nb = (n + BLOCK - 1) // BLOCK
+    bits = np.empty((n, k), dtype=np.uint8)
+    scale = np.empty((nb, kb), dtype=np.float32)
+    for i in range(nb):
+        rows = x[i * BLOCK:(i + 1) * BLOCK].reshape(-1, kb, BLOCK)
+        if blk_mult is not None:
+            rows = rows * blk_mult[i][None, :, None].astype(np.float32)
+        amax = np.abs(rows).max(axis=(0, 2))
+        s = (np.maximum(amax, AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+        scale[i] = s
+        bits[i * BLOCK:(i + 1) * BLOCK] = _cast(rows, s[None, :, None]).reshape(-1, k)
+    return bits, scale
+
+
+def mn_major(scales_mk: np.ndarray, ld: Optional[int] = None) -> np.ndarray:
+    """[M, K/128] row scales -> MN-major [K/128, ld] (zero in the padding columns)."""
+    m, kb = scales_mk.shape
+    ld = sf_aligned(m) if ld is None else ld
+    out = np.zeros((kb, ld), dtype=np.float32)
+    out[:, :m] = scales_mk.T
+    return out
+
+
+def _pow2_mult(rng: np.random.Generator, shape) -> np.ndarray:
+    return np.exp2(rng.integers(-8, 9, size=shape)).astype(np.float32)
+
+
+@dataclasses.dataclass
+class Dense:
+    a: np.ndarray
+    sfa: np.ndarray          # [K/128, ld]
+    b: np.ndarray
+    sfb: np.ndarray
+    c: Optional[np.ndarray]
+    m: int
+    n: int
+    k: int
+
+
+def make_dense(m: int, n: int, k: int, seed: int = 0, with_c: bool = False,
+               c_std: float = 0.1, stress: bool = False) -> Dense:
+    """Dense problem; draw order A, B, C, then (stress) segment and block multipliers."""
+    rng = np.random.default_rng(seed)
+    xa = rng.standard_normal((m, k), dtype=np.float32)
+    xb = rng.standard_normal((n, k), dtype=np.float32)
+    c = (rng.standard_normal((m, n), dtype=np.float32) * np.float32(c_std)) if with_c else None
+    seg = blk = None
+    if stress:
+        seg = _pow2_mult(rng, (m, k // BLOCK))
+        blk = _pow2_mult(rng, ((n + BLOCK - 1) // BLOCK, k // BLOCK))
+    a, sa = quantize_rows(xa, seg)
+    b, sb = quantize_blocks(xb, blk)
+    return Dense(a=a, sfa=mn_major(sa), b=b, sfb=sb, c=c, m=m, n=n, k=k)
+
+
+@dataclasses.dataclass
+class Contiguous:
+    a: np.ndarray            # [M_total, K]
+    sfa: np.ndarray          # [K/128, ld >= M_total]
+    b: np.ndarray            # [G, N, K]
+    sfb: np.ndarray          # [G, ceil(N/128), K/128]
+    m_indices: np.ndarray    # int32 [M_total], -1 on padding rows
+    counts: np.ndarray       # valid rows per group
+    m_total: int
+    n: int
+    k: int
+    num_groups: int
+
+
+def make_contiguous(num_groups: int, total_rows: int, n: int, k: int, seed: int = 0,
+                    counts=None, stress: bool = False, pad_nan: bool = False) -> Contiguous:
+    """Contiguous M-grouped layout.
+
+    Draw order: the ``total_rows`` valid token rows of A, then B for every group, then the
+    routing p ~ Dirichlet(1), counts ~ Multinomial(total_rows, p) (unless ``counts`` is given),
+    then (stress) multipliers. Rows are placed group after group; each group's segment is
+    padded with rows of index -1 to a multiple of 128. Padding rows of A hold 0 (or the e4m3
+    NaN pattern when ``pad_nan``) and scale 1 (NaN when ``pad_nan``).
+    """
+    rng = np.random.default_rng(seed)
+    xa = rng.standard_normal((total_rows, k), dtype=np.float32)
+    xb = rng.standard_normal((num_groups, n, k), dtype=np.float32)
+    if counts is None:
+        p = rng.dirichlet(np.ones(num_groups))
+        counts = rng.multinomial(total_rows, p)
+    counts = np.asarray(counts, dtype=np.int64)
+    assert counts.sum() == total_rows
+    seg = blk = None
+    nb = (n + BLOCK - 1) // BLOCK
+    if stress:
+        seg = _pow2_mult(rng, (total_rows, k // BLOCK))
+        # a distinct power-of-two magnitude per group, so a misrouted row is a >= 2x error
+        gmag = np.exp2(np.arange(num_groups) % 5 - 2).astype(np.float32)
+        blk = _pow2_mult(rng, (num_groups, nb, k // BLOCK)) * gmag[:, None, None]
+    qa, sa = quantize_rows(xa, seg)
+    padded = (counts + BLOCK - 1) // BLOCK * BLOCK
+    m_total = int(padded.sum())
+    a = np.full((m_total, k), E4M3_NAN if pad_nan else 0, dtype=np.uint8)
+    sa_full = np.full((m_total, k // BLOCK), np.nan if pad_nan else 1.0, dtype=np.float32)
+    m_indices = np.full(m_total, -1, dtype=np.int32)
+    src = dst = 0
+    for g in range(num_groups):
+        cnt = int(counts[g])
+        a[dst:dst + cnt] = qa[src:src + cnt]
+        sa_full[dst:dst + cnt] = sa[src:src + cnt]
+        m_indices[dst:dst + cnt] = g
+        src += cnt
+        dst += int(padded[g])
+    b = np.empty((num_groups, n, k), dtype=np.uint8)
+    sfb = np.empty((num_groups, nb, k // BLOCK), dtype=np.float32)
+    for g in range(num_groups):
+        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g])
+    return Contiguous(a=a, sfa=mn_major(sa_full), b=b, sfb=sfb, m_indices=m_indices,
+                      counts=counts, m_total=m_total, n=n, k=k, num_groups=num_groups)
+
+
+@dataclasses.dataclass
+class Masked:
+    a: np.ndarray            # [G, M_max, K]
+    sfa: np.ndarray          # [G, K/128, ld >= M_max]
+    b: np.ndarray            # [G, N, K]
+    sfb: np.ndarray          # [G, ceil(N/128), K/128]
+    masked_m: np.ndarray     # int32 [G]
+    num_groups: int
+    m_max: int
+    n: int
+    k: int
+
+
+def masked_counts(num_groups: int, m_max: int, seed: int, replay: Optional[int] = None) -> np.ndarray:
+    """masked_m ~ U{0..m_max} per group (inclusive). Replay r draws from default_rng((seed, r))."""
+    rng = np.random.default_rng(seed if replay is None else (seed, replay))
+    return rng.integers(0, m_max + 1, size=num_groups).astype(np.int32)
+
+
+def make_masked(num_groups: int, m_max: int, n: int, k: int, seed: int = 0,
+                masked_m=None, stress: bool = False, tail_nan: bool = False) -> Masked:
+    """Masked M-grouped layout. Draw order: A [G, M_max, K], B [G, N, K], masked_m, (stress).
+
+    Every row of A is drawn; rows at or beyond masked_m[g] are ignored by the method and are
+    replaced by the e4m3 NaN pattern (scale NaN) when ``tail_nan``.
+    """
+    rng = np.random.default_rng(seed)
+    xa = rng.standard_normal((num_groups, m_max, k), dtype=np.float32)
+    xb = rng.standard_normal((num_groups, n, k), dtype=np.float32)
+    mm = rng.integers(0, m_max + 1, size=num_groups).astype(np.int32)
+    if masked_m is not None:
+        mm = np.asarray(masked_m, dtype=np.int32)
+    nb = (n + BLOCK - 1) // BLOCK
+    seg = blk = None
+    if stress:
+        seg = _pow2_mult(rng, (num_groups, m_max, k // BLOCK))
+        gmag = np.exp2(np.arange(num_groups) % 5 - 2).astype(np.float32)
+        blk = _pow2_mult(rng, (num_groups, nb, k // BLOCK)) * gmag[:, None, None]
+    ld = sf_aligned(m_max)
+    a = np.empty((num_groups, m_max, k), dtype=np.uint8)
+    sfa = np.zeros((num_groups, k // BLOCK, ld), dtype=np.float32)
+    b = np.empty((num_groups, n, k), dtype=np.uint8)
+    sfb = np.empty((num_groups, nb, k // BLOCK), dtype=np.float32)
+    for g in range(num_groups):
+        a[g], sa = quantize_rows(xa[g], None if seg is None else seg[g])
+        sfa[g] = mn_major(sa, ld)
+        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g])
+        if tail_nan:
+            lim = min(max(int(mm[g]), 0), m_max)
+            a[g, lim:] = E4M3_NAN
+            sfa[g, :, lim:m_max] = np.nan
+    return Masked(a=a, sfa=sfa, b=b, sfb=sfb, masked_m=mm, num_groups=num_groups,
+                  m_max=m_max, n=n, k=k)
+
+
+# The five workloads the library is measured and checked on (sizes from the method's
+# DeepSeek-V3/R1 inference shapes: hidden 7168, MoE intermediate 2048/4096, 2112-wide
+# low-rank projections).
+CONFIGS = {
+    "dense_small": dict(kind="dense", m=128, n=256, k=512, with_c=False),
+    "dense_prefill": dict(kind="dense", m=4096, n=7168, k=2048, with_c=True),
+    "dense_skinny": dict(kind="dense", m=64, n=2112, k=7168, with_c=False),
+    "moe_contiguous": dict(kind="contiguous", num_groups=8, total_rows=32768, n=4096, k=7168),
+    "moe_masked": dict(kind="masked", num_groups=16, m_max=256, n=7168, k=2048),
+}
+
+
+def make_config(name: str, seed: int = 0, **overrides):
+    cfg = dict(CONFIGS[name])
+    cfg.update(overrides)
+    kind = cfg.pop("kind")
+    if kind == "dense":
+        return make_dense(seed=seed, **cfg)
+    if kind == "contiguous":
+        return make_contiguous(seed=seed, **cfg)
+    return make_masked(seed=seed, **cfg)
