@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Throughput of the fine-grained-scaled FP8 GEMM library on one MI355X.
+
+One step = one call of the library's hot path on one batch of seeded synthetic input that
+is already resident in device memory.  The headline workload is the dense prefill GEMM
+M=4096 N=7168 K=2048 with an FP32 C (D = C + A @ B.T, bf16 D); the other workloads (small
+dense, skinny dense, contiguous MoE, masked MoE replayed from a captured graph) are timed
+too and reported under "workloads".  Inputs rotate over several device-resident copies whose
+total exceeds the 256 MB Infinity Cache, so every launch reads its operands from HBM.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOPS (and % of FP8 MFMA / HBM roofline) at 1 GPU"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+ROTATE_BYTES = 1.2e9          # total bytes of rotated input copies per workload
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("dg_gemm.hip", "dg_api.cpp", "dg_internal.h"):
+        with open(os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Case:
+    """One workload: device copies of its inputs and a launch(i) that runs step i."""
+
+    def __init__(self, name):
+        self.name = name
+        self.sets = []
+        self.config = {}
+
+    def launch(self, i):
+        raise NotImplementedError
+
+    def flops(self, i):
+        raise NotImplementedError
+
+    def bytes(self, i):
+        raise NotImplementedError
+
+
+def _dev(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _copies(torch, tensors, set_bytes):
+    n = int(min(64, max(3, math.ceil(ROTATE_BYTES / max(set_bytes, 1)))))
+    out = [tensors]
+    for _ in range(n - 1):
+        out.append({k: (None if v is None else v.clone()) for k, v in tensors.items()})
+    return out
+
+
+def make_dense_case(torch, dg, W, name):
+    p = W.make_config(name, seed=0)
+    c = Case(name)
+    t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
+             c=None if p.c is None else _dev(torch, p.c),
+             d=torch.empty(p.m, p.n, dtype=torch.bfloat16, device="cuda"))
+    kb, nb = p.k // 128, (p.n + 127) // 128
+    nbytes = (p.m * p.k + p.n * p.k + 4 * p.m * kb + 4 * nb * kb + 2 * p.m * p.n
+              + (4 * p.m * p.n if p.c is not None else 0))
+    c.sets = _copies(torch, t, nbytes)
+    c.config = dict(workload=name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
+                    d="bf16", rotating_copies=len(c.sets))
+
+    def launch(i):
+        s = c.sets[i % len(c.sets)]
+        dg.fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["c"])
+
+    c.launch = launch
+    c.flops = lambda i: 2.0 * p.m * p.n * p.k
+    c.bytes = lambda i: float(nbytes)
+    c.problem = p
+    return c
+
+
+def make_contiguous_case(torch, dg, W):
+    p = W.make_config("moe_contiguous", seed=0)
+    c = Case("moe_contiguous")
+    t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
+             idx=_dev(torch, p.m_indices),
+             d=torch.empty(p.m_total, p.n, dtype=torch.bfloat16, device="cuda"))
+    kb, nb = p.k // 128, (p.n + 127) // 128
+    valid = int(p.counts.sum())
+    used = int((p.counts > 0).sum())
+    nbytes = (valid * p.k + used * p.n * p.k + 4 * valid * kb + 4 * used * nb * kb
+              + 2 * valid * p.n + 4 * p.m_total)
+    c.sets = _copies(torch, t, nbytes)
+    c.config = dict(workload="moe_contiguous", groups=p.num_groups, valid_rows=valid,
+                    padded_rows=p.m_total, n=p.n, k=p.k, rotating_copies=len(c.sets))
+
+    def launch(i):
+        s = c.sets[i % len(c.sets)]
+        dg.m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["idx"])
+
+    c.launch = launch
+    c.flops = lambda i: 2.0 * valid * p.n * p.k
+    c.bytes = lambda i: float(nbytes)
+    return c
+
+
+def make_masked_case(torch, dg, W):
+    p = W.make_config("moe_masked", seed=0)
+    c = Case("moe_masked")
+    g, m_max, n, k = p.num_groups, p.m_max, p.n, p.k
+    t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
+             mm=_dev(torch, p.masked_m),
+             d=torch.empty(g, m_max, n, dtype=torch.bfloat16, device="cuda"))
+    kb, nb = k // 128, (n + 127) // 128
+    set_bytes = g * m_max * k + g * n * k + 2 * g * m_max * n
+    c.sets = _copies(torch, t, set_bytes)
+    table = [W.masked_counts(g, m_max, seed=0, replay=r) for r in range(16)]
+    table_dev = [_dev(torch, x) for x in table]
+    graphs = []
+    for s in c.sets:                      # one captured graph per input copy
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dg.m_grouped_fp8_gemm_nt_masked(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"])
+        torch.cuda.current_stream().wait_stream(side)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            dg.m_grouped_fp8_gemm_nt_masked(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"])
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    c.config = dict(workload="moe_masked", groups=g, m_max=m_max, n=n, k=k,
+                    masked_m="U{0..256} per group, a new draw per replay (16 draws)",
+                    launched_as="captured graph replay", rotating_copies=len(c.sets))
+
+    def prepare(i):
+        s = c.sets[i % len(c.sets)]
+        s["mm"].copy_(table_dev[i % len(table)])   # device-side update between replays
+
+    def launch(i):
+        graphs[i % len(graphs)].replay()
+
+    def flops(i):
+        return 2.0 * float(table[i % len(table)].sum()) * n * k
+
+    def nbytes(i):
+        mm = table[i % len(table)]
+        rows = float(mm.sum())
+        used = float((mm > 0).sum())
+        return (rows * k + used * n * k + 4 * rows * kb + 4 * used * nb * kb + 2 * rows * n + 4 * g)
+
+    c.prepare = prepare
+    c.launch = launch
+    c.flops = flops
+    c.bytes = nbytes
+    return c
+
+
+def time_case(torch, case, steps, warmup):
+    prep = getattr(case, "prepare", None)
+    for i in range(warmup):
+        if prep:
+            prep(i)
+        case.launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_all0.record()
+    for i in range(steps):
+        j = warmup + i
+        if prep:
+            prep(j)
+        ev[i][0].record()
+        case.launch(j)
+        ev[i][1].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3       # seconds per launch
+    flops = np.array([case.flops(warmup + i) for i in range(steps)])
+    nbytes = np.array([case.bytes(warmup + i) for i in range(steps)])
+    total = t_all0.elapsed_time(t_all1) * 1e-3
+    return dict(total_s=total, wall_s=wall, per_launch_s=per, flops=flops, bytes=nbytes)
+
+
+def summarize(res):
+    per = res["per_launch_s"]
+    avg = float(per.mean())
+    tflops = float(res["flops"].sum() / per.sum() / 1e12)
+    gbs = float(res["bytes"].sum() / per.sum() / 1e9)
+    return dict(avg_kernel_us=avg * 1e6, p10_us=float(np.percentile(per, 10) * 1e6),
+                p90_us=float(np.percentile(per, 90) * 1e6), tflops=tflops, hbm_gbs=gbs,
+                frac_fp8_peak=tflops / PEAK_FP8_TFLOPS, frac_hbm_peak=gbs / PEAK_HBM_GBS)
+
+
+def cpu_baseline(W, case, target_s):
+    import oracle
+    p = case.problem
+    log("timing the CPU oracle on a row sample of the workload")
+    rows = 2
+    while True:
+        t0 = time.perf_counter()
+        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(p.sfa[:, :rows].T), p.b, p.sfb,
+                           None if p.c is None else p.c[:rows])
+        dt = time.perf_counter() - t0
+        if dt >= target_s or rows >= p.m:
+            break
+        rows = int(min(p.m, max(rows * 2, rows * target_s / max(dt, 1e-3) * 1.1)))
+    flops = 2.0 * rows * p.n * p.k
+    return dict(value=flops / dt / 1e12, unit="TFLOPS", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{rows} of {p.m} rows of the {case.name} workload (all N={p.n}, K={p.k}),"
+                       f" {dt:.1f} s, float64")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_prefill",
+                    choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
+                             "moe_masked"])
+    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this library"
+              " has no multi-GPU path: each GPU would run its own shard independently)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_fp8_amd as dg
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    log(f"device {torch.cuda.get_device_name(0)}, {dg.get_num_cus()} CUs")
+
+    makers = {
+        "dense_small": lambda: make_dense_case(torch, dg, W, "dense_small"),
+        "dense_prefill": lambda: make_dense_case(torch, dg, W, "dense_prefill"),
+        "dense_skinny": lambda: make_dense_case(torch, dg, W, "dense_skinny"),
+        "moe_contiguous": lambda: make_contiguous_case(torch, dg, W),
+        "moe_masked": lambda: make_masked_case(torch, dg, W),
+    }
+    order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
+    results = {}
+    head = None
+    for name in order:
+        log(f"preparing {name}")
+        case = makers[name]()
+        steps = args.steps if name == args.workload else max(20, args.steps // 2)
+        log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
+        res = time_case(torch, case, steps, args.warmup)
+        summ = summarize(res)
+        summ["config"] = case.config
+        results[name] = summ
+        log(f"{name}: {summ['avg_kernel_us']:.1f} us/launch, {summ['tflops']:.1f} TFLOPS, "
+            f"{summ['hbm_gbs']:.0f} GB/s")
+        if name == args.workload:
+            head = (case, res, summ, steps)
+        else:
+            del case
+            torch.cuda.empty_cache()
+
+    case, res, summ, steps = head
+    total_flops = float(res["flops"].sum())
+    value = total_flops / res["total_s"] / 1e12
+    dom = case.name
+    traffic = measured_traffic(dom)
+    achieved = summ["tflops"]
+    roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_FP8_TFLOPS, traffic=traffic,
+                    kernel_avg_us=summ["avg_kernel_us"], hbm_gbs_algorithmic=summ["hbm_gbs"],
+                    hbm_frac_algorithmic=summ["hbm_gbs"] / PEAK_HBM_GBS)
+    if dom in ("dense_skinny", "moe_masked"):
+        roofline.update(bound="hbm", achieved=summ["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=summ["hbm_gbs"] / PEAK_HBM_GBS)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["total_s"] / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic (seeded N(0,1) cast to e4m3 with 1x128 / 128x128 FP32 scales)",
+        "config": case.config,
+        "roofline": roofline,
+        "workloads": results,
+    }
+    if not args.no_cpu and hasattr(case, "problem"):
+        out["cpu_baseline"] = cpu_baseline(W, case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * dg.h — C ABI of the MI355X (gfx950) fine-grained-scaled FP8 GEMM library (libdg.so).
+ *
+ * The operation (DeepGEMM pages: pt.news.hada.io, "Interface GEMM e restrições de layout"
+ * and "GEMM denso e grouped"; feifmx.com release article on fine-grained scaling with
+ * two-level accumulation):
+ *
+ *     D[m, n] = C[m, n] + sum_kb  sfa[m, kb] * sfb[n / 128, kb] * sum_{k in block kb} A[m, k] * B[n, k]
+ *
+ * in NT layout: A is e4m3 [M, K] row-major (K contiguous), B is e4m3 [N, K] row-major, so
+ * B.T is column-major.  One FP32 scale per 1x128 segment of an A row, stored transposed
+ * (MN-major): sfa[m, kb] lives at sfa[kb * ld_sfa + m].  One FP32 scale per 128x128 block of
+ * B: sfb[nb, kb] at sfb[nb * (K/128) + kb], nb = n / 128 (ceil(N/128) block rows; the last
+ * one may cover fewer than 128 rows).  D is bf16 [M, N] row-major, rounded to nearest-even
+ * from the FP32 accumulator.  C is an optional FP32 [M, N] row-major accumulator.
+ * e4m3 is the OCP E4M3FN encoding (max normal 448, S.1111.111 = NaN).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library never frees or
+ *    retains them and never allocates on their behalf.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
+ *    synchronize the host.  Argument checks happen on the host before any HIP call.
+ *  - Return value: DG_OK (0) or a negative dg_status.  dg_last_error() then holds a message
+ *    (thread-local).  A launch failure reported by the HIP runtime returns DG_ERR_HIP.
+ *  - Preconditions: K > 0 and K % 128 == 0; N > 0 and N % 16 == 0; row counts >= 0 (zero
+ *    rows is a no-op that returns DG_OK without touching the device); ld_sfa % 4 == 0 and
+ *    ld_sfa >= the number of A rows; A, B, D and C 16-byte aligned; sfa, sfb 4-byte aligned.
+ *  - Values in device memory cannot be checked without a synchronization, so their
+ *    behaviour is defined instead (see each call).
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, ld_sfa too small     */
+    DG_ERR_UNSUPPORTED = -2, /* a shape outside the preconditions (K % 128, N % 16, ...)  */
+    DG_ERR_MISALIGNED = -3,  /* a pointer or leading dimension breaks the alignment rules */
+    DG_ERR_HIP = -4          /* the HIP runtime reported an error (no device, launch...)   */
+} dg_status;
+
+/*
+ * Dense NT GEMM: D = C + A @ B.T (pt.news.hada.io, "Interface GEMM e restrições de layout":
+ * fp8_gemm_nt computes D = C + A @ B.T; NT layout; LHS scale FP32, transposed).
+ *   a      e4m3 [m, k]
+ *   sfa    FP32 [k/128][ld_sfa], element (row, kb) at kb*ld_sfa + row, ld_sfa >= m
+ *   b      e4m3 [n, k]
+ *   sfb    FP32 [ceil(n/128)][k/128]
+ *   c      FP32 [m, n] or NULL (then C = 0); must not overlap d
+ *   d      bf16 [m, n], written in full
+ * Skinny shapes may split K across workgroups; the partial sums then go through a
+ * library-owned workspace (allocated once per device on first use, outside stream capture)
+ * and are reduced in a fixed order, so results are deterministic.  Concurrent calls on
+ * different streams of one device that both split K share that workspace and must not
+ * overlap in time.
+ */
+int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k,
+                   void *stream);
+
+/*
+ * M-grouped GEMM, contiguous layout (pt.news.hada.io, "GEMM denso e grouped": experts share
+ * N and K; their token rows are concatenated along M; each expert segment is aligned to the
+ * M block, whose size dg_get_mk_alignment_for_contiguous_layout() returns).
+ *   a          e4m3 [m_total, k], m_total % 128 == 0
+ *   sfa        FP32 [k/128][ld_sfa], ld_sfa >= m_total
+ *   b          e4m3 [num_groups, n, k]
+ *   sfb        FP32 [num_groups][ceil(n/128)][k/128]
+ *   d          bf16 [m_total, n]
+ *   m_indices  device int32 [m_total]: the group of each row; -1 marks a padding row
+ * Row r is computed with B[m_indices[r]] and written to D; rows whose index is outside
+ * [0, num_groups) are neither read into any result nor written (D keeps its old contents).
+ * Each aligned 128-row block must hold rows of at most one group (padding aside); a block
+ * mixing two groups computes only the rows of the largest group index in it.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,
+                                        const void *b, const float *sfb, void *d,
+                                        const int32_t *m_indices, int m_total, int n, int k,
+                                        int num_groups, void *stream);
+
+/*
+ * M-grouped GEMM, masked layout (pt.news.hada.io, "GEMM denso e grouped": for decoding under
+ * graph capture, when the host does not know the per-expert token counts, a mask tensor
+ * tells the kernel which region is valid and only that region is computed).
+ *   a         e4m3 [num_groups, m_max, k]
+ *   sfa       FP32 [num_groups][k/128][ld_sfa], ld_sfa >= m_max
+ *   b         e4m3 [num_groups, n, k]
+ *   sfb       FP32 [num_groups][ceil(n/128)][k/128]
+ *   d         bf16 [num_groups, m_max, n]
+ *   masked_m  device int32 [num_groups]: valid rows of each group, read on the device at run
+ *             time (clamped to [0, m_max]); rows at or beyond it are not written
+ *   expected_m  host hint of the typical valid-row count for the tile choice (<= 0: m_max/2)
+ * The call performs no allocation, no host synchronization and no host read of device
+ * memory, so it can be captured in a hipGraph and replayed after masked_m is rewritten.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_sfa,
+                                    const void *b, const float *sfb, void *d,
+                                    const int32_t *masked_m, int num_groups, int m_max, int n,
+                                    int k, int expected_m, void *stream);
+
+/* Row alignment of each group segment in the contiguous layout: 128 (the M block size). */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/* Smallest valid ld_sfa for m rows: m rounded up to a multiple of 4 (16-byte columns). */
+int64_t dg_get_sf_aligned_m(int64_t m);
+
+/* Cap (n > 0) or reset (n <= 0) the number of compute units the tile heuristic plans for;
+ * returns the previous cap (0 = none).  Mirrors the pages' set_num_sms / get_num_sms. */
+int dg_set_num_cus(int n);
+
+/* Compute units the heuristic plans for on the current device (the cap if set), or a
+ * negative dg_status if no device is available. */
+int dg_get_num_cus(void);
+
+/* Message for the most recent non-OK return on this thread ("" if none). */
+const char *dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

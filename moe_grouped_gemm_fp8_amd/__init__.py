@@ -1,0 +1,181 @@
+"""Python binding of libdg.so: the fine-grained-scaled FP8 GEMM for MI355X (gfx950).
+
+Thin marshalling over the C ABI declared in ``include/dg.h``: it checks that the tensors'
+shapes agree with each other (so the kernels' index ranges match the memory handed over),
+passes raw device pointers and the current HIP stream, and turns a non-zero status into an
+exception.  Every step of the computation runs in the HIP kernels; there is no fallback.
+
+Operation (DeepGEMM pages, pt.news.hada.io, "Interface GEMM e restrições de layout"):
+D = C + A @ B.T, A e4m3 [M, K] with FP32 scales per 1x128 row segment stored MN-major as
+``sfa`` [K/128, ld], B e4m3 [N, K] with FP32 scales per 128x128 block ``sfb``
+[ceil(N/128), K/128], D bf16, C optional FP32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "get_mk_alignment_for_contiguous_layout", "get_sf_aligned_m", "set_num_cus", "get_num_cus",
+    "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdg.so")
+_lib = None
+
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+class DGError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"dg error {code}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python -m moe_grouped_gemm_fp8_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.dg_fp8_gemm_nt.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.dg_fp8_gemm_nt.restype = i32
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32,
+                                                        i32, i32, vp]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = i32
+    lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32,
+                                                    i32, i32, vp]
+    lib.dg_m_grouped_fp8_gemm_nt_masked.restype = i32
+    lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
+    lib.dg_get_sf_aligned_m.argtypes = [i64]
+    lib.dg_get_sf_aligned_m.restype = i64
+    lib.dg_set_num_cus.argtypes = [i32]
+    lib.dg_set_num_cus.restype = i32
+    lib.dg_get_num_cus.restype = i32
+    lib.dg_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DGError(rc, _load().dg_last_error().decode(errors="replace"))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: int):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dtype in (dtypes if isinstance(dtypes, tuple) else (dtypes,)),
+          f"{name} has dtype {t.dtype}")
+    _need(t.dim() == ndim, f"{name} must have {ndim} dims, has shape {tuple(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """D = C + A @ B.T.  a [M,K] e4m3, sfa [K/128, ld>=M] f32, b [N,K] e4m3,
+    sfb [ceil(N/128), K/128] f32, d [M,N] bf16 (written), c [M,N] f32 or None."""
+    pa = _dev(a, "a", _FP8_DTYPES, 2)
+    m, k = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 2)
+    n = b.shape[0]
+    _need(b.shape[1] == k, "a and b disagree on K")
+    psfa = _dev(sfa, "sfa", torch.float32, 2)
+    _need(sfa.shape[0] * 128 == k, "sfa must be [K/128, ld]")
+    psfb = _dev(sfb, "sfb", torch.float32, 2)
+    _need(tuple(sfb.shape) == ((n + 127) // 128, k // 128), "sfb must be [ceil(N/128), K/128]")
+    pd = _dev(d, "d", torch.bfloat16, 2)
+    _need(tuple(d.shape) == (m, n), "d must be [M, N]")
+    pc = None
+    if c is not None:
+        pc = _dev(c, "c", torch.float32, 2)
+        _need(tuple(c.shape) == (m, n), "c must be [M, N]")
+    _check(_load().dg_fp8_gemm_nt(pa, psfa, sfa.shape[1], pb, psfb, pc, pd, m, n, k,
+                                  _stream(stream)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, stream=None):
+    """Contiguous M-grouped GEMM.  a [M_total,K], sfa [K/128, ld>=M_total], b [G,N,K],
+    sfb [G, ceil(N/128), K/128], d [M_total,N] bf16, m_indices int32 [M_total] (-1 = padding)."""
+    pa = _dev(a, "a", _FP8_DTYPES, 2)
+    m_total, k = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 3)
+    g, n, kb_ = b.shape
+    _need(kb_ == k, "a and b disagree on K")
+    psfa = _dev(sfa, "sfa", torch.float32, 2)
+    _need(sfa.shape[0] * 128 == k, "sfa must be [K/128, ld]")
+    psfb = _dev(sfb, "sfb", torch.float32, 3)
+    _need(tuple(sfb.shape) == (g, (n + 127) // 128, k // 128), "sfb must be [G, ceil(N/128), K/128]")
+    pd = _dev(d, "d", torch.bfloat16, 2)
+    _need(tuple(d.shape) == (m_total, n), "d must be [M_total, N]")
+    pi = _dev(m_indices, "m_indices", torch.int32, 1)
+    _need(m_indices.shape[0] == m_total, "m_indices must be [M_total]")
+    _check(_load().dg_m_grouped_fp8_gemm_nt_contiguous(pa, psfa, sfa.shape[1], pb, psfb, pd, pi,
+                                                       m_total, n, k, g, _stream(stream)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
+    """Masked M-grouped GEMM.  a [G,M_max,K], sfa [G, K/128, ld>=M_max], b [G,N,K],
+    sfb [G, ceil(N/128), K/128], d [G,M_max,N] bf16, masked_m int32 [G] on the device."""
+    pa = _dev(a, "a", _FP8_DTYPES, 3)
+    g, m_max, k = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 3)
+    _need(b.shape[0] == g and b.shape[2] == k, "a and b disagree on G or K")
+    n = b.shape[1]
+    psfa = _dev(sfa, "sfa", torch.float32, 3)
+    _need(sfa.shape[0] == g and sfa.shape[1] * 128 == k, "sfa must be [G, K/128, ld]")
+    psfb = _dev(sfb, "sfb", torch.float32, 3)
+    _need(tuple(sfb.shape) == (g, (n + 127) // 128, k // 128), "sfb must be [G, ceil(N/128), K/128]")
+    pd = _dev(d, "d", torch.bfloat16, 3)
+    _need(tuple(d.shape) == (g, m_max, n), "d must be [G, M_max, N]")
+    pm = _dev(masked_m, "masked_m", torch.int32, 1)
+    _need(masked_m.shape[0] == g, "masked_m must be [G]")
+    _check(_load().dg_m_grouped_fp8_gemm_nt_masked(pa, psfa, sfa.shape[2], pb, psfb, pd, pm, g,
+                                                   m_max, n, k, int(expected_m), _stream(stream)))
+    return d
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return int(_load().dg_get_mk_alignment_for_contiguous_layout())
+
+
+def get_sf_aligned_m(m: int) -> int:
+    return int(_load().dg_get_sf_aligned_m(int(m)))
+
+
+def set_num_cus(n: int) -> int:
+    return int(_load().dg_set_num_cus(int(n)))
+
+
+def get_num_cus() -> int:
+    v = int(_load().dg_get_num_cus())
+    if v < 0:
+        _check(v)
+    return v

@@ -1,0 +1,365 @@
+// C ABI of the FP8 GEMM library: argument validation (pure host code, no HIP call before it
+// passes), the tile-configuration heuristic, the split-K workspace, and the launches.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+int g_num_cus_cap = 0;
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return DG_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and pointer checks shared by every entry point; `rows` is the number of A rows per
+// group (m, m_total or m_max).  With zero rows A, sfa and D may be null (empty tensors).
+int check_common(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                 const float *sfb, const void *d, int64_t rows, int n, int k)
+{
+    if (!b || !sfb || (rows > 0 && (!a || !sfa || !d)))
+        return fail(DG_ERR_INVALID_ARG, "null tensor pointer");
+    if (rows < 0 || n <= 0 || k <= 0)
+        return fail(DG_ERR_INVALID_ARG, "sizes must be positive (rows=%lld n=%d k=%d)",
+                    (long long)rows, n, k);
+    if (k % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "k=%d is not a multiple of 128", k);
+    if (n % 16 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "n=%d is not a multiple of 16", n);
+    if (ld_sfa < rows)
+        return fail(DG_ERR_INVALID_ARG, "ld_sfa=%lld is smaller than the row count %lld",
+                    (long long)ld_sfa, (long long)rows);
+    if (ld_sfa % 4 != 0)
+        return fail(DG_ERR_MISALIGNED, "ld_sfa=%lld is not a multiple of 4", (long long)ld_sfa);
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16))
+        return fail(DG_ERR_MISALIGNED, "A, B and D must be 16-byte aligned");
+    if (!aligned(sfa, 4) || !aligned(sfb, 4))
+        return fail(DG_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
+    return DG_OK;
+}
+
+int device_cus(int *out)
+{
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(DG_ERR_HIP, "no HIP device available");
+    std::lock_guard<std::mutex> lk(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            cus <= 0)
+            return fail(DG_ERR_HIP, "cannot query the compute-unit count");
+        cached[dev] = cus;
+    }
+    *out = cached[dev];
+    if (g_num_cus_cap > 0 && g_num_cus_cap < *out)
+        *out = g_num_cus_cap;
+    return DG_OK;
+}
+
+// Split-K workspace: one per device, allocated on the first call that needs it while the
+// stream is not being captured, then reused.  Counters start at zero (hipMemset at
+// allocation) and every reduction resets its own counter.
+struct Workspace {
+    float *partials = nullptr;
+    int *counters = nullptr;
+    size_t partial_floats = 0;
+    int counter_count = 0;
+};
+constexpr size_t kWsFloats = size_t(16) << 20;  // 64 MiB of FP32 partial tiles
+constexpr int kWsCounters = 1 << 16;
+
+int get_workspace(hipStream_t stream, Workspace **out)
+{
+    static std::mutex mu;
+    static Workspace ws[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(DG_ERR_HIP, "no HIP device available");
+    std::lock_guard<std::mutex> lk(mu);
+    Workspace &w = ws[dev];
+    if (!w.partials) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            *out = nullptr;  // caller falls back to a configuration without split-K
+            return DG_OK;
+        }
+        if (hipMalloc(&w.partials, kWsFloats * sizeof(float)) != hipSuccess)
+            return fail(DG_ERR_HIP, "split-K workspace allocation failed");
+        if (hipMalloc(&w.counters, kWsCounters * sizeof(int)) != hipSuccess ||
+            hipMemset(w.counters, 0, kWsCounters * sizeof(int)) != hipSuccess) {
+            (void)hipFree(w.partials);
+            w.partials = nullptr;
+            return fail(DG_ERR_HIP, "split-K counter allocation failed");
+        }
+        w.partial_floats = kWsFloats;
+        w.counter_count = kWsCounters;
+    }
+    *out = &w;
+    return DG_OK;
+}
+
+int forced_config()
+{
+    const char *s = getenv("DG_FORCE_CONFIG");
+    if (!s || !*s)
+        return -1;
+    for (int c = 0; c < dg::CFG_COUNT; ++c)
+        if (strcmp(s, dg::kTiles[c].name) == 0)
+            return c;
+    return -1;
+}
+
+int forced_splits()
+{
+    const char *s = getenv("DG_FORCE_SPLITS");
+    return (s && *s) ? atoi(s) : 0;
+}
+
+void print_config(const char *what, int m, int n, int k, int g, int cfg, int splits)
+{
+    static std::mutex mu;
+    static std::set<std::tuple<std::string, int, int, int, int>> seen;
+    const char *env = getenv("DG_PRINT_CONFIGS");
+    if (!env || !*env || *env == '0')
+        return;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!seen.insert(std::make_tuple(std::string(what), m, n, k, g)).second)
+        return;
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %s (%dx%d), splits=%d\n", what, m,
+            n, k, g, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn, splits);
+}
+
+// Estimated cost of a tile choice: waves of workgroups over the CUs times the work of one
+// tile, with a small per-tile overhead term that favours larger tiles on ties.
+double tile_cost(int bm, int bn, int64_t tiles, int cus)
+{
+    int64_t waves = (tiles + cus - 1) / cus;
+    return (double)waves * ((double)bm * bn + 64.0 * (bm + bn));
+}
+
+int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
+{
+    int64_t grid = dg::grid_size(mode, cfg, args);
+    if (grid <= 0 || grid > 0x7fffffff)
+        return fail(DG_ERR_UNSUPPORTED, "problem too large for one launch (%lld workgroups)",
+                    (long long)grid);
+    hipError_t e = dg::launch_gemm(mode, cfg, args, stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m, n, k);
+    if (rc != DG_OK)
+        return rc;
+    if (m == 0)
+        return ok();  // empty problem: nothing to write
+    if (c && !aligned(c, 16))
+        return fail(DG_ERR_MISALIGNED, "C must be 16-byte aligned");
+    if (c && (const void *)c == d)
+        return fail(DG_ERR_INVALID_ARG, "C and D must not alias");
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != DG_OK)
+        return rc;
+    hipStream_t s = (hipStream_t)stream;
+
+    const int kb = k / 128;
+    int cfg = forced_config();
+    int splits = 1;
+    if (cfg < 0) {
+        if (m <= 64) {
+            cfg = dg::CFG_64x32;
+        } else {
+            const int cands[] = {dg::CFG_256x224, dg::CFG_128x256, dg::CFG_128x128};
+            double best = 0;
+            for (int cnd : cands) {
+                const dg::TileInfo &t = dg::kTiles[cnd];
+                int64_t tiles = (int64_t)((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
+                double cost = tile_cost(t.bm, t.bn, tiles, cus);
+                if (cfg < 0 || cost < best) {
+                    best = cost;
+                    cfg = cnd;
+                }
+            }
+        }
+    }
+    const dg::TileInfo &ti = dg::kTiles[cfg];
+    const int64_t tiles = (int64_t)((m + ti.bm - 1) / ti.bm) * ((n + ti.bn - 1) / ti.bn);
+    // split K when the tiles cannot fill the CUs; at least 4 K blocks per split
+    if (tiles < cus) {
+        splits = (int)((cus + tiles - 1) / tiles);
+        if (splits > kb / 4)
+            splits = kb / 4;
+        if (splits < 1)
+            splits = 1;
+    }
+    int fs = forced_splits();
+    if (fs > 0)
+        splits = fs > kb ? kb : fs;
+
+    dg::GemmArgs args{};
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.ld_sfa = ld_sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.c = c;
+    args.d = (uint16_t *)d;
+    args.m = m;
+    args.n = n;
+    args.k = k;
+    args.num_groups = 1;
+    args.splits = 1;
+    if (splits > 1) {
+        Workspace *w = nullptr;
+        if ((rc = get_workspace(s, &w)) != DG_OK)
+            return rc;
+        if (w && (size_t)tiles * splits * ti.bm * ti.bn <= w->partial_floats &&
+            tiles <= w->counter_count) {
+            args.splits = splits;
+            args.ws = w->partials;
+            args.counters = w->counters;
+        }
+    }
+    print_config("fp8_gemm_nt", m, n, k, 1, cfg, args.splits);
+    return launch(dg::MODE_DENSE, cfg, args, s);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,
+                                        const void *b, const float *sfb, void *d,
+                                        const int32_t *m_indices, int m_total, int n, int k,
+                                        int num_groups, void *stream)
+{
+    int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m_total, n, k);
+    if (rc != DG_OK)
+        return rc;
+    if (!m_indices)
+        return fail(DG_ERR_INVALID_ARG, "null m_indices");
+    if (num_groups <= 0)
+        return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be positive", num_groups);
+    if (m_total % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "m_total=%d is not a multiple of 128", m_total);
+    if (!aligned(m_indices, 4))
+        return fail(DG_ERR_MISALIGNED, "m_indices must be 4-byte aligned");
+    if (m_total == 0)
+        return ok();
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != DG_OK)
+        return rc;
+    int cfg = forced_config();
+    if (cfg < 0 || 128 % dg::kTiles[cfg].bm != 0)
+        cfg = (n % 256 == 0) ? dg::CFG_128x256 : dg::CFG_128x128;
+    dg::GemmArgs args{};
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.ld_sfa = ld_sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.d = (uint16_t *)d;
+    args.grp = m_indices;
+    args.m = m_total;
+    args.n = n;
+    args.k = k;
+    args.num_groups = num_groups;
+    args.splits = 1;
+    print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1);
+    return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_sfa,
+                                    const void *b, const float *sfb, void *d,
+                                    const int32_t *masked_m, int num_groups, int m_max, int n,
+                                    int k, int expected_m, void *stream)
+{
+    int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m_max, n, k);
+    if (rc != DG_OK)
+        return rc;
+    if (!masked_m)
+        return fail(DG_ERR_INVALID_ARG, "null masked_m");
+    if (num_groups <= 0)
+        return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be positive", num_groups);
+    if (!aligned(masked_m, 4))
+        return fail(DG_ERR_MISALIGNED, "masked_m must be 4-byte aligned");
+    if (m_max == 0)
+        return ok();
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != DG_OK)
+        return rc;
+    (void)expected_m;
+    int cfg = forced_config();
+    if (cfg < 0)
+        cfg = m_max > 128 ? dg::CFG_256x128 : dg::CFG_128x128;
+    dg::GemmArgs args{};
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.ld_sfa = ld_sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.d = (uint16_t *)d;
+    args.grp = masked_m;
+    args.m = m_max;
+    args.n = n;
+    args.k = k;
+    args.num_groups = num_groups;
+    args.splits = 1;
+    print_config("m_grouped_masked", m_max, n, k, num_groups, cfg, 1);
+    return launch(dg::MODE_MASKED, cfg, args, (hipStream_t)stream);
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int64_t dg_get_sf_aligned_m(int64_t m) { return m <= 0 ? 0 : (m + 3) / 4 * 4; }
+
+int dg_set_num_cus(int n)
+{
+    int prev = g_num_cus_cap;
+    g_num_cus_cap = n > 0 ? n : 0;
+    return prev;
+}
+
+int dg_get_num_cus(void)
+{
+    int cus = 0;
+    int rc = device_cus(&cus);
+    return rc == DG_OK ? cus : rc;
+}
+
+const char *dg_last_error(void) { return g_err; }
+
+}  // extern "C"

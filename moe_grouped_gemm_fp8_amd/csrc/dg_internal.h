@@ -1,0 +1,52 @@
+// Internal interface between the C ABI layer (dg_api.cpp) and the HIP kernels (dg_gemm.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+
+// Tile configurations compiled ahead of time.  Each is (BM x BN) output rows x columns per
+// workgroup, split over WM x WN waves of 64 lanes; every wave owns a (BM/WM) x (BN/WN) block
+// built from 16x16 MFMA sub-tiles.
+enum TileCfg : int {
+    CFG_256x224 = 0,  // 8 waves (4x2), wave tile 64x112: large dense GEMMs, N % 224 friendly
+    CFG_128x256 = 1,  // 4 waves (2x2), wave tile 64x128: contiguous MoE (128-row segments)
+    CFG_128x128 = 2,  // 4 waves (2x2), wave tile 64x64
+    CFG_64x32 = 3,    // 4 waves (2x2), wave tile 32x16: skinny M with split-K
+    CFG_256x128 = 4,  // 8 waves (4x2), wave tile 64x64: masked decode, one tile spans m_max
+    CFG_COUNT
+};
+
+struct TileInfo {
+    int bm, bn, threads;
+    const char *name;
+};
+extern const TileInfo kTiles[CFG_COUNT];
+
+struct GemmArgs {
+    const uint8_t *a;
+    const float *sfa;
+    int64_t ld_sfa;
+    const uint8_t *b;
+    const float *sfb;
+    const float *c;       // dense only, may be null
+    uint16_t *d;
+    const int32_t *grp;   // contiguous: m_indices[m_total]; masked: masked_m[num_groups]
+    int m;                // dense: M; contiguous: m_total; masked: m_max
+    int n, k;
+    int num_groups;
+    int splits;           // dense split-K factor (1 = none)
+    float *ws;            // split-K partial tiles
+    int *counters;        // split-K arrival counters, one per output tile, self-resetting
+};
+
+// Grid size in workgroups for a launch (host-side, no HIP call).
+int64_t grid_size(int mode, int cfg, const GemmArgs &args);
+
+// Launches the kernel for (mode, cfg) on `stream`; returns the HIP error of the launch.
+hipError_t launch_gemm(int mode, int cfg, const GemmArgs &args, hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,211 @@
+"""Parity of the HIP path (called through the C ABI binding) with the CPU oracle, on the
+same seeded inputs: small problems compared element by element across several tiles and
+ragged tails, the full-size workloads on sampled rows, edge cases, and the masked call
+replayed from a captured graph with masked_m rewritten on the device."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_fp8_amd as dg
+import oracle
+import workloads as W
+from gpu_util import (DEV, assert_parity, bits, dense_rows_ref, dev, run_contiguous, run_dense,
+                      run_masked, sentinel_like)
+
+pytestmark = pytest.mark.gpu
+
+TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8"]
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    _say(f"start {request.node.name}")
+    yield
+
+
+# ------------------------------------------------------------------------------ dense
+
+def test_dense_small_workload_full():
+    p = W.make_config("dense_small", seed=0)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "dense_small")
+
+
+@pytest.mark.parametrize("cfg", TILE_CONFIGS)
+def test_dense_ragged_every_tile_config(cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_dense(200, 336, 384, seed=21, with_c=True)       # ragged M and N tails
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), cfg)
+
+
+def test_dense_stress_scales():
+    p = W.make_dense(130, 272, 512, seed=22, stress=True)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "stress")
+
+
+def test_dense_c_dominant():
+    p = W.make_dense(96, 224, 256, seed=23, with_c=True, c_std=30.0)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "c_dominant")
+
+
+def test_dense_zero_a_gives_bf16_of_c_bit_exact():
+    p = W.make_dense(64, 128, 256, seed=24, with_c=True, c_std=3.0)
+    p.a[:] = 0
+    got = run_dense(p)
+    want = torch.from_numpy(p.c).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_dense_empty_is_a_noop():
+    d = sentinel_like((1, 16))
+    dg.fp8_gemm_nt(torch.empty(0, 128, dtype=torch.uint8, device=DEV),
+                   torch.empty(1, 0, device=DEV), torch.zeros(16, 128, dtype=torch.uint8, device=DEV),
+                   torch.ones(1, 1, device=DEV), d[:0])
+    torch.cuda.synchronize()
+    assert np.all(bits(d) == W.BF16_SENTINEL)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_dense_forced_split_k_with_ragged_tiles(splits, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "128x128w4")
+    monkeypatch.setenv("DG_FORCE_SPLITS", str(splits))
+    p = W.make_dense(200, 336, 1024, seed=25, with_c=True)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"split{splits}")
+
+
+def test_dense_skinny_workload_full_and_deterministic():
+    p = W.make_config("dense_skinny", seed=0)                  # 64 x 2112 x 7168, split K
+    ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    d1 = run_dense(p)
+    assert_parity(d1, ref, "dense_skinny")
+    d2 = run_dense(p)
+    assert np.array_equal(d1, d2), "split-K reduction is not deterministic"
+
+
+def test_dense_prefill_workload_sampled_rows():
+    p = W.make_config("dense_prefill", seed=0)                 # 4096 x 7168 x 2048 with C
+    got = run_dense(p)
+    assert not np.any(got == W.BF16_SENTINEL), "some outputs were never written"
+    rng = np.random.default_rng(100)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(p.m - 8, p.m),
+                                     rng.choice(p.m, 48, replace=False)]))
+    assert_parity(got[rows], dense_rows_ref(p, rows), "dense_prefill")
+
+
+# ------------------------------------------------------------------------------ contiguous
+
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4"])
+def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_contiguous(5, 600, 256, 512, seed=31, counts=[0, 130, 41, 300, 129], pad_nan=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(run_contiguous(p), ref, f"contiguous {cfg}")
+
+
+def test_contiguous_stress_routing():
+    p = W.make_contiguous(4, 700, 384, 256, seed=32, stress=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(run_contiguous(p), ref, "contiguous stress")
+
+
+def test_contiguous_all_padding_writes_nothing():
+    p = W.make_contiguous(3, 200, 128, 256, seed=33, counts=[0, 200, 0])
+    p.m_indices[:] = -1
+    got = run_contiguous(p)
+    assert np.all(got == W.BF16_SENTINEL)
+
+
+def test_contiguous_workload_sampled_rows():
+    p = W.make_config("moe_contiguous", seed=0)                # 8 experts, 32768 rows, 4096 x 7168
+    got = run_contiguous(p)
+    pad = p.m_indices < 0
+    assert np.all(got[pad] == W.BF16_SENTINEL), "padding rows were written"
+    rng = np.random.default_rng(101)
+    rows = []
+    for g in range(p.num_groups):
+        idx = np.nonzero(p.m_indices == g)[0]
+        if idx.size:
+            rows += [idx[0], idx[-1]] + list(rng.choice(idx, min(6, idx.size), replace=False))
+    rows = np.unique(np.array(rows))
+    ref = np.stack([oracle.fp8_gemm_nt(p.a[r:r + 1], W.mn_major(p.sfa[:, r:r + 1].T),
+                                       p.b[p.m_indices[r]], p.sfb[p.m_indices[r]])[0]
+                    for r in rows])
+    assert_parity(got[rows], ref, "moe_contiguous")
+    assert not np.any(got[~pad] == W.BF16_SENTINEL), "valid rows were left unwritten"
+
+
+# ------------------------------------------------------------------------------ masked
+
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4"])
+def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    mm = [0, 1, 255, 256, 130, 999, -3]
+    p = W.make_masked(7, 256, 384, 512, seed=41, masked_m=mm, tail_nan=True)
+    ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(run_masked(p), ref, f"masked {cfg}")
+
+
+def test_masked_ragged_m_max_and_n():
+    p = W.make_masked(3, 100, 2112, 256, seed=42, masked_m=[100, 37, 64])
+    ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(run_masked(p), ref, "masked ragged")
+
+
+def test_masked_all_zero_writes_nothing():
+    p = W.make_masked(4, 64, 128, 256, seed=43, masked_m=[0, 0, 0, 0])
+    assert np.all(run_masked(p) == W.BF16_SENTINEL)
+
+
+def test_masked_workload_sampled_rows():
+    p = W.make_config("moe_masked", seed=0)                    # 16 x 256 x 7168 x 2048
+    got = run_masked(p)
+    rng = np.random.default_rng(102)
+    for g in range(p.num_groups):
+        valid = int(p.masked_m[g])
+        assert np.all(got[g, valid:] == W.BF16_SENTINEL), f"group {g}: tail written"
+        if valid == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, valid - 1], rng.choice(valid, min(4, valid),
+                                                                      replace=False)]))
+        ref = oracle.fp8_gemm_nt(p.a[g, rows], W.mn_major(p.sfa[g][:, rows].T), p.b[g], p.sfb[g])
+        assert_parity(got[g, rows], ref, f"moe_masked group {g}")
+        assert not np.any(got[g, :valid] == W.BF16_SENTINEL)
+
+
+def test_masked_graph_replays_follow_device_masked_m():
+    g_, m_max, n, k = 6, 128, 256, 512
+    p = W.make_masked(g_, m_max, n, k, seed=44, tail_nan=False)
+    a, sfa, b, sfb = dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb)
+    mm_dev = dev(p.masked_m)
+    d = sentinel_like((g_, m_max, n))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                                # warm-up outside capture
+        dg.m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, mm_dev)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, mm_dev)
+    for r in range(5):
+        mm = W.masked_counts(g_, m_max, seed=44, replay=r)
+        if r == 3:
+            mm[:] = 0
+        d.view(torch.int16).fill_(W.BF16_SENTINEL)
+        mm_dev.copy_(torch.from_numpy(mm))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bits(d)
+        ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, mm)
+        assert_parity(got, ref, f"graph replay {r}")
+        eager = run_masked(p, mm)
+        assert np.array_equal(got, eager), f"replay {r} differs from the eager call"
