@@ -4,22 +4,29 @@
 // GEMM e restrições de layout" and "GEMM denso e grouped"; feifmx.com release article,
 // two-level accumulation of fine-grained-scaled FP8 products).
 //
-// Design, per workgroup tile of BM x BN outputs:
-//  * K advances one 128-deep block at a time: that is one v_mfma_f32_16x16x128_f8f6f4 per
-//    16x16 sub-tile, so each MFMA result is exactly one scale block's partial sum.
+// Design, per workgroup tile of BM x BN outputs split over WM x WN waves:
+//  * K advances one 128-deep block at a time: one v_mfma_f32_16x16x128_f8f6f4 per 16x16
+//    sub-tile, so every MFMA result is exactly one scale block's partial sum.
 //  * The MFMA is issued as D^T = B_tile x A_tile^T (B fragment as the first operand).  A lane
 //    of the 16x16 result then holds four consecutive columns of ONE output row, so the A
-//    row-segment scale is a single per-lane float and the promotion of a partial into the
-//    FP32 accumulators costs one multiply (sa * sb) plus four FMAs per MFMA.
-//  * Operands are staged global -> registers -> LDS, double buffered (one barrier per K
-//    block).  LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ ((r >> 1) & 7), which makes both the 16-byte-per-lane stores and the fragment reads
-//    (16 rows x one chunk per 16-lane group) hit 16 distinct 16-byte bank groups.
+//    row-segment scale is a single per-lane float and promoting a partial into the FP32
+//    accumulators costs one multiply (sa * sb) plus four FMAs per MFMA.
+//  * Every global read of the main loop (A, B and the A scales) is a gfx950 direct-to-LDS
+//    copy (global_load_lds_dwordx4): nothing in flight targets registers, so the only waits
+//    are explicit ones.  Copies run through a ring of RING half-block slots (64 K-bytes of
+//    the A and B tiles each), giving (RING - 2) halves of look-ahead with one barrier per
+//    K block.  Barriers are bare s_barrier (no release fence, which would drain the ring).
+//  * LDS rows are 64 bytes; the 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 3),
+//    so a 16-lane fragment read (16 consecutive rows, one chunk) touches 16 distinct 16-byte
+//    bank groups.  A copy writes 1 KB contiguously per wave, so the swizzle is applied by
+//    choosing which global chunk each lane fetches.  Fragment reads are inline-asm
+//    ds_read_b128 with explicit lgkmcnt waits, so the compiler never pairs an LDS read with
+//    the in-flight copies and drains them.
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
-//    runs a contiguous range of tiles, and tiles are rastered in groups of 4 M-tiles, so the
-//    tiles that run together on one XCD share A rows and B columns in that XCD's L2.
-//  * Skinny dense shapes split K over workgroups: each writes an FP32 partial tile, the last
-//    one to arrive (atomic counter) sums the partials in split order and writes D.
+//    runs a contiguous range of tiles, rastered in groups of 4 M-tiles, so tiles that run
+//    together on one XCD share A rows and B columns in that XCD's L2.
+//  * Skinny dense shapes split K over workgroups: each writes an FP32 partial tile and the
+//    last one to arrive (atomic counter) sums the partials in split order and writes D.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,9 +37,12 @@ namespace dg {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+#define DG_LDS __attribute__((address_space(3)))
+#define DG_CONST __attribute__((address_space(4)))  // read-only for the kernel: scalar loads
 
-constexpr int KBLK = 128;       // K block = scale granularity = MFMA depth
-constexpr int GROUP_M = 4;      // tile raster: M-tiles per group
+constexpr int KBLK = 128;   // K block = scale granularity = MFMA depth
+constexpr int HALF = 64;    // K bytes per ring slot
+constexpr int GROUP_M = 4;  // tile raster: M-tiles per group
 
 const TileInfo kTiles[CFG_COUNT] = {
     {256, 224, 512, "256x224w8"},
@@ -58,6 +68,87 @@ __device__ __forceinline__ void store_bf16x4(uint16_t *dst, v4f v)
     *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Same, for a wave-uniform count known only at run time (anything above 31 waits for all).
+__device__ __forceinline__ void wait_vm_dyn(int n)
+{
+    switch (n) {
+#define DG_WAIT_CASE(k) \
+    case k:             \
+        wait_vm<k>();   \
+        break;
+        DG_WAIT_CASE(1) DG_WAIT_CASE(2) DG_WAIT_CASE(3) DG_WAIT_CASE(4) DG_WAIT_CASE(5)
+        DG_WAIT_CASE(6) DG_WAIT_CASE(7) DG_WAIT_CASE(8) DG_WAIT_CASE(9) DG_WAIT_CASE(10)
+        DG_WAIT_CASE(11) DG_WAIT_CASE(12) DG_WAIT_CASE(13) DG_WAIT_CASE(14) DG_WAIT_CASE(15)
+        DG_WAIT_CASE(16) DG_WAIT_CASE(17) DG_WAIT_CASE(18) DG_WAIT_CASE(19) DG_WAIT_CASE(20)
+        DG_WAIT_CASE(21) DG_WAIT_CASE(22) DG_WAIT_CASE(23) DG_WAIT_CASE(24) DG_WAIT_CASE(25)
+        DG_WAIT_CASE(26) DG_WAIT_CASE(27) DG_WAIT_CASE(28) DG_WAIT_CASE(29) DG_WAIT_CASE(30)
+        DG_WAIT_CASE(31)
+#undef DG_WAIT_CASE
+    default:
+        wait_vm<0>();
+        break;
+    }
+}
+
+__device__ __forceinline__ void bare_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS reads issued as inline asm (see the header comment).  Their results are valid only
+// after lds_wait() followed by tie() on each result, which orders every use after the wait.
+__device__ __forceinline__ v4i lds_read16(uint32_t addr)
+{
+    v4i v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ float lds_read4(uint32_t addr)
+{
+    float v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// All but the N most recent LDS reads have landed (LDS reads retire in order; outstanding
+// scalar loads only make the condition stricter).
+template <int N>
+__device__ __forceinline__ void lds_wait_n()
+{
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+// lds_wait_n for a count that is a constant only after loop unrolling
+__device__ __forceinline__ void lds_wait_le(int n)
+{
+    switch (n) {
+#define DG_LGKM_CASE(k)    \
+    case k:                \
+        lds_wait_n<k>();   \
+        break;
+        DG_LGKM_CASE(1) DG_LGKM_CASE(2) DG_LGKM_CASE(3) DG_LGKM_CASE(4) DG_LGKM_CASE(5)
+        DG_LGKM_CASE(6) DG_LGKM_CASE(7) DG_LGKM_CASE(8) DG_LGKM_CASE(9) DG_LGKM_CASE(10)
+        DG_LGKM_CASE(11) DG_LGKM_CASE(12) DG_LGKM_CASE(13) DG_LGKM_CASE(14) DG_LGKM_CASE(15)
+#undef DG_LGKM_CASE
+    default:
+        lds_wait_n<0>();
+        break;
+    }
+}
+__device__ __forceinline__ void tie(v4i &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(float &v) { asm volatile("" : "+v"(v)); }
+
 // Workgroup id -> tile id such that XCD x (ids x, x+8, x+16, ...) gets one contiguous range.
 __device__ __forceinline__ int xcd_remap(int bid, int nblk)
 {
@@ -77,19 +168,26 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm,
     tn = rem / gsz;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int RING, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
-    constexpr int NT = 64 * WM * WN;
+    constexpr int NW = WM * WN;
+    constexpr int NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
-    constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per K block
-    constexpr int A_PT = (A_CH + NT - 1) / NT, B_PT = (B_CH + NT - 1) / NT;
-    constexpr int STAGE = (BM + BN) * KBLK;
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && BM <= 256, "tile shape");
+    static_assert(RING >= 4 && RING <= 9, "ring depth");
+    constexpr int IA = BM / 16;                   // 1 KB copies per slot: A rows (16 per copy)
+    constexpr int IB = BN / 16;                   //                         B rows
+    constexpr int ICOPY = IA + IB + 1;            // + the block's A scales (64 x 16 bytes)
+    constexpr int MAXI = (ICOPY + NW - 1) / NW;   // copies per wave per slot (padded)
+    constexpr int SA_OFF = (BM + BN) * HALF;      // A scales inside a slot
+    constexpr int HSLOT = SA_OFF + 1024;          // bytes per ring slot
+    static_assert(MAXI * (RING - 2) < 64, "outstanding copies must fit vmcnt");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[RING * HSLOT];
     __shared__ int s_flag;
 
     const int tid = threadIdx.x;
@@ -151,44 +249,89 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const uint8_t *B = p.b + (int64_t)g * N * K;
-    const float *SFB = p.sfb + (int64_t)g * NB * KB;
+    // B scales are wave-uniform and never written by the kernel: read them through the
+    // constant address space so they become scalar loads
+    const DG_CONST float *SFB = (const DG_CONST float *)(p.sfb + (int64_t)g * NB * KB);
+    const int nkb = kb1 - kb0;
+    const int nhalf = 2 * nkb;
 
-    // ---- per-thread global sources and LDS destinations of the staged chunks: 32-bit
-    // offsets from the tile's first A row / B row (rows past the valid range are clamped to
-    // the last valid row, so every load stays inside the operand)
+    // ---- this wave's copies of one ring slot.  Copy q of a slot is A rows [16q, 16q+16)
+    // for q < IA, B rows [16(q-IA), ...) for q < IA+IB, and the block's A scales (64 lanes x
+    // 4 rows, rows clamped to the allocation) for q == IA+IB; both halves of a block carry
+    // the scales.  Waves with fewer real copies repeat one (same bytes to the same place),
+    // so every wave issues MAXI copies per slot and the waits are compile-time constants.
+    // Lane l of a row copy fetches row 16q' + l/4, logical chunk (l & 3) ^ ((row >> 2) & 3):
+    // the swizzled layout.  Rows past the valid range are clamped to the last valid row so
+    // every read stays inside its operand; the rows they feed are never stored.
+    // per copy: a wave-uniform base, K-block stride, half offset and LDS destination, and a
+    // 32-bit per-lane offset (the only per-lane part)
     const uint8_t *a_tile = A + (int64_t)m0 * K;
     const uint8_t *b_tile = B + (int64_t)n0 * K;
-    uint32_t a_off[A_PT], b_off[B_PT];
-    int a_dst[A_PT], b_dst[B_PT];
+    const uint8_t *cbase[MAXI];
+    int64_t cstride[MAXI];  // bytes per K block
+    int choff[MAXI];        // bytes per half block
+    int cdst[MAXI];         // byte offset inside a slot
+    uint32_t coff[MAXI];    // per-lane byte offset from cbase
 #pragma unroll
-    for (int i = 0; i < A_PT; ++i) {
-        int q = tid + i * NT;
-        int r = q >> 3, c = q & 7;
-        int gr = min(m0 + r, row_limit - 1) - m0;
-        a_off[i] = (uint32_t)gr * (uint32_t)K + c * 16;
-        a_dst[i] = r * KBLK + ((c ^ ((r >> 1) & 7)) << 4);
+    for (int i = 0; i < MAXI; ++i) {
+        const int q = (wave + i * NW) % ICOPY;
+        const int sub = lane >> 2, pc = lane & 3;
+        if (q < IA) {
+            const int r = 16 * q + sub;
+            const int gr = min(m0 + r, row_limit - 1);
+            cbase[i] = a_tile;
+            coff[i] = (uint32_t)(gr - m0) * (uint32_t)K + ((pc ^ ((r >> 2) & 3)) << 4);
+            cstride[i] = KBLK;
+            choff[i] = HALF;
+            cdst[i] = q * 1024;
+        } else if (q < IA + IB) {
+            const int r = 16 * (q - IA) + sub;
+            const int gr = min(n0 + r, N - 1);
+            cbase[i] = b_tile;
+            coff[i] = (uint32_t)(gr - n0) * (uint32_t)K + ((pc ^ ((r >> 2) & 3)) << 4);
+            cstride[i] = KBLK;
+            choff[i] = HALF;
+            cdst[i] = BM * HALF + (q - IA) * 1024;
+        } else {
+            const int64_t r4 = min((int64_t)m0 + 4 * lane, ld - 4);
+            cbase[i] = (const uint8_t *)SFA;
+            coff[i] = (uint32_t)(r4 * 4);
+            cstride[i] = ld * 4;
+            choff[i] = 0;
+            cdst[i] = SA_OFF;
+        }
     }
+    DG_LDS uint8_t *ring = (DG_LDS uint8_t *)lds_ring;
+    auto issue_half = [&](int h, int slot) {
+        const int64_t kb = kb0 + (h >> 1);
+        const int hb = h & 1;
 #pragma unroll
-    for (int i = 0; i < B_PT; ++i) {
-        int q = tid + i * NT;
-        int r = q >> 3, c = q & 7;
-        int gr = min(n0 + r, N - 1) - n0;
-        b_off[i] = (uint32_t)gr * (uint32_t)K + c * 16;
-        b_dst[i] = BM * KBLK + r * KBLK + ((c ^ ((r >> 1) & 7)) << 4);
-    }
+        for (int i = 0; i < MAXI; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(cbase[i] + kb * cstride[i] + hb * choff[i] + coff[i]),
+                (DG_LDS void *)(ring + slot * HSLOT + cdst[i]), 16, 0, 0);
+    };
 
-    // per-lane A-scale rows (one per M sub-tile) and per-sub-tile B-scale block rows
-    int sa_row[SM];
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-        sa_row[i] = min(m0 + wm + 16 * i + (lane & 15), row_limit - 1);
     int sb_off[SN];
 #pragma unroll
     for (int j = 0; j < SN; ++j)
-        sb_off[j] = (min(n0 + wn + 16 * j, N - 1) / KBLK) * KB;
+        sb_off[j] = __builtin_amdgcn_readfirstlane((min(n0 + wn + 16 * j, N - 1) / KBLK) * KB);
 
-    // a wave whose rows are all invalid (masked tail) skips the MFMA work
+    // a wave whose rows are all invalid (masked tail, ragged M) skips the MFMA work but still
+    // issues its copies, so the ring is filled the same way for every wave
     const bool wave_active = (m0 + wm) < row_limit;
+
+    // per-lane fragment addresses inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32)
+    // of 16 rows: half g/2 of the block, logical chunks 2(g%2) and 2(g%2)+1
+    const int fr = lane & 15;
+    const int fc = 2 * ((lane >> 4) & 1);
+    const int fsw = (fr >> 2) & 3;
+    const uint32_t lo_off = (uint32_t)((fc ^ fsw) << 4), hi_off = (uint32_t)(((fc + 1) ^ fsw) << 4);
+    const uint32_t a_row_off = (uint32_t)(wm + fr) * HALF;
+    const uint32_t b_row_off = (uint32_t)(BM + wn + fr) * HALF;
+    const uint32_t sa_off = SA_OFF + (uint32_t)(wm + fr) * 4;
+    const uint32_t ring_base = (uint32_t)(uintptr_t)ring;
+    const bool upper = (lane >> 5) & 1;  // this lane reads the block's second half
 
     v4f acc[SM][SN];
 #pragma unroll
@@ -197,107 +340,158 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
         for (int j = 0; j < SN; ++j)
             acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    v4i ra[A_PT], rb[B_PT];
-    auto load_regs = [&](int kb) {
-        const int off = kb * KBLK;
+    // prologue: halves 0 .. RING-2 into slots 0 .. RING-2
+    int issue_slot = 0;
+    for (int h = 0; h < RING - 1 && h < nhalf; ++h) {
+        issue_half(h, issue_slot);
+        issue_slot = issue_slot + 1 == RING ? 0 : issue_slot + 1;
+    }
+    float sb_cur[SN], sb_nxt[SN];
 #pragma unroll
-        for (int i = 0; i < A_PT; ++i)
-            if (A_CH % NT == 0 || tid + i * NT < A_CH)
-                ra[i] = *reinterpret_cast<const v4i *>(a_tile + a_off[i] + off);
-#pragma unroll
-        for (int i = 0; i < B_PT; ++i)
-            if (B_CH % NT == 0 || tid + i * NT < B_CH)
-                rb[i] = *reinterpret_cast<const v4i *>(b_tile + b_off[i] + off);
-    };
-    auto store_lds = [&](int st) {
-        uint8_t *base = lds + st * STAGE;
-#pragma unroll
-        for (int i = 0; i < A_PT; ++i)
-            if (A_CH % NT == 0 || tid + i * NT < A_CH)
-                *reinterpret_cast<v4i *>(base + a_dst[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_PT; ++i)
-            if (B_CH % NT == 0 || tid + i * NT < B_CH)
-                *reinterpret_cast<v4i *>(base + b_dst[i]) = rb[i];
-    };
+    for (int jj = 0; jj < SN; ++jj)
+        sb_cur[jj] = SFB[sb_off[jj] + kb0];
 
-    float sa_cur[SM], sa_nxt[SM];
-    auto load_sa = [&](int kb, float *dst) {
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-            dst[i] = SFA[(int64_t)kb * ld + sa_row[i]];
-    };
-
-    load_regs(kb0);
-    load_sa(kb0, sa_cur);
-    store_lds(0);
-    __syncthreads();
-
-    const int frag_row = lane & 15;
-    const int frag_chunk = (lane >> 4) * 2;  // lanes 16g..16g+15 take K bytes [32g, 32g+32)
-    for (int kb = kb0; kb < kb1; ++kb) {
-        const int st = (kb - kb0) & 1;
-        const bool more = kb + 1 < kb1;
-        if (more) {
-            load_regs(kb + 1);
-            load_sa(kb + 1, sa_nxt);
-        }
-        if (wave_active) {
-            const uint8_t *la = lds + st * STAGE;
-            const uint8_t *lb = la + BM * KBLK;
-            float sb[SN];
-#pragma unroll
-            for (int j = 0; j < SN; ++j)
-                sb[j] = SFB[sb_off[j] + kb];
-            // fragment of 16 rows x 128 K bytes: lane reads row (lane & 15), bytes [32g, 32g+32)
-            auto frag = [&](const uint8_t *base, int r) {
-                const int sw = (r >> 1) & 7;
-                const uint8_t *rowp = base + r * KBLK;
-                v4i lo = *reinterpret_cast<const v4i *>(rowp + ((frag_chunk ^ sw) << 4));
-                v4i hi = *reinterpret_cast<const v4i *>(rowp + (((frag_chunk + 1) ^ sw) << 4));
-                return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            };
-            // hold the fragments of the dimension with fewer sub-tiles, stream the other
-            if constexpr (SM <= SN) {
-                v8i af[SM];
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-                    af[i] = frag(la, wm + 16 * i + frag_row);
-#pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    const v8i bf = frag(lb, wn + 16 * j + frag_row);
-#pragma unroll
-                    for (int i = 0; i < SM; ++i) {
-                        v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bf, af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                        acc[i][j] += part * (sa_cur[i] * sb[j]);
-                    }
-                }
-            } else {
-                v8i bf[SN];
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-                    bf[j] = frag(lb, wn + 16 * j + frag_row);
-#pragma unroll
-                for (int i = 0; i < SM; ++i) {
-                    const v8i af = frag(la, wm + 16 * i + frag_row);
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) {
-                        v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                        acc[i][j] += part * (sa_cur[i] * sb[j]);
-                    }
-                }
+    int read_slot = 0;  // slot of half 2j
+    for (int j = 0; j < nkb; ++j) {
+        // block j needs halves 2j and 2j+1; everything issued after them may stay in flight
+        const int issued_hi = min(j == 0 ? RING - 2 : 2 * j + RING - 3, nhalf - 1);
+        const int pending = issued_hi - (2 * j + 1);
+        if (pending == RING - 4 && j > 0) {
+            wait_vm<MAXI *(RING - 4)>();  // steady state
+        } else {
+            switch (pending) {
+            case 0: wait_vm<0>(); break;
+            case 1: wait_vm<MAXI>(); break;
+            case 2: wait_vm<MAXI * 2>(); break;
+            case 3: wait_vm<MAXI * 3>(); break;
+            case 4: wait_vm<(MAXI * 4 < 64 ? MAXI * 4 : 0)>(); break;
+            case 5: wait_vm<(MAXI * 5 < 64 ? MAXI * 5 : 0)>(); break;
+            case 6: wait_vm<(MAXI * 6 < 64 ? MAXI * 6 : 0)>(); break;
+            default: wait_vm<0>(); break;
             }
         }
-        if (more) {
-            store_lds(st ^ 1);
+        bare_barrier();  // all copies of block j have landed; block j-1's slots are free
+        // this block refills the ring with half RING-1 (block 0) or halves 2j+RING-2 and
+        // 2j+RING-1
+        const int h_first = (j == 0) ? RING - 1 : 2 * j + RING - 2;
+        const int n_iss = max(0, min((j == 0) ? 1 : 2, nhalf - h_first));
+        auto issue_copy = [&](int c) {  // c is a constant after unrolling
+            const int e = c / MAXI, i = c % MAXI;
+            if (e < n_iss) {
+                const int h = h_first + e;
+                const int slot = issue_slot + e >= RING ? issue_slot + e - RING : issue_slot + e;
+                // the address is formed at the issue point (kept from being hoisted and held
+                // in registers across the MFMA steps)
+                uint32_t o = coff[i];
+                asm volatile("" : "+v"(o));
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(cbase[i] + (int64_t)(kb0 + (h >> 1)) * cstride[i] +
+                                   (h & 1) * choff[i] + o),
+                    (DG_LDS void *)(ring + slot * HSLOT + cdst[i]), 16, 0, 0);
+            }
+        };
+        const int kb = kb0 + j;
+        if (j + 1 < nkb) {  // B scales of the next block, one iteration ahead
+#pragma unroll
+            for (int jj = 0; jj < SN; ++jj)
+                sb_nxt[jj] = SFB[sb_off[jj] + kb + 1];
+        }
+        if (wave_active) {
+            const int slot1 = read_slot + 1 == RING ? 0 : read_slot + 1;
+            const uint32_t base = ring_base + (upper ? slot1 : read_slot) * HSLOT;
+            const uint32_t sa_addr = ring_base + read_slot * HSLOT + sa_off;
+            // Reads go out in the order B(0), then (A_i, A-scale_i) per sub-tile, then B(1);
+            // the first step waits for each A_i separately (LDS reads retire in order), so
+            // the MFMAs start as soon as their own operands land instead of after the whole
+            // burst that every wave issues right after the barrier.
+            static_assert(3 * (SM - 1) + 4 < 16, "lgkmcnt range");
+            v4i blo[SN], bhi[SN];
+            blo[0] = lds_read16(base + b_row_off + lo_off);
+            bhi[0] = lds_read16(base + b_row_off + hi_off);
+            v4i alo[SM], ahi[SM];
+            float sav[SM];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                alo[i] = lds_read16(base + a_row_off + i * 1024 + lo_off);
+                ahi[i] = lds_read16(base + a_row_off + i * 1024 + hi_off);
+                sav[i] = lds_read4(sa_addr + i * 64);
+            }
+            if constexpr (SN > 1) {
+                blo[1] = lds_read16(base + b_row_off + 1024 + lo_off);
+                bhi[1] = lds_read16(base + b_row_off + 1024 + hi_off);
+            }
+            // ring refill: after the block's first LDS reads so those are not queued behind
+            // the copies (each copy holds the wave's in-order issue until accepted)
+#pragma unroll
+            for (int c = 0; c < 2 * MAXI; ++c)
+                issue_copy(c);
+            // Step jj issues the SM MFMAs of fragment jj, each followed by the promotion of
+            // the partial of fragment jj-1 in the same row (issued SM MFMAs earlier, so its
+            // result is ready), with the reads of fragment jj+2 in flight.  The schedule
+            // barriers keep that interleave: the compiler would otherwise cluster the MFMAs.
+            v4f pend[SM];
+            // reads issued after the A reads and before the first step's waits: B(1), B(2)
+            constexpr int B1 = (SN > 1 ? 2 : 0) + (SN > 2 ? 2 : 0);
+#pragma unroll
+            for (int jj = 0; jj < SN; ++jj) {
+                const v8i bf = v8i{blo[jj].x, blo[jj].y, blo[jj].z, blo[jj].w,
+                                   bhi[jj].x, bhi[jj].y, bhi[jj].z, bhi[jj].w};
+                if (jj + 2 < SN) {
+                    blo[jj + 2] = lds_read16(base + b_row_off + (jj + 2) * 1024 + lo_off);
+                    bhi[jj + 2] = lds_read16(base + b_row_off + (jj + 2) * 1024 + hi_off);
+                }
+                v4f part[SM];
+#pragma unroll
+                for (int i = 0; i < SM; ++i) {
+                    if (jj == 0) {  // B(0) and A_i have landed once only younger reads remain
+                        lds_wait_le(3 * (SM - 1 - i) + B1);
+                        if (i == 0) {
+                            tie(blo[0]);
+                            tie(bhi[0]);
+                        }
+                        tie(alo[i]);
+                        tie(ahi[i]);
+                        tie(sav[i]);
+                    }
+                    const v8i af = v8i{alo[i].x, alo[i].y, alo[i].z, alo[i].w,
+                                       ahi[i].x, ahi[i].y, ahi[i].z, ahi[i].w};
+                    part[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf, af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    if (jj > 0)
+                        acc[i][jj - 1] += pend[i] * (sav[i] * sb_cur[jj - 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+                    pend[i] = part[i];
+                if (jj + 1 < SN) {
+                    if (jj + 2 < SN)
+                        lds_wait_n<2>();  // B(jj+1) has landed, B(jj+2) may be in flight
+                    else
+                        lds_wait_n<0>();
+                    tie(blo[jj + 1]);
+                    tie(bhi[jj + 1]);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < SM; ++i)
-                sa_cur[i] = sa_nxt[i];
+                acc[i][SN - 1] += pend[i] * (sav[i] * sb_cur[SN - 1]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2 * MAXI; ++c)
+                issue_copy(c);
         }
-        __syncthreads();
+        issue_slot += n_iss;
+        if (issue_slot >= RING)
+            issue_slot -= RING;
+        if (j + 1 < nkb) {
+#pragma unroll
+            for (int jj = 0; jj < SN; ++jj)
+                sb_cur[jj] = sb_nxt[jj];
+        }
+        read_slot = read_slot + 2 >= RING ? read_slot + 2 - RING : read_slot + 2;
     }
+    wait_vm<0>();  // no copy may still be writing LDS past this point
 
     // ---- split-K: publish the partial tile; the last arriving workgroup reduces in order
     if constexpr (MODE == MODE_DENSE) {
@@ -384,7 +578,7 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     return g;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int RING>
 static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
 {
     int tiles_m, tiles_n;
@@ -401,15 +595,15 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     dim3 g((unsigned)grid), b(cfg_threads);
     switch (mode) {
     case MODE_DENSE:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_DENSE>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_DENSE>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_CONTIG>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_CONTIG>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_MASKED>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_MASKED>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     }
@@ -420,15 +614,15 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
 {
     switch (cfg) {
     case CFG_256x224:
-        return launch_cfg<256, 224, 4, 2>(mode, a, stream);
+        return launch_cfg<256, 224, 4, 2, 5>(mode, a, stream);
     case CFG_128x256:
-        return launch_cfg<128, 256, 2, 2>(mode, a, stream);
+        return launch_cfg<128, 256, 2, 2, 6>(mode, a, stream);
     case CFG_128x128:
-        return launch_cfg<128, 128, 2, 2>(mode, a, stream);
+        return launch_cfg<128, 128, 2, 2, 6>(mode, a, stream);
     case CFG_64x32:
-        return launch_cfg<64, 32, 2, 2>(mode, a, stream);
+        return launch_cfg<64, 32, 2, 2, 8>(mode, a, stream);
     case CFG_256x128:
-        return launch_cfg<256, 128, 4, 2>(mode, a, stream);
+        return launch_cfg<256, 128, 4, 2, 6>(mode, a, stream);
     default:
         return hipErrorInvalidValue;
     }
