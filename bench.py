@@ -46,7 +46,7 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -187,47 +187,61 @@ def make_masked_case(torch, dg, W):
 
 
 def time_case(torch, case, steps, warmup):
+    """Warm up, then time exactly `steps` steps as one region bracketed by HIP events on the
+    launch stream (the step time and, for cases without a per-step device update, the kernel's
+    average launch duration); then a second pass with an event pair around every launch gives
+    the spread (and the average for cases whose update copy must stay outside the pair)."""
     prep = getattr(case, "prepare", None)
     for i in range(warmup):
         if prep:
             prep(i)
         case.launch(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_all0.record()
     for i in range(steps):
-        j = warmup + i
         if prep:
-            prep(j)
-        ev[i][0].record()
-        case.launch(j)
-        ev[i][1].record()
+            prep(warmup + i)
+        case.launch(warmup + i)
     t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    total = t_all0.elapsed_time(t_all1) * 1e-3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        if prep:
+            prep(warmup + i)
+        ev[i][0].record()
+        case.launch(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
     per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3       # seconds per launch
     flops = np.array([case.flops(warmup + i) for i in range(steps)])
     nbytes = np.array([case.bytes(warmup + i) for i in range(steps)])
-    total = t_all0.elapsed_time(t_all1) * 1e-3
-    return dict(total_s=total, wall_s=wall, per_launch_s=per, flops=flops, bytes=nbytes)
+    avg = per.mean() if prep else total / steps
+    return dict(total_s=total, wall_s=wall, per_launch_s=per, avg_s=avg,
+                timing="per-launch event pairs" if prep else "timed region / steps",
+                flops=flops, bytes=nbytes)
 
 
 def summarize(res):
     per = res["per_launch_s"]
-    avg = float(per.mean())
-    tflops = float(res["flops"].sum() / per.sum() / 1e12)
-    gbs = float(res["bytes"].sum() / per.sum() / 1e9)
-    return dict(avg_kernel_us=avg * 1e6, p10_us=float(np.percentile(per, 10) * 1e6),
+    avg = float(res["avg_s"])
+    tflops = float(res["flops"].mean() / avg / 1e12)
+    gbs = float(res["bytes"].mean() / avg / 1e9)
+    return dict(avg_kernel_us=avg * 1e6, timing=res["timing"],
+                per_launch_event_us=float(per.mean() * 1e6),
+                p10_us=float(np.percentile(per, 10) * 1e6),
                 p90_us=float(np.percentile(per, 90) * 1e6), tflops=tflops, hbm_gbs=gbs,
                 frac_fp8_peak=tflops / PEAK_FP8_TFLOPS, frac_hbm_peak=gbs / PEAK_HBM_GBS)
 
 
 def cpu_baseline(W, case, target_s):
+    """The CPU oracle on a bounded sample of the workload: the first rows of A (all of N and K),
+    grown until one call takes a good part of `target_s`, then repeated to about `target_s`."""
     import oracle
     p = case.problem
     log("timing the CPU oracle on a row sample of the workload")
@@ -237,13 +251,39 @@ def cpu_baseline(W, case, target_s):
         oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(p.sfa[:, :rows].T), p.b, p.sfb,
                            None if p.c is None else p.c[:rows])
         dt = time.perf_counter() - t0
-        if dt >= target_s or rows >= p.m:
+        if dt >= target_s / 4 or rows >= p.m:
             break
-        rows = int(min(p.m, max(rows * 2, rows * target_s / max(dt, 1e-3) * 1.1)))
-    flops = 2.0 * rows * p.n * p.k
-    return dict(value=flops / dt / 1e12, unit="TFLOPS", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{rows} of {p.m} rows of the {case.name} workload (all N={p.n}, K={p.k}),"
-                       f" {dt:.1f} s, float64")
+        rows = int(min(p.m, max(rows * 2, rows * target_s / 4 / max(dt, 1e-3))))
+    reps, total = 1, dt
+    while total < target_s:
+        t0 = time.perf_counter()
+        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(p.sfa[:, :rows].T), p.b, p.sfb,
+                           None if p.c is None else p.c[:rows])
+        total += time.perf_counter() - t0
+        reps += 1
+    flops = 2.0 * rows * p.n * p.k * reps
+    return dict(value=flops / total / 1e12, unit="TFLOPS", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"{reps} x {rows} of {p.m} rows of the {case.name} workload (all N={p.n}, "
+                       f"K={p.k}), {total:.1f} s of float64 work")
+
+
+def calibration_copy(torch):
+    """A plain device-to-device copy of 1 GiB from a source written long before (evicted from
+    the caches by 2 GiB of other writes): the HBM-traffic counters of this copy, divided by
+    its known 1 GiB read and 1 GiB write, give their scale factors."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    flush = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
+    flush.fill_(2)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy of 1 GiB done")
+    del src, flush, dst
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -257,6 +297,8 @@ def main():
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 1 GiB device copy (reference for HBM-traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -272,6 +314,8 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     log(f"device {torch.cuda.get_device_name(0)}, {dg.get_num_cus()} CUs")
+    if args.calibrate_copy:
+        calibration_copy(torch)
 
     makers = {
         "dense_small": lambda: make_dense_case(torch, dg, W, "dense_small"),
