@@ -41,7 +41,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define DG_CONST __attribute__((address_space(4)))  // read-only for the kernel: scalar loads
 
 constexpr int KBLK = 128;   // K block = scale granularity = MFMA depth
-constexpr int HALF = 64;    // K bytes per ring slot
 constexpr int GROUP_M = 4;  // tile raster: M-tiles per group
 
 const TileInfo kTiles[CFG_COUNT] = {
@@ -168,7 +167,29 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm,
     tn = rem / gsz;
 }
 
-template <int BM, int BN, int WM, int WN, int RING, int MODE>
+// 128-bit buffer resource for raw (unstrided) loads of `bytes` bytes from `base`: any lane
+// whose offset falls outside the range reads zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// Register buffer that holds B fragment jj (of SN per block).  Fragment jj+2 is read while
+// jj is in use and jj+1 may be in flight, and the next block's fragments 0 and 1 are read
+// while fragment SN-1 is in use, so any three consecutive fragments (across the block
+// boundary too) need distinct buffers: jj % 3, except that the last one takes buffer 3 when
+// jj % 3 would collide with the next block's 0 or 1.
+__host__ __device__ constexpr int bbuf(int jj, int sn)
+{
+    return (jj == sn - 1 && sn > 2 && (jj % 3) != 2) ? 3 : jj % 3;
+}
+__host__ __device__ constexpr int bbuf_count(int sn)
+{
+    return sn <= 3 ? sn : ((sn - 1) % 3 == 2 ? 3 : 4);
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
@@ -176,18 +197,26 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
     constexpr int NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
+    constexpr int NBUF = bbuf_count(SN);
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
-    static_assert(BM % 16 == 0 && BN % 16 == 0 && BM <= 256, "tile shape");
-    static_assert(RING >= 4 && RING <= 9, "ring depth");
-    constexpr int IA = BM / 16;                   // 1 KB copies per slot: A rows (16 per copy)
-    constexpr int IB = BN / 16;                   //                         B rows
-    constexpr int ICOPY = IA + IB + 1;            // + the block's A scales (64 x 16 bytes)
-    constexpr int MAXI = (ICOPY + NW - 1) / NW;   // copies per wave per slot (padded)
-    constexpr int SA_OFF = (BM + BN) * HALF;      // A scales inside a slot
-    constexpr int HSLOT = SA_OFF + 1024;          // bytes per ring slot
-    static_assert(MAXI * (RING - 2) < 64, "outstanding copies must fit vmcnt");
+    static_assert(BM % 8 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
+    // LDS: two A slots (BM rows of one K block, then its BM A scales in a 1 KB area) and
+    // three B slots (BN rows of one K block).  Rows are 128 bytes; 16-byte chunk c of row r
+    // sits at chunk c ^ ((r >> 1) & 7).
+    constexpr int A_BYTES = BM * KBLK;
+    constexpr int A_SLOT = A_BYTES + 1024;
+    constexpr int B_SLOT = BN * KBLK;
+    constexpr int B_BASE = 2 * A_SLOT;
+    constexpr int LDS_BYTES = B_BASE + 3 * B_SLOT;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
+    static_assert(IA % NW == 0, "A copies must split evenly over the waves");
+    constexpr int CA = IA / NW;                   // A copies per wave per block
+    constexpr int CB = (IB + NW - 1) / NW;        // B copies per wave per block (padded)
+    constexpr int MAXI = CA + CB;                 // + wave 0 copies the block's A scales
+    static_assert(2 * MAXI < 64, "outstanding copies must fit vmcnt");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[RING * HSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     __shared__ int s_flag;
 
     const int tid = threadIdx.x;
@@ -253,85 +282,79 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
     // constant address space so they become scalar loads
     const DG_CONST float *SFB = (const DG_CONST float *)(p.sfb + (int64_t)g * NB * KB);
     const int nkb = kb1 - kb0;
-    const int nhalf = 2 * nkb;
 
-    // ---- this wave's copies of one ring slot.  Copy q of a slot is A rows [16q, 16q+16)
-    // for q < IA, B rows [16(q-IA), ...) for q < IA+IB, and the block's A scales (64 lanes x
-    // 4 rows, rows clamped to the allocation) for q == IA+IB; both halves of a block carry
-    // the scales.  Waves with fewer real copies repeat one (same bytes to the same place),
-    // so every wave issues MAXI copies per slot and the waits are compile-time constants.
-    // Lane l of a row copy fetches row 16q' + l/4, logical chunk (l & 3) ^ ((row >> 2) & 3):
-    // the swizzled layout.  Rows past the valid range are clamped to the last valid row so
-    // every read stays inside its operand; the rows they feed are never stored.
-    // per copy: a wave-uniform base, K-block stride, half offset and LDS destination, and a
-    // 32-bit per-lane offset (the only per-lane part)
-    const uint8_t *a_tile = A + (int64_t)m0 * K;
-    const uint8_t *b_tile = B + (int64_t)n0 * K;
-    const uint8_t *cbase[MAXI];
-    int64_t cstride[MAXI];  // bytes per K block
-    int choff[MAXI];        // bytes per half block
-    int cdst[MAXI];         // byte offset inside a slot
-    uint32_t coff[MAXI];    // per-lane byte offset from cbase
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-        const int q = (wave + i * NW) % ICOPY;
-        const int sub = lane >> 2, pc = lane & 3;
-        if (q < IA) {
-            const int r = 16 * q + sub;
-            const int gr = min(m0 + r, row_limit - 1);
-            cbase[i] = a_tile;
-            coff[i] = (uint32_t)(gr - m0) * (uint32_t)K + ((pc ^ ((r >> 2) & 3)) << 4);
-            cstride[i] = KBLK;
-            choff[i] = HALF;
-            cdst[i] = q * 1024;
-        } else if (q < IA + IB) {
-            const int r = 16 * (q - IA) + sub;
-            const int gr = min(n0 + r, N - 1);
-            cbase[i] = b_tile;
-            coff[i] = (uint32_t)(gr - n0) * (uint32_t)K + ((pc ^ ((r >> 2) & 3)) << 4);
-            cstride[i] = KBLK;
-            choff[i] = HALF;
-            cdst[i] = BM * HALF + (q - IA) * 1024;
+    // ---- copies.  Wave w's copy c < CA of a block is A rows [8q, 8q+8) with q = w + c*NW;
+    // copy CA + c is B rows [8q, 8q+8) with q = min(w + c*NW, IB-1) (a wave past the last B
+    // rows repeats it: same bytes to the same place); wave 0 also copies the block's A
+    // scales.  Lane l of a row copy fetches row 8q + l/8, logical chunk (l & 7) ^
+    // ((row >> 1) & 7), so the contiguous 1 KB that the copy writes is the swizzled layout;
+    // (row >> 1) & 7 = (l >> 4) ^ 4(q & 1).  Operands are read through buffer resources that
+    // end at the last valid row, so rows past it read as zeros (their outputs are never
+    // stored); past the last K block the resources are empty and the copies only write
+    // zeros into slots nobody reads, which keeps the per-wave copy count constant.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * K, (int64_t)(row_limit - m0) * K);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA, (int64_t)KB * ld * 4);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(SFA, 0);
+    const uint32_t lane_even = (uint32_t)(lane >> 3) * (uint32_t)K +
+                               (uint32_t)((((lane & 7) ^ (lane >> 4))) << 4);
+    const uint32_t lane_sfa = (uint32_t)(m0 + 4 * lane) * 4u;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)lds;
+    DG_LDS uint8_t *ldsp = (DG_LDS uint8_t *)lds;
+
+    // issue copy c (0 <= c < MAXI; a constant after unrolling) of K block kb into A slot
+    // aslot and B slot bslot, through resources rA / rB / rS
+    auto issue_copy = [&](int c, int kb, int aslot, int bslot, __amdgpu_buffer_rsrc_t rA,
+                          __amdgpu_buffer_rsrc_t rB) {
+        uint32_t le = lane_even;
+        asm volatile("" : "+v"(le));  // formed here, not held in a register per copy
+        if (c < CA) {
+            const int q = wave + c * NW;
+            const uint32_t vo = (le ^ (uint32_t)((q & 1) << 6)) + (uint32_t)(8 * q) * (uint32_t)K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rA, (DG_LDS void *)(ldsp + aslot * A_SLOT + q * 1024), 16, vo,
+                (uint32_t)kb * KBLK, 0, 0);
         } else {
-            const int64_t r4 = min((int64_t)m0 + 4 * lane, ld - 4);
-            cbase[i] = (const uint8_t *)SFA;
-            coff[i] = (uint32_t)(r4 * 4);
-            cstride[i] = ld * 4;
-            choff[i] = 0;
-            cdst[i] = SA_OFF;
+            const int q = min(wave + (c - CA) * NW, IB - 1);
+            const uint32_t vo = (le ^ (uint32_t)((q & 1) << 6)) + (uint32_t)(8 * q) * (uint32_t)K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rB, (DG_LDS void *)(ldsp + B_BASE + bslot * B_SLOT + q * 1024), 16, vo,
+                (uint32_t)kb * KBLK, 0, 0);
         }
-    }
-    DG_LDS uint8_t *ring = (DG_LDS uint8_t *)lds_ring;
-    auto issue_half = [&](int h, int slot) {
-        const int64_t kb = kb0 + (h >> 1);
-        const int hb = h & 1;
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(cbase[i] + kb * cstride[i] + hb * choff[i] + coff[i]),
-                (DG_LDS void *)(ring + slot * HSLOT + cdst[i]), 16, 0, 0);
     };
+    auto issue_scales = [&](int kb, int aslot, __amdgpu_buffer_rsrc_t rS) {
+        if (wave == 0) {
+            uint32_t vo = lane_sfa;
+            asm volatile("" : "+v"(vo));
+            vo += (uint32_t)((int64_t)kb * ld * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rS, (DG_LDS void *)(ldsp + aslot * A_SLOT + A_BYTES), 16, vo, 0, 0, 0);
+        }
+    };
+    // wait until the copies issued before the most recent block's have landed
+    auto wait_older_copies = [&]() {
+        if (wave == 0)
+            wait_vm<MAXI + 1>();
+        else
+            wait_vm<MAXI>();
+    };
+
+    // per-lane fragment offsets inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32) of
+    // 16 consecutive rows, i.e. logical chunks 2g and 2g+1
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
+    const uint32_t f_lo = (uint32_t)(fr * KBLK + (((2 * fg) ^ (fr >> 1)) << 4));
+    const uint32_t f_hi = (uint32_t)(fr * KBLK + (((2 * fg + 1) ^ (fr >> 1)) << 4));
+    const uint32_t a_lo = lds_base + (uint32_t)(wm * KBLK) + f_lo;
+    const uint32_t a_hi = lds_base + (uint32_t)(wm * KBLK) + f_hi;
+    const uint32_t sa_lane = lds_base + A_BYTES + (uint32_t)(wm + fr) * 4;
+    const uint32_t b_lo = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_lo;
+    const uint32_t b_hi = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_hi;
 
     int sb_off[SN];
 #pragma unroll
     for (int j = 0; j < SN; ++j)
         sb_off[j] = __builtin_amdgcn_readfirstlane((min(n0 + wn + 16 * j, N - 1) / KBLK) * KB);
-
-    // a wave whose rows are all invalid (masked tail, ragged M) skips the MFMA work but still
-    // issues its copies, so the ring is filled the same way for every wave
-    const bool wave_active = (m0 + wm) < row_limit;
-
-    // per-lane fragment addresses inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32)
-    // of 16 rows: half g/2 of the block, logical chunks 2(g%2) and 2(g%2)+1
-    const int fr = lane & 15;
-    const int fc = 2 * ((lane >> 4) & 1);
-    const int fsw = (fr >> 2) & 3;
-    const uint32_t lo_off = (uint32_t)((fc ^ fsw) << 4), hi_off = (uint32_t)(((fc + 1) ^ fsw) << 4);
-    const uint32_t a_row_off = (uint32_t)(wm + fr) * HALF;
-    const uint32_t b_row_off = (uint32_t)(BM + wn + fr) * HALF;
-    const uint32_t sa_off = SA_OFF + (uint32_t)(wm + fr) * 4;
-    const uint32_t ring_base = (uint32_t)(uintptr_t)ring;
-    const bool upper = (lane >> 5) & 1;  // this lane reads the block's second half
 
     v4f acc[SM][SN];
 #pragma unroll
@@ -340,157 +363,213 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
         for (int j = 0; j < SN; ++j)
             acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: halves 0 .. RING-2 into slots 0 .. RING-2
-    int issue_slot = 0;
-    for (int h = 0; h < RING - 1 && h < nhalf; ++h) {
-        issue_half(h, issue_slot);
-        issue_slot = issue_slot + 1 == RING ? 0 : issue_slot + 1;
+    // Fragments.  A (all SM row sub-tiles) and its scales S are held for a whole block; during
+    // the block's last step each A[i] / S[i] is replaced by the next block's right after the
+    // last MFMA that reads it.  B fragments are read two steps ahead; the next block's B(0)
+    // and B(1) are read during the last step.
+    v4i Af[SM][2];
+    float Sf[SM];
+    v4i Bf[NBUF][2];
+    // MFMA partials of the previous step, promoted during the next one, and (across a block
+    // boundary) the scales of the last step's partials.  Zero before the first step: a no-op.
+    v4f pend[SM];
+    float psc[SM];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        pend[i] = v4f{0.f, 0.f, 0.f, 0.f};
+        psc[i] = 0.f;
     }
     float sb_cur[SN], sb_nxt[SN];
+
+    auto read_a = [&](int aslot, int i) {
+        const uint32_t so = (uint32_t)(aslot * A_SLOT) + (uint32_t)(i * 16 * KBLK);
+        Af[i][0] = lds_read16(a_lo + so);
+        Af[i][1] = lds_read16(a_hi + so);
+        Sf[i] = lds_read4(sa_lane + (uint32_t)(aslot * A_SLOT) + i * 64);
+    };
+    auto read_b = [&](int bslot, int jj, v4i (&bf)[2]) {
+        const uint32_t so = (uint32_t)(bslot * B_SLOT) + (uint32_t)(jj * 16 * KBLK);
+        bf[0] = lds_read16(b_lo + so);
+        bf[1] = lds_read16(b_hi + so);
+    };
+
+    // One MFMA step: for each row sub-tile i, first promote the previous step's partial of row
+    // i (issued SM MFMAs earlier, so it is ready) with scale `scale(i)`, then issue MFMA
+    // (i, jj) into the freed partial; `extra(i)` slots in copies and reads after it.
+    auto mfma_step = [&](int jj, const v4i (&bf)[2], auto scale, auto extra) {
+        const v8i bv = v8i{bf[0].x, bf[0].y, bf[0].z, bf[0].w, bf[1].x, bf[1].y, bf[1].z, bf[1].w};
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+            {
+                v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
+                a += pend[i] * scale(i);
+                // keep the promotion here: left free, the compiler hoists every MFMA of the
+                // block above all promotions and holds SM*SN partials live at once
+                asm volatile("" : "+v"(a));
+            }
+            const v8i av = v8i{Af[i][0].x, Af[i][0].y, Af[i][0].z, Af[i][0].w,
+                               Af[i][1].x, Af[i][1].y, Af[i][1].z, Af[i][1].w};
+            pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            extra(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: blocks 0 and 1 in flight, block 0's fragments read
+    {
+        const bool two = nkb > 1;
+        issue_scales(kb0, 0, rs);
+#pragma unroll
+        for (int c = 0; c < MAXI; ++c)
+            issue_copy(c, kb0, 0, 0, ra, rb);
+        issue_scales(two ? kb0 + 1 : kb0, 1, two ? rs : rz);
+#pragma unroll
+        for (int c = 0; c < MAXI; ++c)
+            issue_copy(c, two ? kb0 + 1 : kb0, 1, 1, two ? ra : rz, two ? rb : rz);
+    }
 #pragma unroll
     for (int jj = 0; jj < SN; ++jj)
         sb_cur[jj] = SFB[sb_off[jj] + kb0];
+    wait_older_copies();
+    bare_barrier();
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+        read_a(0, i);
+    read_b(0, 0, Bf[0]);
+    if constexpr (SN > 1)
+        read_b(0, 1, Bf[1]);
 
-    int read_slot = 0;  // slot of half 2j
+    int bslot = 0;  // B slot of the current block; its A slot is the block's parity
     for (int j = 0; j < nkb; ++j) {
-        // block j needs halves 2j and 2j+1; everything issued after them may stay in flight
-        const int issued_hi = min(j == 0 ? RING - 2 : 2 * j + RING - 3, nhalf - 1);
-        const int pending = issued_hi - (2 * j + 1);
-        if (pending == RING - 4 && j > 0) {
-            wait_vm<MAXI *(RING - 4)>();  // steady state
-        } else {
-            switch (pending) {
-            case 0: wait_vm<0>(); break;
-            case 1: wait_vm<MAXI>(); break;
-            case 2: wait_vm<MAXI * 2>(); break;
-            case 3: wait_vm<MAXI * 3>(); break;
-            case 4: wait_vm<(MAXI * 4 < 64 ? MAXI * 4 : 0)>(); break;
-            case 5: wait_vm<(MAXI * 5 < 64 ? MAXI * 5 : 0)>(); break;
-            case 6: wait_vm<(MAXI * 6 < 64 ? MAXI * 6 : 0)>(); break;
-            default: wait_vm<0>(); break;
-            }
+        const int aslot = j & 1;
+        const bool refill = j + 2 < nkb;
+        const int kb_fill = refill ? kb0 + j + 2 : kb0;
+        const __amdgpu_buffer_rsrc_t fa = refill ? ra : rz;
+        const __amdgpu_buffer_rsrc_t fb = refill ? rb : rz;
+        const __amdgpu_buffer_rsrc_t fs = refill ? rs : rz;
+        const int bslot_next = bslot == 2 ? 0 : bslot + 1;
+        const int bslot_fill = bslot == 0 ? 2 : bslot - 1;  // (j + 2) % 3
+        // this block's A fragments and scales and its B(0), B(1) were read during the last
+        // step of the previous block
+        lds_wait();
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+            tie(Af[i][0]);
+            tie(Af[i][1]);
+            tie(Sf[i]);
         }
-        bare_barrier();  // all copies of block j have landed; block j-1's slots are free
-        // this block refills the ring with half RING-1 (block 0) or halves 2j+RING-2 and
-        // 2j+RING-1
-        const int h_first = (j == 0) ? RING - 1 : 2 * j + RING - 2;
-        const int n_iss = max(0, min((j == 0) ? 1 : 2, nhalf - h_first));
-        auto issue_copy = [&](int c) {  // c is a constant after unrolling
-            const int e = c / MAXI, i = c % MAXI;
-            if (e < n_iss) {
-                const int h = h_first + e;
-                const int slot = issue_slot + e >= RING ? issue_slot + e - RING : issue_slot + e;
-                // the address is formed at the issue point (kept from being hoisted and held
-                // in registers across the MFMA steps)
-                uint32_t o = coff[i];
-                asm volatile("" : "+v"(o));
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(cbase[i] + (int64_t)(kb0 + (h >> 1)) * cstride[i] +
-                                   (h & 1) * choff[i] + o),
-                    (DG_LDS void *)(ring + slot * HSLOT + cdst[i]), 16, 0, 0);
-            }
-        };
-        const int kb = kb0 + j;
-        if (j + 1 < nkb) {  // B scales of the next block, one iteration ahead
+        tie(Bf[0][0]);
+        tie(Bf[0][1]);
+        if constexpr (SN > 1) {
+            tie(Bf[1][0]);
+            tie(Bf[1][1]);
+        }
+        {  // B scales of the next block (of the last block again at the end)
+            const int kbn = min(kb0 + j + 1, KB - 1);
 #pragma unroll
             for (int jj = 0; jj < SN; ++jj)
-                sb_nxt[jj] = SFB[sb_off[jj] + kb + 1];
+                sb_nxt[jj] = SFB[sb_off[jj] + kbn];
         }
-        if (wave_active) {
-            const int slot1 = read_slot + 1 == RING ? 0 : read_slot + 1;
-            const uint32_t base = ring_base + (upper ? slot1 : read_slot) * HSLOT;
-            const uint32_t sa_addr = ring_base + read_slot * HSLOT + sa_off;
-            // Reads go out in the order B(0), then (A_i, A-scale_i) per sub-tile, then B(1);
-            // the first step waits for each A_i separately (LDS reads retire in order), so
-            // the MFMAs start as soon as their own operands land instead of after the whole
-            // burst that every wave issues right after the barrier.
-            static_assert(3 * (SM - 1) + 4 < 16, "lgkmcnt range");
-            v4i blo[SN], bhi[SN];
-            blo[0] = lds_read16(base + b_row_off + lo_off);
-            bhi[0] = lds_read16(base + b_row_off + hi_off);
-            v4i alo[SM], ahi[SM];
-            float sav[SM];
+        // every wave holds this block's A: its A slot may take block j+2; the B slot of block
+        // j-1 was released at the previous block's second barrier
+        bare_barrier();
+        issue_scales(kb_fill, aslot, fs);
+        if constexpr (SN == 1) {
 #pragma unroll
-            for (int i = 0; i < SM; ++i) {
-                alo[i] = lds_read16(base + a_row_off + i * 1024 + lo_off);
-                ahi[i] = lds_read16(base + a_row_off + i * 1024 + hi_off);
-                sav[i] = lds_read4(sa_addr + i * 64);
-            }
-            if constexpr (SN > 1) {
-                blo[1] = lds_read16(base + b_row_off + 1024 + lo_off);
-                bhi[1] = lds_read16(base + b_row_off + 1024 + hi_off);
-            }
-            // ring refill: after the block's first LDS reads so those are not queued behind
-            // the copies (each copy holds the wave's in-order issue until accepted)
+            for (int c = 0; c < MAXI; ++c)
+                issue_copy(c, kb_fill, aslot, bslot_fill, fa, fb);
+        }
+        // steps 0 .. SN-2, with this block's refill copies spread over them
 #pragma unroll
-            for (int c = 0; c < 2 * MAXI; ++c)
-                issue_copy(c);
-            // Step jj issues the SM MFMAs of fragment jj, each followed by the promotion of
-            // the partial of fragment jj-1 in the same row (issued SM MFMAs earlier, so its
-            // result is ready), with the reads of fragment jj+2 in flight.  The schedule
-            // barriers keep that interleave: the compiler would otherwise cluster the MFMAs.
-            v4f pend[SM];
-            // reads issued after the A reads and before the first step's waits: B(1), B(2)
-            constexpr int B1 = (SN > 1 ? 2 : 0) + (SN > 2 ? 2 : 0);
+        for (int jj = 0; jj + 1 < SN; ++jj) {
+            auto extra = [&](int i) {
+                if (i == 0 && jj + 2 < SN)
+                    read_b(bslot, jj + 2, Bf[bbuf(jj + 2, SN)]);
+                // copies c with c * (SN - 1) / MAXI == jj, after MFMAs 0, 2, ...
 #pragma unroll
-            for (int jj = 0; jj < SN; ++jj) {
-                const v8i bf = v8i{blo[jj].x, blo[jj].y, blo[jj].z, blo[jj].w,
-                                   bhi[jj].x, bhi[jj].y, bhi[jj].z, bhi[jj].w};
-                if (jj + 2 < SN) {
-                    blo[jj + 2] = lds_read16(base + b_row_off + (jj + 2) * 1024 + lo_off);
-                    bhi[jj + 2] = lds_read16(base + b_row_off + (jj + 2) * 1024 + hi_off);
-                }
-                v4f part[SM];
-#pragma unroll
-                for (int i = 0; i < SM; ++i) {
-                    if (jj == 0) {  // B(0) and A_i have landed once only younger reads remain
-                        lds_wait_le(3 * (SM - 1 - i) + B1);
-                        if (i == 0) {
-                            tie(blo[0]);
-                            tie(bhi[0]);
-                        }
-                        tie(alo[i]);
-                        tie(ahi[i]);
-                        tie(sav[i]);
+                for (int c = 0; c < MAXI; ++c) {
+                    if ((c * (SN - 1)) / MAXI == jj) {
+                        const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
+                        const int pos = c - first;
+                        if (i == (SM == 1 ? 0 : (pos * 2) % SM))
+                            issue_copy(c, kb_fill, aslot, bslot_fill, fa, fb);
                     }
-                    const v8i af = v8i{alo[i].x, alo[i].y, alo[i].z, alo[i].w,
-                                       ahi[i].x, ahi[i].y, ahi[i].z, ahi[i].w};
-                    part[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                    if (jj > 0)
-                        acc[i][jj - 1] += pend[i] * (sav[i] * sb_cur[jj - 1]);
-                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-                    pend[i] = part[i];
-                if (jj + 1 < SN) {
-                    if (jj + 2 < SN)
-                        lds_wait_n<2>();  // B(jj+1) has landed, B(jj+2) may be in flight
-                    else
-                        lds_wait_n<0>();
-                    tie(blo[jj + 1]);
-                    tie(bhi[jj + 1]);
-                }
+            };
+            if (jj >= 2) {
+                // B(jj) was read two steps ago; only B(jj+1), read one step ago, may be in
+                // flight (LDS reads retire in order)
+                lds_wait_n<2>();
+                tie(Bf[bbuf(jj, SN)][0]);
+                tie(Bf[bbuf(jj, SN)][1]);
             }
-#pragma unroll
-            for (int i = 0; i < SM; ++i)
-                acc[i][SN - 1] += pend[i] * (sav[i] * sb_cur[SN - 1]);
+            if (jj == 0)
+                mfma_step(0, Bf[0], [&](int i) { return psc[i]; }, extra);
+            else
+                mfma_step(jj, Bf[bbuf(jj, SN)], [&](int i) { return Sf[i] * sb_cur[jj - 1]; }, extra);
+        }
+        // last step: the next block's copies have landed everywhere (past the last block the
+        // reads below are harmless and unused)
+        wait_older_copies();
+        bare_barrier();
+        lds_wait();
+        if constexpr (SN >= 2) {
+            tie(Bf[bbuf(SN - 1, SN)][0]);
+            tie(Bf[bbuf(SN - 1, SN)][1]);
+        }
+        const int an = aslot ^ 1;
+        if constexpr (SN == 1) {
+            mfma_step(0, Bf[0],
+                      [&](int i) {
+                          const float prev = psc[i];
+                          psc[i] = Sf[i] * sb_cur[0];
+                          return prev;
+                      },
+                      [&](int i) {
+                          read_a(an, i);
+                          if (i == SM - 1)  // after the last MFMA that reads B(0)
+                              read_b(bslot_next, 0, Bf[0]);
+                      });
         } else {
-#pragma unroll
-            for (int c = 0; c < 2 * MAXI; ++c)
-                issue_copy(c);
+            mfma_step(SN - 1, Bf[bbuf(SN - 1, SN)],
+                      [&](int i) {
+                          psc[i] = Sf[i] * sb_cur[SN - 1];
+                          return Sf[i] * sb_cur[SN - 2];
+                      },
+                      [&](int i) {
+                          // B(0) (and B(1) when SN > 2) were last read steps ago; with
+                          // SN == 2, B(1) is this step's and is replaced after its last MFMA
+                          if (i == 0)
+                              read_b(bslot_next, 0, Bf[0]);
+                          if (i == (SN > 2 ? (SM > 1 ? 1 : 0) : SM - 1))
+                              read_b(bslot_next, 1, Bf[1]);
+                          read_a(an, i);
+                      });
         }
-        issue_slot += n_iss;
-        if (issue_slot >= RING)
-            issue_slot -= RING;
-        if (j + 1 < nkb) {
 #pragma unroll
-            for (int jj = 0; jj < SN; ++jj)
-                sb_cur[jj] = sb_nxt[jj];
-        }
-        read_slot = read_slot + 2 >= RING ? read_slot + 2 - RING : read_slot + 2;
+        for (int jj = 0; jj < SN; ++jj)
+            sb_cur[jj] = sb_nxt[jj];
+        bslot = bslot_next;
     }
+    // the last block also read (unused) fragments: they must land before their registers
+    // can be reused
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        tie(Af[i][0]);
+        tie(Af[i][1]);
+        tie(Sf[i]);
+    }
+    tie(Bf[0][0]);
+    tie(Bf[0][1]);
+    if constexpr (SN > 1) {
+        tie(Bf[1][0]);
+        tie(Bf[1][1]);
+    }
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+        acc[i][SN - 1] += pend[i] * psc[i];
     wait_vm<0>();  // no copy may still be writing LDS past this point
 
     // ---- split-K: publish the partial tile; the last arriving workgroup reduces in order
@@ -578,7 +657,7 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     return g;
 }
 
-template <int BM, int BN, int WM, int WN, int RING>
+template <int BM, int BN, int WM, int WN>
 static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
 {
     int tiles_m, tiles_n;
@@ -595,15 +674,15 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     dim3 g((unsigned)grid), b(cfg_threads);
     switch (mode) {
     case MODE_DENSE:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_DENSE>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_DENSE>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_CONTIG>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_CONTIG>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, RING, MODE_MASKED>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_MASKED>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     }
@@ -614,15 +693,15 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
 {
     switch (cfg) {
     case CFG_256x224:
-        return launch_cfg<256, 224, 4, 2, 5>(mode, a, stream);
+        return launch_cfg<256, 224, 4, 2>(mode, a, stream);
     case CFG_128x256:
-        return launch_cfg<128, 256, 2, 2, 6>(mode, a, stream);
+        return launch_cfg<128, 256, 2, 2>(mode, a, stream);
     case CFG_128x128:
-        return launch_cfg<128, 128, 2, 2, 6>(mode, a, stream);
+        return launch_cfg<128, 128, 2, 2>(mode, a, stream);
     case CFG_64x32:
-        return launch_cfg<64, 32, 2, 2, 8>(mode, a, stream);
+        return launch_cfg<64, 32, 2, 2>(mode, a, stream);
     case CFG_256x128:
-        return launch_cfg<256, 128, 4, 2, 6>(mode, a, stream);
+        return launch_cfg<256, 128, 4, 2>(mode, a, stream);
     default:
         return hipErrorInvalidValue;
     }
