@@ -85,17 +85,14 @@ int device_cus(int *out)
     return DG_OK;
 }
 
-// Split-K workspace: one per device, allocated on the first call that needs it while the
-// stream is not being captured, then reused.  Counters start at zero (hipMemset at
-// allocation) and every reduction resets its own counter.
+// Split-K workspace of the streaming kernel: one per device, allocated on the first call that
+// needs it while the stream is not being captured, then reused.  Calls that overlap on one
+// device (different streams) share it and must not run concurrently.
 struct Workspace {
     float *partials = nullptr;
-    int *counters = nullptr;
     size_t partial_floats = 0;
-    int counter_count = 0;
 };
 constexpr size_t kWsFloats = size_t(16) << 20;  // 64 MiB of FP32 partial tiles
-constexpr int kWsCounters = 1 << 16;
 
 int get_workspace(hipStream_t stream, Workspace **out)
 {
@@ -114,14 +111,7 @@ int get_workspace(hipStream_t stream, Workspace **out)
         }
         if (hipMalloc(&w.partials, kWsFloats * sizeof(float)) != hipSuccess)
             return fail(DG_ERR_HIP, "split-K workspace allocation failed");
-        if (hipMalloc(&w.counters, kWsCounters * sizeof(int)) != hipSuccess ||
-            hipMemset(w.counters, 0, kWsCounters * sizeof(int)) != hipSuccess) {
-            (void)hipFree(w.partials);
-            w.partials = nullptr;
-            return fail(DG_ERR_HIP, "split-K counter allocation failed");
-        }
         w.partial_floats = kWsFloats;
-        w.counter_count = kWsCounters;
     }
     *out = &w;
     return DG_OK;
@@ -200,39 +190,6 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     hipStream_t s = (hipStream_t)stream;
 
     const int kb = k / 128;
-    int cfg = forced_config();
-    int splits = 1;
-    if (cfg < 0) {
-        if (m <= 64) {
-            cfg = dg::CFG_64x32;
-        } else {
-            const int cands[] = {dg::CFG_256x224, dg::CFG_128x256, dg::CFG_128x128};
-            double best = 0;
-            for (int cnd : cands) {
-                const dg::TileInfo &t = dg::kTiles[cnd];
-                int64_t tiles = (int64_t)((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
-                double cost = tile_cost(t.bm, t.bn, tiles, cus);
-                if (cfg < 0 || cost < best) {
-                    best = cost;
-                    cfg = cnd;
-                }
-            }
-        }
-    }
-    const dg::TileInfo &ti = dg::kTiles[cfg];
-    const int64_t tiles = (int64_t)((m + ti.bm - 1) / ti.bm) * ((n + ti.bn - 1) / ti.bn);
-    // split K when the tiles cannot fill the CUs; at least 4 K blocks per split
-    if (tiles < cus) {
-        splits = (int)((cus + tiles - 1) / tiles);
-        if (splits > kb / 4)
-            splits = kb / 4;
-        if (splits < 1)
-            splits = 1;
-    }
-    int fs = forced_splits();
-    if (fs > 0)
-        splits = fs > kb ? kb : fs;
-
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;
     args.sfa = sfa;
@@ -246,15 +203,52 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     args.k = k;
     args.num_groups = 1;
     args.splits = 1;
-    if (splits > 1) {
-        Workspace *w = nullptr;
-        if ((rc = get_workspace(s, &w)) != DG_OK)
-            return rc;
-        if (w && (size_t)tiles * splits * ti.bm * ti.bn <= w->partial_floats &&
-            tiles <= w->counter_count) {
-            args.splits = splits;
-            args.ws = w->partials;
-            args.counters = w->counters;
+
+    // Pipelined tiles for shapes that fill the CUs; the split-K streaming kernel for skinny M
+    // and for shapes whose big tiles would leave most CUs idle.
+    int cfg = forced_config();
+    if (cfg < 0) {
+        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256, dg::CFG_128x128};
+        double best = 0;
+        int64_t best_tiles = 0;
+        for (int cnd : cands) {
+            const dg::TileInfo &t = dg::kTiles[cnd];
+            int64_t tiles = (int64_t)((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
+            double cost = tile_cost(t.bm, t.bn, tiles, cus);
+            if (cfg < 0 || cost < best) {
+                best = cost;
+                cfg = cnd;
+                best_tiles = tiles;
+            }
+        }
+        if (m <= 64 || 2 * best_tiles < cus)
+            cfg = dg::CFG_STREAM64;
+    }
+    if (cfg == dg::CFG_STREAM64) {
+        // one workgroup per (64x64 tile, split): enough splits to cover the CUs, never more
+        // than stream_max_kblocks() K blocks in one split, every split non-empty
+        const int64_t tiles = (int64_t)((m + 63) / 64) * ((n + 63) / 64);
+        const int maxkb = dg::stream_max_kblocks();
+        const int min_splits = (kb + maxkb - 1) / maxkb;
+        int want = (int)(tiles >= cus ? 1 : cus / tiles);
+        const int fs = forced_splits();
+        if (fs > 0)
+            want = fs;
+        want = want < min_splits ? min_splits : (want > kb ? kb : want);
+        const int kbs = (kb + want - 1) / want;
+        args.splits = (kb + kbs - 1) / kbs;
+        if (args.splits > 1) {
+            Workspace *w = nullptr;
+            if ((rc = get_workspace(s, &w)) != DG_OK)
+                return rc;
+            if (w && (size_t)tiles * args.splits * 64 * 64 <= w->partial_floats) {
+                args.ws = w->partials;
+            } else {
+                // no workspace (first call made under graph capture) or too little: the
+                // pipelined kernel without split-K is slower here but needs none
+                cfg = dg::CFG_64x32;
+                args.splits = 1;
+            }
         }
     }
     print_config("fp8_gemm_nt", m, n, k, 1, cfg, args.splits);
@@ -283,7 +277,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
     if ((rc = device_cus(&cus)) != DG_OK)
         return rc;
     int cfg = forced_config();
-    if (cfg < 0 || 128 % dg::kTiles[cfg].bm != 0)
+    if (cfg < 0 || cfg == dg::CFG_STREAM64 || 128 % dg::kTiles[cfg].bm != 0)
         cfg = (n % 256 == 0) ? dg::CFG_128x256 : dg::CFG_128x128;
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;
@@ -323,7 +317,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
         return rc;
     (void)expected_m;
     int cfg = forced_config();
-    if (cfg < 0)
+    if (cfg < 0 || cfg == dg::CFG_STREAM64)
         cfg = m_max > 128 ? dg::CFG_256x128 : dg::CFG_128x128;
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;

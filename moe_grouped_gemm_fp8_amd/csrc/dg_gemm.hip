@@ -29,26 +29,18 @@
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
 //    runs a contiguous range of tiles, rastered in groups of 4 M-tiles, so tiles that run
 //    together on one XCD share A rows and B columns in that XCD's L2.
-//  * Skinny dense shapes split K over workgroups: each writes an FP32 partial tile and the
-//    last one to arrive (atomic counter) sums the partials in split order and writes D.
+//  * Shapes too small to fill the CUs with these tiles go to the split-K streaming kernel
+//    (dg_stream.hip) instead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
 #include <utility>
 
+#include "dg_device.h"
 #include "dg_internal.h"
 
 namespace dg {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-#define DG_LDS __attribute__((address_space(3)))
-#define DG_CONST __attribute__((address_space(4)))  // read-only for the kernel: scalar loads
-
-constexpr int KBLK = 128;   // K block = scale granularity = MFMA depth
-constexpr int GROUP_M = 4;  // tile raster: M-tiles per group
 
 const TileInfo kTiles[CFG_COUNT] = {
     {256, 224, 512, "256x224w8"},
@@ -56,178 +48,8 @@ const TileInfo kTiles[CFG_COUNT] = {
     {128, 128, 256, "128x128w4"},
     {64, 32, 256, "64x32w4"},
     {256, 128, 512, "256x128w8"},
+    {64, 64, 256, "stream64"},
 };
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)  // NaN: keep it a (quiet) NaN
-        return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
-__device__ __forceinline__ void store_bf16x4(uint16_t *dst, v4f v)
-{
-    uint32_t lo = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
-    uint32_t hi = f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16);
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Same, for a wave-uniform count known only at run time (anything above 31 waits for all).
-__device__ __forceinline__ void wait_vm_dyn(int n)
-{
-    switch (n) {
-#define DG_WAIT_CASE(k) \
-    case k:             \
-        wait_vm<k>();   \
-        break;
-        DG_WAIT_CASE(1) DG_WAIT_CASE(2) DG_WAIT_CASE(3) DG_WAIT_CASE(4) DG_WAIT_CASE(5)
-        DG_WAIT_CASE(6) DG_WAIT_CASE(7) DG_WAIT_CASE(8) DG_WAIT_CASE(9) DG_WAIT_CASE(10)
-        DG_WAIT_CASE(11) DG_WAIT_CASE(12) DG_WAIT_CASE(13) DG_WAIT_CASE(14) DG_WAIT_CASE(15)
-        DG_WAIT_CASE(16) DG_WAIT_CASE(17) DG_WAIT_CASE(18) DG_WAIT_CASE(19) DG_WAIT_CASE(20)
-        DG_WAIT_CASE(21) DG_WAIT_CASE(22) DG_WAIT_CASE(23) DG_WAIT_CASE(24) DG_WAIT_CASE(25)
-        DG_WAIT_CASE(26) DG_WAIT_CASE(27) DG_WAIT_CASE(28) DG_WAIT_CASE(29) DG_WAIT_CASE(30)
-        DG_WAIT_CASE(31)
-#undef DG_WAIT_CASE
-    default:
-        wait_vm<0>();
-        break;
-    }
-}
-
-__device__ __forceinline__ void bare_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// LDS reads issued as inline asm (see the header comment).  Their results are valid only
-// after lds_wait() followed by tie() on each result, which orders every use after the wait.
-__device__ __forceinline__ v4i lds_read16(uint32_t addr)
-{
-    v4i v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-
-__device__ __forceinline__ float lds_read4(uint32_t addr)
-{
-    float v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-
-// The same with a compile-time byte offset in the instruction's offset field, so that reads of
-// one slot share a single base register and cost no address arithmetic.
-template <int OFF>
-__device__ __forceinline__ v4i lds_read16_at(uint32_t base)
-{
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    v4i v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
-    return v;
-}
-
-template <int OFF>
-__device__ __forceinline__ float lds_read4_at(uint32_t base)
-{
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    float v;
-    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
-    return v;
-}
-
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// All but the N most recent LDS reads have landed (LDS reads retire in order; outstanding
-// scalar loads only make the condition stricter).
-template <int N>
-__device__ __forceinline__ void lds_wait_n()
-{
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
-// lds_wait_n for a count that is a constant only after loop unrolling
-__device__ __forceinline__ void lds_wait_le(int n)
-{
-    switch (n) {
-#define DG_LGKM_CASE(k)    \
-    case k:                \
-        lds_wait_n<k>();   \
-        break;
-        DG_LGKM_CASE(1) DG_LGKM_CASE(2) DG_LGKM_CASE(3) DG_LGKM_CASE(4) DG_LGKM_CASE(5)
-        DG_LGKM_CASE(6) DG_LGKM_CASE(7) DG_LGKM_CASE(8) DG_LGKM_CASE(9) DG_LGKM_CASE(10)
-        DG_LGKM_CASE(11) DG_LGKM_CASE(12) DG_LGKM_CASE(13) DG_LGKM_CASE(14) DG_LGKM_CASE(15)
-#undef DG_LGKM_CASE
-    default:
-        lds_wait_n<0>();
-        break;
-    }
-}
-__device__ __forceinline__ void tie(v4i &v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ void tie(float &v) { asm volatile("" : "+v"(v)); }
-
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: loop indices usable as constants.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
-{
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Workgroup id -> tile id such that XCD x (ids x, x+8, x+16, ...) gets one contiguous range.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk)
-{
-    int q = nblk >> 3, r = nblk & 7, xcd = bid & 7, loc = bid >> 3;
-    return (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
-}
-
-// Tile id -> (tm, tn) in groups of GROUP_M M-tiles, N fastest within a group column.
-__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm, int &tn)
-{
-    int per_group = GROUP_M * tiles_n;
-    int grp = t / per_group;
-    int first = grp * GROUP_M;
-    int gsz = min(tiles_m - first, GROUP_M);
-    int rem = t - grp * per_group;
-    tm = first + rem % gsz;
-    tn = rem / gsz;
-}
-
-// 128-bit buffer resource for raw (unstrided) loads of `bytes` bytes from `base`: any lane
-// whose offset falls outside the range reads zeros instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-
-// Register buffer that holds B fragment jj (of SN per block).  Fragment jj+2 is read while
-// jj is in use and jj+1 may be in flight, and the next block's fragments 0 and 1 are read
-// while fragment SN-1 is in use, so any three consecutive fragments (across the block
-// boundary too) need distinct buffers: jj % 3, except that the last one takes buffer 3 when
-// jj % 3 would collide with the next block's 0 or 1.
-__host__ __device__ constexpr int bbuf(int jj, int sn)
-{
-    return (jj == sn - 1 && sn > 2 && (jj % 3) != 2) ? 3 : jj % 3;
-}
-__host__ __device__ constexpr int bbuf_count(int sn)
-{
-    return sn <= 3 ? sn : ((sn - 1) % 3 == 2 ? 3 : 4);
-}
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int tiles_n)
@@ -275,8 +97,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
 
     // ---- which tile, which group, which rows are valid
     int t = xcd_remap(blockIdx.x, gridDim.x);
-    int tm, tn, split = 0, g = 0, row_limit;
-    int kb0 = 0, kb1 = KB;
+    int tm, tn, g = 0, row_limit;
+    const int kb0 = 0, kb1 = KB;
     const uint8_t *A = p.a;
     const float *SFA = p.sfa;
     uint16_t *D = p.d;
@@ -310,12 +132,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
             return;  // a block of padding rows only
         row_limit = p.m;
     } else {
-        if (p.splits > 1) {
-            split = t % p.splits;
-            t /= p.splits;
-            kb0 = split * KB / p.splits;
-            kb1 = (split + 1) * KB / p.splits;
-        }
         raster(t, tiles_m, tiles_n, tm, tn);
         row_limit = p.m;
     }
@@ -696,54 +512,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         acc[i][SN - 1] += pend[i] * psc[i];
     wait_vm<0>();  // no copy may still be writing LDS past this point
 
-    // ---- split-K: publish the partial tile; the last arriving workgroup reduces in order
-    if constexpr (MODE == MODE_DENSE) {
-        if (p.splits > 1) {
-            const int tile = tm * tiles_n + tn;
-            float *ws_tile = p.ws + (int64_t)tile * p.splits * (BM * BN);
-#pragma unroll
-            for (int i = 0; i < SM; ++i)
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-                    *reinterpret_cast<v4f *>(ws_tile + (int64_t)split * BM * BN +
-                                             ((i * SN + j) * NT + tid) * 4) = acc[i][j];
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) {
-                int prev = atomicAdd(p.counters + tile, 1);
-                int last = prev == p.splits - 1;
-                if (last)
-                    atomicExch(p.counters + tile, 0);  // ready for the next call
-                s_flag = last;
-            }
-            __syncthreads();
-            if (!s_flag)
-                return;
-            __threadfence();
-            // sum the partials in split order; each split's whole partial tile is requested
-            // before any of it is added, so the loads overlap
-#pragma unroll
-            for (int i = 0; i < SM; ++i)
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-                    acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < p.splits; ++s) {
-                v4f part[SM][SN];
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SN; ++j)
-                        part[i][j] = *reinterpret_cast<const v4f *>(
-                            ws_tile + (int64_t)s * BM * BN + ((i * SN + j) * NT + tid) * 4);
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SN; ++j)
-                        acc[i][j] += part[i][j];
-            }
-        }
-    }
-
     // ---- epilogue: + C, round to bf16, store the valid rows.  All of the wave's C values (and
     // row groups) are requested before any is used, so the loads overlap instead of each
     // waiting for the one before; C goes through a buffer resource bounded by the valid rows,
@@ -809,13 +577,13 @@ static void tiles_for(int mode, int cfg, const GemmArgs &a, int &tiles_m, int &t
 
 int64_t grid_size(int mode, int cfg, const GemmArgs &a)
 {
+    if (cfg == CFG_STREAM64)
+        return mode == MODE_DENSE ? stream_grid_size(a) : -1;
     int tiles_m, tiles_n;
     tiles_for(mode, cfg, a, tiles_m, tiles_n);
     int64_t g = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         g *= a.num_groups;
-    if (mode == MODE_DENSE)
-        g *= a.splits;
     return g;
 }
 
@@ -829,8 +597,6 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     int64_t grid = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         grid *= a.num_groups;
-    if (mode == MODE_DENSE)
-        grid *= a.splits;
     if (grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     dim3 g((unsigned)grid), b(cfg_threads);
@@ -864,6 +630,8 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
         return launch_cfg<64, 32, 2, 2>(mode, a, stream);
     case CFG_256x128:
         return launch_cfg<256, 128, 4, 2>(mode, a, stream);
+    case CFG_STREAM64:
+        return mode == MODE_DENSE ? launch_stream(a, stream) : hipErrorInvalidValue;
     default:
         return hipErrorInvalidValue;
     }

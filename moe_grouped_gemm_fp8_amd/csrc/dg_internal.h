@@ -17,6 +17,7 @@ enum TileCfg : int {
     CFG_128x128 = 2,  // 4 waves (2x2), wave tile 64x64
     CFG_64x32 = 3,    // 4 waves (2x2), wave tile 32x16: skinny M with split-K
     CFG_256x128 = 4,  // 8 waves (4x2), wave tile 64x64: masked decode, one tile spans m_max
+    CFG_STREAM64 = 5, // split-K streaming kernel, 64x64 tiles, <= 8 K blocks per split: skinny M
     CFG_COUNT
 };
 
@@ -38,9 +39,8 @@ struct GemmArgs {
     int m;                // dense: M; contiguous: m_total; masked: m_max
     int n, k;
     int num_groups;
-    int splits;           // dense split-K factor (1 = none)
-    float *ws;            // split-K partial tiles
-    int *counters;        // split-K arrival counters, one per output tile, self-resetting
+    int splits;           // split-K factor of the streaming kernel (1 = none)
+    float *ws;            // split-K partial tiles (streaming kernel, splits > 1)
 };
 
 // Grid size in workgroups for a launch (host-side, no HIP call).
@@ -48,5 +48,11 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &args);
 
 // Launches the kernel for (mode, cfg) on `stream`; returns the HIP error of the launch.
 hipError_t launch_gemm(int mode, int cfg, const GemmArgs &args, hipStream_t stream);
+
+// The split-K streaming kernel (dense form only): grid size, the most K blocks one split may
+// hold, and the launch (rejects a split count that leaves a split empty or too long).
+int64_t stream_grid_size(const GemmArgs &args);
+int stream_max_kblocks();
+hipError_t launch_stream(const GemmArgs &args, hipStream_t stream);
 
 }  // namespace dg

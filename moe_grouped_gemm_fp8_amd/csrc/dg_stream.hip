@@ -1,0 +1,273 @@
+// Split-K streaming form of the fine-grained-scaled FP8 GEMM D = C + A @ B.T (NT layout; one
+// FP32 scale per 1x128 segment of an A row and per 128x128 block of B; DeepGEMM pages:
+// pt.news.hada.io, "Interface GEMM e restrições de layout"; feifmx.com release article,
+// two-level accumulation) for skinny M, where the work is reading B once from HBM.
+//
+// Design:
+//  * A workgroup owns a 64 x 64 output tile and a range of at most 8 K blocks (a split).  Its
+//    whole share of A, B and both scale sets is requested up front as direct-to-LDS copies
+//    (up to 128 KB in flight per workgroup), in K-block order, and each block is consumed as
+//    soon as its own copies have landed, while the later blocks are still arriving.
+//  * Four waves, one 16-column slice of B each; a wave runs one v_mfma_f32_16x16x128_f8f6f4
+//    per (16-row A sub-tile, K block) and promotes the partial with sa * sb into FP32
+//    accumulators, exactly as the pipelined kernels do.
+//  * With several splits, each writes its FP32 partial tile to a workspace and a second
+//    kernel sums the partials in split order (deterministic), adds C, rounds to bf16 and
+//    stores the valid rows and columns.  The kernel boundary makes the partials visible; a
+//    fence-and-counter handshake inside one kernel would need a device-scope release per
+//    workgroup, which on this part writes back and invalidates the XCD's whole L2.
+//  * LDS rows are 128 bytes with the same chunk swizzle as the pipelined kernels
+//    (c ^ h(r), h(r) = r3 | r1 << 1 | r2 << 2), so the 16-row fragment reads are conflict free.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+constexpr int ST_BM = 64;   // tile rows
+constexpr int ST_BN = 64;   // tile columns (4 waves x 16)
+constexpr int ST_KSB = 8;   // K blocks per split at most
+
+__device__ __forceinline__ void stream_epilogue(const GemmArgs &p, v4f (&acc)[4], int m0, int n0,
+                                                int wave, int fr, int fg)
+{
+    // + C (all loads first), round to bf16, store the valid rows and columns
+    const int M = p.m, N = p.n;
+    const int col = n0 + wave * 16 + 4 * fg;
+    if (p.c) {
+        const __amdgpu_buffer_rsrc_t rcc =
+            make_rsrc(p.c + (int64_t)m0 * N, (int64_t)(M - m0) * N * 4);
+        v4f cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cv[i] = __builtin_bit_cast(
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                         rcc, (uint32_t)(((i * 16 + fr) * N + col) * 4), 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[i] += cv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + i * 16 + fr;
+        if (row < M && col < N)
+            store_bf16x4(p.d + (int64_t)row * N + col, acc[i]);
+    }
+}
+
+__global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m, int tiles_n)
+{
+    constexpr int A_SLOT = ST_BM * KBLK;             // one K block of the tile's A rows
+    constexpr int B_SLOT = ST_BN * KBLK;
+    constexpr int B_BASE = ST_KSB * A_SLOT;          // 64 KB
+    constexpr int SA_BASE = B_BASE + ST_KSB * B_SLOT;  // 128 KB: 64 A scales per K block
+    constexpr int SB_BASE = SA_BASE + ST_KSB * 256;    // B scales, one per K block
+    constexpr int LDS_BYTES = SB_BASE + 256;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = p.k, N = p.n, M = p.m;
+    const int KB = K / KBLK;
+    const int NB = (N + KBLK - 1) / KBLK;
+    const int64_t ld = p.ld_sfa;
+
+    // workgroup id -> (m tile, n tile, split); splits of one tile are adjacent ids, so they
+    // land on different XCDs and finish at about the same time
+    int t = blockIdx.x;
+    const int split = t % p.splits;
+    t /= p.splits;
+    const int tn = t % tiles_n;
+    const int tm = t / tiles_n;
+    const int kbs = (KB + p.splits - 1) / p.splits;  // <= ST_KSB (host-checked)
+    const int kb0 = split * kbs;
+    const int nk = min(kbs, KB - kb0);               // >= 1 (host-checked)
+    const int m0 = tm * ST_BM, n0 = tn * ST_BN;
+
+    // ---- the whole split's operands, as direct-to-LDS copies.  Copy c < 8*nk is A rows
+    // [8q, 8q+8) of K block c/8 (q = c % 8), the rest likewise for B.  Lane l of a copy fetches
+    // row 8q + l/8, logical chunk (l & 7) ^ h(row): the contiguous 1 KB it writes is the
+    // swizzled layout.  Rows past M or N read zeros (buffer range), never stored.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * K, (int64_t)(M - m0) * K);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (int64_t)KB * ld * 4);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sfb, (int64_t)NB * KB * 4);
+    DG_LDS uint8_t *ldsp = (DG_LDS uint8_t *)lds;
+    const uint32_t lane_even = (uint32_t)(lane >> 3) * (uint32_t)K +
+                               (uint32_t)((((lane & 7) ^ ((lane >> 4) << 1))) << 4);
+    // scales first (older than every operand copy, so each block's wait below covers them):
+    // A scales one 4-byte-per-lane copy per K block (lane = tile row); B scales one copy, the
+    // tile's 64 columns lying in one 128-column block (n0 % 128 is 0 or 64), lane l < nk taking
+    // K block kb0 + l and the other lanes reading outside the resource (zeros)
+    for (int kb = wave; kb < nk; kb += 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (DG_LDS void *)(ldsp + SA_BASE + kb * 256), 4,
+            (uint32_t)(((int64_t)(kb0 + kb) * ld + m0 + lane) * 4), 0, 0, 0);
+    if (wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsb, (DG_LDS void *)(ldsp + SB_BASE), 4,
+            lane < nk ? (uint32_t)(((n0 / KBLK) * KB + kb0 + lane) * 4) : 0x80000000u, 0, 0, 0);
+    // operands, K block by K block: block kb's 16 copies (8 of A rows, 8 of B rows) are four
+    // per wave, copy 4u + wave of the block
+    for (int kb = 0; kb < nk; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int cc = 4 * u + wave;  // 0..7: A row group cc; 8..15: B row group cc - 8
+            const int q = cc & 7;
+            const uint32_t vo =
+                (lane_even ^ (uint32_t)((q & 1) << 4)) + (uint32_t)(8 * q) * (uint32_t)K;
+            if (cc < 8)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (DG_LDS void *)(ldsp + kb * A_SLOT + q * 1024), 16, vo,
+                    (uint32_t)(kb0 + kb) * KBLK, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (DG_LDS void *)(ldsp + B_BASE + kb * B_SLOT + q * 1024), 16, vo,
+                    (uint32_t)(kb0 + kb) * KBLK, 0, 0);
+        }
+    }
+
+    // ---- MFMAs: wave w owns columns [n0 + 16w, n0 + 16w + 16) and all 64 rows (4 sub-tiles)
+    const int fr = lane & 15, fg = lane >> 4;
+    const int fh = ((fr >> 3) & 1) | (fr & 2) | (((fr >> 2) & 1) << 2);  // h(fr)
+    const int f_lo = fr * KBLK + (((2 * fg) ^ fh) << 4);
+    const int f_hi = fr * KBLK + (((2 * fg + 1) ^ fh) << 4);
+    // LDS reads are inline asm with an explicit wait: plain loads would make the compiler
+    // wait for every outstanding copy before the first of them (it cannot tell which slot a
+    // copy writes), which would undo the per-block overlap
+    const uint32_t base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)lds;
+    v4f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    // fragments of one K block: B slice, four A sub-tiles, their scales, the B scale
+    v4i b0, b1, a0[4], a1[4];
+    float sa[4], sb;
+    auto read_block = [&](int kb) {
+        const uint32_t as = base + (uint32_t)(kb * A_SLOT);
+        const uint32_t bs = base + (uint32_t)(B_BASE + kb * B_SLOT + wave * 16 * KBLK);
+        b0 = lds_read16(bs + f_lo);
+        b1 = lds_read16(bs + f_hi);
+        sb = lds_read4(base + SB_BASE + kb * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a0[i] = lds_read16(as + i * 16 * KBLK + f_lo);
+            a1[i] = lds_read16(as + i * 16 * KBLK + f_hi);
+            sa[i] = lds_read4(base + SA_BASE + kb * 256 + (i * 16 + fr) * 4);
+        }
+    };
+    // block kb's copies (and, being older, the scales) have landed once at most the later
+    // blocks' 4 copies each are outstanding; the barrier covers the other waves' copies
+    auto land = [&](int kb) {
+        wait_vm_dyn(4 * (nk - 1 - kb));
+        bare_barrier();  // no fence: a workgroup fence would wait for every copy in flight
+    };
+    land(0);
+    read_block(0);
+    for (int kb = 0; kb < nk; ++kb) {
+        lds_wait();
+        tie(b0);
+        tie(b1);
+        tie(sb);
+        const v8i bv = v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        v8i av[4];
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tie(a0[i]);
+            tie(a1[i]);
+            tie(sa[i]);
+            av[i] = v8i{a0[i].x, a0[i].y, a0[i].z, a0[i].w, a1[i].x, a1[i].y, a1[i].z, a1[i].w};
+            sc[i] = sa[i] * sb;
+        }
+        if (kb + 1 < nk) {  // the next block's reads overlap this block's MFMAs
+            land(kb + 1);
+            read_block(kb + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bv, av[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            acc[i] += part * sc[i];
+        }
+    }
+
+    // ---- several splits: publish this split's partial tile (the reduce kernel finishes it)
+    if (p.splits > 1) {
+        float *ws_tile = p.ws + ((int64_t)(tm * tiles_n + tn) * p.splits + split) * (ST_BM * ST_BN);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<v4f *>(ws_tile + (i * 256 + tid) * 4) = acc[i];
+        return;
+    }
+    stream_epilogue(p, acc, m0, n0, wave, fr, fg);
+}
+
+// Sums the splits' partial tiles in split order, then + C, bf16, store.  Workgroup (tile, i)
+// finishes the tile's rows i*16 .. i*16+15: each thread one 16-byte slice, with the slices of
+// all splits requested before any is added (one round trip instead of one per split).
+
+__global__ __launch_bounds__(256) void dg_stream_reduce_kernel(GemmArgs p, int tiles_n)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tile = blockIdx.x >> 2, i = blockIdx.x & 3;
+    const int tn = tile % tiles_n, tm = tile / tiles_n;
+    const int fr = lane & 15, fg = lane >> 4;
+    const float *src = p.ws + (int64_t)tile * p.splits * (ST_BM * ST_BN) + (i * 256 + tid) * 4;
+    v4f part[8];
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {  // up to 8 splits in flight, added in order
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < p.splits)
+                part[u] = *reinterpret_cast<const v4f *>(src + (int64_t)(s0 + u) * ST_BM * ST_BN);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < p.splits)
+                acc += part[u];
+    }
+    const int M = p.m, N = p.n;
+    const int row = tm * ST_BM + i * 16 + fr;
+    const int col = tn * ST_BN + wave * 16 + 4 * fg;
+    if (row < M && col < N) {
+        if (p.c)
+            acc += *reinterpret_cast<const v4f *>(p.c + (int64_t)row * N + col);
+        store_bf16x4(p.d + (int64_t)row * N + col, acc);
+    }
+}
+
+int64_t stream_grid_size(const GemmArgs &a)
+{
+    const int tiles_m = (a.m + ST_BM - 1) / ST_BM;
+    const int tiles_n = (a.n + ST_BN - 1) / ST_BN;
+    return (int64_t)tiles_m * tiles_n * a.splits;
+}
+
+int stream_max_kblocks() { return ST_KSB; }
+
+hipError_t launch_stream(const GemmArgs &a, hipStream_t stream)
+{
+    const int tiles_m = (a.m + ST_BM - 1) / ST_BM;
+    const int tiles_n = (a.n + ST_BN - 1) / ST_BN;
+    const int kb = a.k / KBLK;
+    const int kbs = (kb + a.splits - 1) / a.splits;
+    if (a.splits < 1 || kbs > ST_KSB || (int64_t)(a.splits - 1) * kbs >= kb)
+        return hipErrorInvalidValue;  // every split must hold 1..ST_KSB K blocks
+    const int64_t grid = stream_grid_size(a);
+    if (grid <= 0 || grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(dg_stream_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, tiles_m,
+                       tiles_n);
+    if (a.splits > 1)
+        hipLaunchKernelGGL(dg_stream_reduce_kernel, dim3((unsigned)(tiles_m * tiles_n * 4)),
+                           dim3(256), 0, stream, a, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace dg

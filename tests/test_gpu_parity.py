@@ -17,7 +17,7 @@ from gpu_util import (DEV, assert_parity, bits, dense_rows_ref, dev, run_contigu
 
 pytestmark = pytest.mark.gpu
 
-TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8"]
+TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "stream64"]
 
 
 def _say(msg):
@@ -74,7 +74,7 @@ def test_dense_empty_is_a_noop():
 
 @pytest.mark.parametrize("splits", [2, 3, 7])
 def test_dense_forced_split_k_with_ragged_tiles(splits, monkeypatch):
-    monkeypatch.setenv("DG_FORCE_CONFIG", "128x128w4")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "stream64")
     monkeypatch.setenv("DG_FORCE_SPLITS", str(splits))
     p = W.make_dense(200, 336, 1024, seed=25, with_c=True)
     assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"split{splits}")
