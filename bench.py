@@ -29,6 +29,7 @@ METRIC = "FP8 block-scaled GEMM TFLOPS (and % of FP8 MFMA / HBM roofline) at 1 G
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 ROTATE_BYTES = 1.2e9          # total bytes of rotated input copies per workload
+GRAPH_STEPS = 8               # steps captured back to back in one graph
 
 
 def log(msg: str):
@@ -37,7 +38,7 @@ def log(msg: str):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("dg_gemm.hip", "dg_api.cpp", "dg_internal.h"):
+    for f in ("dg_gemm.hip", "dg_stream.hip", "dg_api.cpp", "dg_device.h", "dg_internal.h"):
         with open(os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,6 +87,46 @@ def _copies(torch, tensors, set_bytes):
     return out
 
 
+def _capture(torch, sets, call, per_graph=1):
+    """Captured graphs over the input copies, as (singles, multi): singles[i] replays the
+    library call once on copy i; multi[g] replays it on copies per_graph*g ..
+    per_graph*(g+1)-1 in turn, so that back-to-back steps run without a host-side launch
+    between them.  An uncaptured call on each copy comes first, on a side stream, so lazily
+    allocated state exists before capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in sets:
+            call(s)
+    torch.cuda.current_stream().wait_stream(side)
+
+    def cap(chunk):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for s in chunk:
+                call(s)
+        return gr
+
+    singles = [cap([s]) for s in sets]
+    multi = [cap(sets[g0:g0 + per_graph]) for g0 in range(0, len(sets) - per_graph + 1, per_graph)]
+    torch.cuda.synchronize()
+    return singles, multi
+
+
+def _graph_launcher(c, singles, multi, per_graph):
+    """launch(i, n) runs steps i .. i+n-1: one single-step replay, or (n == per_graph) one
+    replay of a multi-step graph."""
+    c.cycle = per_graph if multi else 1
+
+    def launch(i, n=1):
+        if n == 1:
+            singles[i % len(singles)].replay()
+        else:
+            assert n == c.cycle
+            multi[(i // n) % len(multi)].replay()
+    c.launch = launch
+
+
 def make_dense_case(torch, dg, W, name):
     p = W.make_config(name, seed=0)
     c = Case(name)
@@ -96,14 +137,15 @@ def make_dense_case(torch, dg, W, name):
     nbytes = (p.m * p.k + p.n * p.k + 4 * p.m * kb + 4 * nb * kb + 2 * p.m * p.n
               + (4 * p.m * p.n if p.c is not None else 0))
     c.sets = _copies(torch, t, nbytes)
-    c.config = dict(workload=name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
-                    d="bf16", rotating_copies=len(c.sets))
+    per_graph = min(len(c.sets), GRAPH_STEPS)
 
-    def launch(i):
-        s = c.sets[i % len(c.sets)]
+    def call(s):
         dg.fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["c"])
 
-    c.launch = launch
+    _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
+    c.config = dict(workload=name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
+                    d="bf16", launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
     c.flops = lambda i: 2.0 * p.m * p.n * p.k
     c.bytes = lambda i: float(nbytes)
     c.problem = p
@@ -122,14 +164,16 @@ def make_contiguous_case(torch, dg, W):
     nbytes = (valid * p.k + used * p.n * p.k + 4 * valid * kb + 4 * used * nb * kb
               + 2 * valid * p.n + 4 * p.m_total)
     c.sets = _copies(torch, t, nbytes)
-    c.config = dict(workload="moe_contiguous", groups=p.num_groups, valid_rows=valid,
-                    padded_rows=p.m_total, n=p.n, k=p.k, rotating_copies=len(c.sets))
+    per_graph = min(len(c.sets), GRAPH_STEPS)
 
-    def launch(i):
-        s = c.sets[i % len(c.sets)]
+    def call(s):
         dg.m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["idx"])
 
-    c.launch = launch
+    _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
+    c.config = dict(workload="moe_contiguous", groups=p.num_groups, valid_rows=valid,
+                    padded_rows=p.m_total, n=p.n, k=p.k,
+                    launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
     c.flops = lambda i: 2.0 * valid * p.n * p.k
     c.bytes = lambda i: float(nbytes)
     return c
@@ -147,18 +191,8 @@ def make_masked_case(torch, dg, W):
     c.sets = _copies(torch, t, set_bytes)
     table = [W.masked_counts(g, m_max, seed=0, replay=r) for r in range(16)]
     table_dev = [_dev(torch, x) for x in table]
-    graphs = []
-    for s in c.sets:                      # one captured graph per input copy
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            dg.m_grouped_fp8_gemm_nt_masked(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"])
-        torch.cuda.current_stream().wait_stream(side)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            dg.m_grouped_fp8_gemm_nt_masked(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"])
-        graphs.append(gr)
-    torch.cuda.synchronize()
+    graphs, _ = _capture(torch, c.sets, lambda s: dg.m_grouped_fp8_gemm_nt_masked(
+        s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"]))
     c.config = dict(workload="moe_masked", groups=g, m_max=m_max, n=n, k=k,
                     masked_m="U{0..256} per group, a new draw per replay (16 draws)",
                     launched_as="captured graph replay", rotating_copies=len(c.sets))
@@ -167,7 +201,7 @@ def make_masked_case(torch, dg, W):
         s = c.sets[i % len(c.sets)]
         s["mm"].copy_(table_dev[i % len(table)])   # device-side update between replays
 
-    def launch(i):
+    def launch(i, n=1):
         graphs[i % len(graphs)].replay()
 
     def flops(i):
@@ -189,42 +223,62 @@ def make_masked_case(torch, dg, W):
 def time_case(torch, case, steps, warmup):
     """Warm up, then time exactly `steps` steps as one region bracketed by HIP events on the
     launch stream (the step time and, for cases without a per-step device update, the kernel's
-    average launch duration); then a second pass with an event pair around every launch gives
-    the spread (and the average for cases whose update copy must stay outside the pair)."""
+    average launch duration); then a second pass with an event pair around every replay gives
+    the spread (and the average for cases whose update copy must stay outside the pair).
+    Cases captured `cycle` steps to a graph run whole graphs while at least `cycle` steps
+    remain and single-step graphs for the rest, so the count stays exact."""
+    cyc = getattr(case, "cycle", 1)
     prep = getattr(case, "prepare", None)
-    for i in range(warmup):
-        if prep:
-            prep(i)
-        case.launch(i)
+
+    def chunks(start, count):
+        i = 0
+        while i < count:
+            n = cyc if (cyc > 1 and count - i >= cyc) else 1
+            yield start + i, n
+            i += n
+
+    # warm-up: the requested steps, then more until half a second has passed, so that clocks
+    # and caches are in their steady state when the timed region starts
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_w < 0.5:
+        for i, n in chunks(done, max(cyc, 16)):
+            if prep:
+                prep(i)
+            case.launch(i, n)
+        done += max(cyc, 16)
+        torch.cuda.synchronize()
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_all0.record()
-    for i in range(steps):
+    for i, n in chunks(warmup, steps):
         if prep:
-            prep(warmup + i)
-        case.launch(warmup + i)
+            prep(i)
+        case.launch(i, n)
     t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total = t_all0.elapsed_time(t_all1) * 1e-3
+    plan = list(chunks(warmup, steps))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
+          for _ in plan]
+    for (i, n), (e0, e1) in zip(plan, ev):
         if prep:
-            prep(warmup + i)
-        ev[i][0].record()
-        case.launch(warmup + i)
-        ev[i][1].record()
+            prep(i)
+        e0.record()
+        case.launch(i, n)
+        e1.record()
     torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3       # seconds per launch
+    per = np.concatenate([np.full(n, e0.elapsed_time(e1) * 1e-3 / n)
+                          for (i, n), (e0, e1) in zip(plan, ev)])   # seconds per step
     flops = np.array([case.flops(warmup + i) for i in range(steps)])
     nbytes = np.array([case.bytes(warmup + i) for i in range(steps)])
     avg = per.mean() if prep else total / steps
     return dict(total_s=total, wall_s=wall, per_launch_s=per, avg_s=avg,
                 timing="per-launch event pairs" if prep else "timed region / steps",
-                flops=flops, bytes=nbytes)
+                steps=steps, flops=flops, bytes=nbytes)
 
 
 def summarize(res):
@@ -344,7 +398,8 @@ def main():
             del case
             torch.cuda.empty_cache()
 
-    case, res, summ, steps = head
+    case, res, summ, _ = head
+    steps = res["steps"]
     total_flops = float(res["flops"].sum())
     value = total_flops / res["total_s"] / 1e12
     dom = case.name

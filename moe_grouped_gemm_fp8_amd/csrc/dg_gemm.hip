@@ -70,8 +70,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     constexpr int B_BASE = 2 * A_SLOT;
     constexpr int SA_BASE = B_BASE + 3 * B_SLOT;
     constexpr int SB_BASE = SA_BASE + 2 * 1024;
-    constexpr int TOUCH_BASE = SB_BASE + 2 * 256;  // 256 bytes per wave, never read
-    constexpr int LDS_BYTES = TOUCH_BASE + (MODE == MODE_DENSE ? NW * 256 : 0);
+    constexpr int LDS_BYTES = SB_BASE + 2 * 256;
     static_assert(A_SLOT % 4096 == 0 && B_SLOT % 4096 == 0, "slots start on 4 KB boundaries");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
@@ -240,36 +239,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     const uint32_t sb_hi_addr = lds_base + SB_BASE + (uint32_t)(nb_hi - nb_first) * 4;
     float vsb_lo, vsb_hi;  // this block's two B scales (all lanes equal)
 
-    // C prefetch (dense form): during the K loop each wave touches the C rows its epilogue
-    // reads, one dword per 128-byte line, so C moves from HBM into the memory-side cache while
-    // the MFMAs run instead of in one burst in the epilogue.  A touch is a 4-byte-per-lane
-    // direct-to-LDS copy into a scratch area nobody reads (no register is written), issued at
-    // the start of a block before that block's copies, so the block's copy wait covers it.
-    // Lane l touches wave row wm + l (lanes past TM get an offset outside every resource),
-    // line cl of the wave's TN * 4 bytes of C in that row.
-    static_assert(TM <= 64, "one C row per lane");
-    constexpr int C_LINES = (TN * 4 + 127) / 128;  // lines per row (+1 for a straddling start)
-    int c_first = 0;                               // first block that touches
+    // C, streamed into the accumulators (dense form).  Half h of column jj of the wave's
+    // sub-tiles (acc[i][jj] for the SM/2 row sub-tiles i of that half) takes its C values at
+    // step jj of block c_j0 + 2 jj + h, from registers cb loaded one block earlier (right
+    // after the previous half's add; the first half in the prologue).  The C traffic is thus
+    // spread over the K loop instead of arriving in one burst in the epilogue, with a block of
+    // compute to hide each load, and every add uses a compile-time accumulator index.
+    // Columns whose blocks lie past the last K block (short K) take C in the epilogue.
+    bool stream_c = false;
+    int c_j0 = 0;
     __amdgpu_buffer_rsrc_t rc = rz;
-    uint32_t c_row = 0x80000000u;
+    uint32_t c_lane = 0;
     if constexpr (MODE == MODE_DENSE) {
-        c_first = max(0, nkb - C_LINES - 3);
-        if (p.c != nullptr)
+        stream_c = p.c != nullptr;
+        c_j0 = max(0, nkb - 2 * SN);  // all columns streamed when nkb >= 2 SN
+        if (stream_c)
             rc = make_rsrc(p.c + (int64_t)m0 * N, (int64_t)(row_limit - m0) * N * 4);
-        if (lane < TM)
-            c_row = (uint32_t)(((wm + lane) * N + n0 + wn) * 4);
+        c_lane = (uint32_t)(((wm + fr) * N + n0 + wn + 4 * fg) * 4);
     }
-    auto touch_c = [&](int j) {
-        if constexpr (MODE == MODE_DENSE) {
-            const int cl = j - c_first;
-            // the line offset goes into the lane offset, so the resource's range check covers
-            // the whole address (a touch past the end of C reads nothing)
-            if (cl >= 0 && cl <= C_LINES)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rc, (DG_LDS void *)(ldsp + TOUCH_BASE + wave * 256), 4,
-                    c_row + (uint32_t)(cl * 128), 0, 0, 0);
-        }
+    static_assert(SM % 2 == 0, "C is streamed in halves of the row sub-tiles");
+    constexpr int HM = SM / 2;
+    v4f cb[HM];
+    auto load_c_half = [&](int jj, int h) {
+#pragma unroll
+        for (int i = 0; i < HM; ++i)
+            cb[i] = __builtin_bit_cast(
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                         rc, c_lane + (uint32_t)((16 * (h * HM + i) * N + 16 * jj) * 4), 0, 0));
     };
+    // both halves of column jj were streamed (the second half's block is the later one)
+    auto c_streamed = [&](int jj) { return stream_c && c_j0 + 2 * jj + 1 < nkb; };
     auto read_sfb = [&](int aslot) {
         vsb_lo = lds_read4(sb_lo_addr + (uint32_t)(aslot * 256));
         vsb_hi = lds_read4(sb_hi_addr + (uint32_t)(aslot * 256));
@@ -347,7 +346,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         });
     };
 
+    // C of column JJ's half added when block j is that half's block, then the next half loaded
+    auto c_step = [&](int j, auto JJ) {
+        constexpr int jj = decltype(JJ)::value;
+        if constexpr (MODE == MODE_DENSE) {
+            // only columns whose two halves both fall inside the K loop; the others take all
+            // of their C in the epilogue
+            if (c_streamed(jj) && j == c_j0 + 2 * jj) {
+#pragma unroll
+                for (int i = 0; i < HM; ++i)
+                    acc[i][jj] += cb[i];
+                load_c_half(jj, 1);
+            }
+            if (c_streamed(jj) && j == c_j0 + 2 * jj + 1) {
+#pragma unroll
+                for (int i = 0; i < HM; ++i)
+                    acc[HM + i][jj] += cb[i];
+                if constexpr (jj + 1 < SN) {
+                    if (c_streamed(jj + 1))
+                        load_c_half(jj + 1, 0);
+                }
+            }
+        }
+    };
+
     // ---- prologue: blocks 0 and 1 in flight, block 0's fragments read
+    if constexpr (MODE == MODE_DENSE) {
+        if (c_streamed(0))
+            load_c_half(0, 0);  // older than every copy: landed once the first copies have
+    }
     {
         const bool two = nkb > 1;
         issue_scales(kb0, 0, rs, rsb);
@@ -400,7 +427,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         // every wave holds this block's A: its A slot may take block j+2; the B slot of block
         // j-1 was released at the previous block's second barrier
         bare_barrier();
-        touch_c(j);
         issue_scales(kb_fill, aslot, fs, refill ? rsb : rz);
         if constexpr (SN == 1)
 #pragma unroll
@@ -432,6 +458,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
                 tie(Bf[bbuf(jj, SN)][0]);
                 tie(Bf[bbuf(jj, SN)][1]);
             }
+            c_step(j, JJ);
             if constexpr (jj == 0)
                 mfma_step(JJ, Bf[0], [&](int i) { return psc[i]; }, extra);
             else
@@ -452,6 +479,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         const uint32_t sa_n = sa_lane + (uint32_t)(an * 1024);
         const uint32_t blo_n = b_lo + (uint32_t)(bslot_next * B_SLOT);
         const uint32_t bhi_n = b_hi + (uint32_t)(bslot_next * B_SLOT);
+        c_step(j, std::integral_constant<int, SN - 1>{});
         constexpr auto C0 = std::integral_constant<int, 0>{};
         constexpr auto C1 = std::integral_constant<int, 1>{};
         if constexpr (SN == 1) {
@@ -520,15 +548,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         if (p.c) {
             const __amdgpu_buffer_rsrc_t rcc =
                 make_rsrc(p.c + (int64_t)m0 * N, (int64_t)(row_limit - m0) * N * 4);
-            const uint32_t c_lane = (uint32_t)(((wm + fr) * N + n0 + wn + 4 * fg) * 4);
             v4f cv[SM][SN];
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
                 for (int j = 0; j < SN; ++j)
-                    cv[i][j] = __builtin_bit_cast(
-                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                 rcc, c_lane + (uint32_t)((16 * i * N + 16 * j) * 4), 0, 0));
+                    cv[i][j] = c_streamed(j)
+                                   ? v4f{0.f, 0.f, 0.f, 0.f}
+                                   : __builtin_bit_cast(
+                                         v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rcc, c_lane + (uint32_t)((16 * i * N + 16 * j) * 4),
+                                                  0, 0));
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll

@@ -45,6 +45,15 @@ def test_dense_ragged_every_tile_config(cfg, monkeypatch):
     assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), cfg)
 
 
+@pytest.mark.parametrize("k", [128, 384, 1664, 1792, 1920, 2048])
+def test_dense_c_stream_boundaries(k, monkeypatch):
+    # C is added during the K loop for the columns whose blocks fit inside it and in the
+    # epilogue for the rest: K from 1 to 16 blocks crosses every such split for 256x224 tiles
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x224w8")
+    p = W.make_dense(256, 448, k, seed=26, with_c=True, c_std=2.0)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"k={k}")
+
+
 def test_dense_stress_scales():
     p = W.make_dense(130, 272, 512, seed=22, stress=True)
     assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "stress")
