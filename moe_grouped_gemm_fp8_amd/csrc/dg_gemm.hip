@@ -11,11 +11,16 @@
 //    of the 16x16 result then holds four consecutive columns of ONE output row, so the A
 //    row-segment scale is a single per-lane float and promoting a partial into the FP32
 //    accumulators costs one multiply (sa * sb) plus four FMAs per MFMA.
-//  * Every global read of the main loop (A, B and the A scales) is a gfx950 direct-to-LDS
-//    copy (global_load_lds_dwordx4): nothing in flight targets registers, so the only waits
-//    are explicit ones.  Copies run through a ring of RING half-block slots (64 K-bytes of
-//    the A and B tiles each), giving (RING - 2) halves of look-ahead with one barrier per
-//    K block.  Barriers are bare s_barrier (no release fence, which would drain the ring).
+//  * Every global read of the main loop (A, B, the A scales and the tile's B scales) is a
+//    gfx950 direct-to-LDS copy through a buffer resource: nothing in flight targets
+//    registers, so the only waits are explicit ones.  A has two LDS slots and B three, each
+//    a whole 128-deep K block, so block j+1's copies are in flight while block j is
+//    multiplied, with one barrier per K block.  A wave holds its A fragments for the whole
+//    block and reads B fragments two sub-tile steps ahead of the MFMAs that use them.
+//    Barriers are bare s_barrier (a release fence would wait for every copy in flight).
+//  * Dense with C: during the last K blocks each wave loads C for one half of an accumulator
+//    column at a time (16-byte buffer loads into registers, hidden behind the MFMAs) and adds
+//    it in, so that most of C's HBM read overlaps the main loop; the epilogue adds the rest.
 //  * LDS rows are 128 bytes (one K block of one row); the 16-byte chunk c of row r sits at
 //    chunk c ^ h(r), h(r) = r3 | r1 << 1 | r2 << 2 (bits of r).  gfx950 serves a ds_read_b128
 //    16 lanes at a time and its bank selection hashes higher address bits, so the plain
