@@ -20,20 +20,25 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int KBLK = 128;   // K block = scale granularity = MFMA depth
 constexpr int GROUP_M = 4;  // tile raster: M-tiles per group
 
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// Two FP32 values rounded to nearest-even bf16 and packed (low half = a): gfx950's
+// v_cvt_pk_bf16_f32, which keeps a NaN a quiet NaN and infinities infinite.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)  // NaN: keep it a (quiet) NaN
-        return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// 8-byte LDS write (two dwords) at a byte address; completion is counted by lgkmcnt
+__device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t hi)
+{
+    asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(make_uint2(lo, hi)) : "memory");
 }
 
 __device__ __forceinline__ void store_bf16x4(uint16_t *dst, v4f v)
 {
-    uint32_t lo = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
-    uint32_t hi = f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16);
+    uint32_t lo = pack_bf16x2(v.x, v.y);
+    uint32_t hi = pack_bf16x2(v.z, v.w);
     *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
 }
 

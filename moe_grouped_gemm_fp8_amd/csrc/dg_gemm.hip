@@ -54,9 +54,25 @@ const TileInfo kTiles[CFG_COUNT] = {
     {64, 32, 256, "64x32w4"},
     {256, 128, 512, "256x128w8"},
     {64, 64, 256, "stream64"},
+    {128, 128, 256, "128x128w4d4"},
+    {128, 128, 512, "128x128w8d4"},
 };
 
-template <int BM, int BN, int WM, int WN, int MODE>
+// True when 8 consecutive rows `stride` bytes apart start in 8 distinct 32-byte bank groups
+// of a 256-byte bank period (the 32 lanes of a half fragment write then hit distinct banks).
+constexpr bool rows_on_distinct_banks(int stride)
+{
+    int seen = 0;
+    for (int r = 0; r < 8; ++r) {
+        const int off = (r * stride) % 256;
+        if (off % 32 != 0 || (seen >> (off / 32)) & 1)
+            return false;
+        seen |= 1 << (off / 32);
+    }
+    return true;
+}
+
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int tiles_n)
 {
     constexpr int NW = WM * WN;
@@ -66,16 +82,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     constexpr int NBUF = bbuf_count(SN);
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
     static_assert(BM % 8 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
-    // LDS: two A slots (BM rows of one K block), three B slots (BN rows of one K block), and
-    // per A slot a 1 KB area for its A scales and a 256-byte area for the B scales of the
-    // 128-column blocks the tile touches.  Rows are 128 bytes; 16-byte chunk c of row r sits
-    // at chunk c ^ h(r) (header comment).
+    // LDS: DEPTH A slots (BM rows of one K block), DEPTH + 1 B slots (BN rows of one K
+    // block), and per A slot a 1 KB area for its A scales and a 256-byte area for the B scales
+    // of the 128-column blocks the tile touches.  Block j + DEPTH is copied while block j is
+    // multiplied.  Rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ h(r)
+    // (header comment).
+    static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
-    constexpr int B_BASE = 2 * A_SLOT;
-    constexpr int SA_BASE = B_BASE + 3 * B_SLOT;
-    constexpr int SB_BASE = SA_BASE + 2 * 1024;
-    constexpr int LDS_BYTES = SB_BASE + 2 * 256;
+    constexpr int B_BASE = DEPTH * A_SLOT;
+    constexpr int SA_BASE = B_BASE + (DEPTH + 1) * B_SLOT;
+    constexpr int SB_BASE = SA_BASE + DEPTH * 1024;
+    constexpr int LDS_BYTES = SB_BASE + DEPTH * 256;
     static_assert(A_SLOT % 4096 == 0 && B_SLOT % 4096 == 0, "slots start on 4 KB boundaries");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
@@ -83,10 +101,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     constexpr int CA = IA / NW;                   // A copies per wave per block
     constexpr int CB = (IB + NW - 1) / NW;        // B copies per wave per block (padded)
     constexpr int MAXI = CA + CB;                 // + wave 0 copies the block's scales (2)
-    static_assert(2 * MAXI < 64, "outstanding copies must fit vmcnt");
+    static_assert(DEPTH * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     __shared__ int s_flag;
+    __shared__ int s_grp[MODE == MODE_CONTIG ? BM : 1];  // contiguous: the tile's row groups
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,6 +146,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         __syncthreads();
         for (int i = tid; i < BM; i += NT) {
             int v = p.grp[tm * BM + i];
+            s_grp[i] = v;
             if (v >= 0 && v < p.num_groups)
                 atomicMax(&s_flag, v);
         }
@@ -140,6 +160,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         row_limit = p.m;
     }
     const int m0 = tm * BM, n0 = tn * BN;
+    // masked form: the wave's row sub-tiles that hold a valid row (the others are never
+    // stored, so their MFMAs and promotions are skipped; copies and barriers are not)
+    int sm_act = SM;
+    if constexpr (MODE == MODE_MASKED) {
+        const int v = (row_limit - m0 - wm + 15) >> 4;
+        sm_act = __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > SM ? SM : v));
+    }
     const uint8_t *B = p.b + (int64_t)g * N * K;
     const float *SFB = p.sfb + (int64_t)g * NB * KB;
     const int nkb = kb1 - kb0;
@@ -208,12 +235,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
                 0);
         }
     };
-    // wait until the copies issued before the most recent block's have landed
+    // wait until the next block's copies have landed (those of the DEPTH - 1 blocks after it
+    // may still be in flight)
     auto wait_older_copies = [&]() {
         if (wave == 0)
-            wait_vm<MAXI + 2>();
+            wait_vm<(DEPTH - 1) * (MAXI + 2)>();
         else
-            wait_vm<MAXI>();
+            wait_vm<(DEPTH - 1) * MAXI>();
     };
 
     // per-lane fragment offsets inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32) of
@@ -335,17 +363,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         const v8i bv = v8i{bf[0].x, bf[0].y, bf[0].z, bf[0].w, bf[1].x, bf[1].y, bf[1].z, bf[1].w};
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            {
-                v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
-                a += pend[i] * scale(i);
-                // keep the promotion here: left free, the compiler hoists every MFMA of the
-                // block above all promotions and holds SM*SN partials live at once
-                asm volatile("" : "+v"(a));
+            if (MODE != MODE_MASKED || i < sm_act) {
+                {
+                    v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
+                    a += pend[i] * scale(i);
+                    // keep the promotion here: left free, the compiler hoists every MFMA of
+                    // the block above all promotions and holds SM*SN partials live at once
+                    asm volatile("" : "+v"(a));
+                }
+                const v8i av = v8i{Af[i][0].x, Af[i][0].y, Af[i][0].z, Af[i][0].w,
+                                   Af[i][1].x, Af[i][1].y, Af[i][1].z, Af[i][1].w};
+                pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
             }
-            const v8i av = v8i{Af[i][0].x, Af[i][0].y, Af[i][0].z, Af[i][0].w,
-                               Af[i][1].x, Af[i][1].y, Af[i][1].z, Af[i][1].w};
-            pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
             extra(I);
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -375,21 +405,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         }
     };
 
-    // ---- prologue: blocks 0 and 1 in flight, block 0's fragments read
+    // ---- prologue: blocks 0 .. DEPTH-1 in flight, block 0's fragments read
     if constexpr (MODE == MODE_DENSE) {
         if (c_streamed(0))
             load_c_half(0, 0);  // older than every copy: landed once the first copies have
     }
-    {
-        const bool two = nkb > 1;
-        issue_scales(kb0, 0, rs, rsb);
+    // (blocks past the last are copied from empty resources, which keeps the per-wave copy
+    // count constant)
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        const bool in = d < nkb;
+        issue_scales(in ? kb0 + d : kb0, d, in ? rs : rz, in ? rsb : rz);
 #pragma unroll
         for (int c = 0; c < MAXI; ++c)
-            issue_copy(c, kb0, 0, 0, ra, rb);
-        issue_scales(two ? kb0 + 1 : kb0, 1, two ? rs : rz, two ? rsb : rz);
-#pragma unroll
-        for (int c = 0; c < MAXI; ++c)
-            issue_copy(c, two ? kb0 + 1 : kb0, 1, 1, two ? ra : rz, two ? rb : rz);
+            issue_copy(c, in ? kb0 + d : kb0, d, d, in ? ra : rz, in ? rb : rz);
     }
     wait_older_copies();
     bare_barrier();
@@ -399,17 +428,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     if constexpr (SN > 1)
         read_b(b_lo, b_hi, std::integral_constant<int, 1>{}, Bf[1]);
 
-    int bslot = 0;  // B slot of the current block; its A slot is the block's parity
+    int aslot = 0;  // A slot of the current block: j % DEPTH
+    int bslot = 0;  // B slot of the current block: j % (DEPTH + 1)
     for (int j = 0; j < nkb; ++j) {
-        const int aslot = j & 1;
-        const bool refill = j + 2 < nkb;
-        const int kb_fill = refill ? kb0 + j + 2 : kb0;
+        const bool refill = j + DEPTH < nkb;
+        const int kb_fill = refill ? kb0 + j + DEPTH : kb0;
         const __amdgpu_buffer_rsrc_t fa = refill ? ra : rz;
         const __amdgpu_buffer_rsrc_t fb = refill ? rb : rz;
         const __amdgpu_buffer_rsrc_t fs = refill ? rs : rz;
-        const int bslot_next = bslot == 2 ? 0 : bslot + 1;
-        const int bslot_fill = bslot == 0 ? 2 : bslot - 1;  // (j + 2) % 3
-        const int an = aslot ^ 1;
+        const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
+        const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
+        const int an = aslot == DEPTH - 1 ? 0 : aslot + 1;
         // slot bases of this block's B reads and of the next block's A and B reads
         const uint32_t blo_c = b_lo + (uint32_t)(bslot * B_SLOT);
         const uint32_t bhi_c = b_hi + (uint32_t)(bslot * B_SLOT);
@@ -429,8 +458,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
             tie(Bf[1][1]);
         }
         take_sfb();
-        // every wave holds this block's A: its A slot may take block j+2; the B slot of block
-        // j-1 was released at the previous block's second barrier
+        // every wave holds this block's A: its A slot may take block j+DEPTH, whose B slot
+        // (block j-1's) was released at the previous block's second barrier
         bare_barrier();
         issue_scales(kb_fill, aslot, fs, refill ? rsb : rz);
         if constexpr (SN == 1)
@@ -521,6 +550,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
                           read_a(alo_n, ahi_n, sa_n, I);
                       });
         }
+        aslot = an;
         bslot = bslot_next;
     }
     // the last block also read (unused) fragments: they must land before their registers
@@ -571,31 +601,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
                     acc[i][j] += cv[i][j];
         }
     }
-    bool row_ok[SM];
+    // The tile goes out through LDS: each wave writes its sub-tiles there as bf16 (8 bytes per
+    // lane), then every thread stores whole 16-byte pieces of rows, so a wave's store covers
+    // contiguous row segments instead of sixteen 32-byte pieces.  Output rows are OS bytes
+    // apart in LDS; OS = 32 (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct
+    // banks (two 256-byte halves).
+    constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
+    static_assert(rows_on_distinct_banks(OS), "output row stride");
+    static_assert(BM * OS <= LDS_BYTES, "output tile fits the operand slots");
+    constexpr int CPR = BN / 8;  // 16-byte pieces per output row
+    static_assert((BM * CPR) % NT == 0, "output pieces split evenly over the threads");
+    constexpr int PPT = BM * CPR / NT;  // pieces per thread
+    bare_barrier();  // every wave is past its last fragment read and copy: LDS is free
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        const int row = m0 + wm + 16 * i + fr;
-        row_ok[i] = row < row_limit;
-        if constexpr (MODE == MODE_CONTIG)
-            row_ok[i] = row < row_limit && p.grp[row] == g;
-    }
-#pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        const int row = m0 + wm + 16 * i + fr;
+    for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
-            const int col = n0 + wn + 16 * j + 4 * fg;
-            if (row_ok[i] && col < N)
-                store_bf16x4(D + (int64_t)row * N + col, acc[i][j]);
+            const uint32_t lo = pack_bf16x2(acc[i][j].x, acc[i][j].y);
+            const uint32_t hi = pack_bf16x2(acc[i][j].z, acc[i][j].w);
+            lds_write8(lds_base + (uint32_t)((wm + 16 * i + fr) * OS + (wn + 16 * j + 4 * fg) * 2),
+                       lo, hi);
         }
+    lds_wait();
+    bare_barrier();
+    v4i piece[PPT];
+#pragma unroll
+    for (int t = 0; t < PPT; ++t) {
+        const int q = tid + t * NT;
+        piece[t] = lds_read16(lds_base + (uint32_t)((q / CPR) * OS + (q % CPR) * 16));
+    }
+    int rowg[PPT];
+    if constexpr (MODE == MODE_CONTIG) {
+#pragma unroll
+        for (int t = 0; t < PPT; ++t)
+            rowg[t] = s_grp[(tid + t * NT) / CPR];
+    }
+    lds_wait();
+#pragma unroll
+    for (int t = 0; t < PPT; ++t) {
+        const int q = tid + t * NT;
+        const int row = m0 + q / CPR;
+        const int col = n0 + (q % CPR) * 8;
+        bool ok = row < row_limit && col < N;
+        if constexpr (MODE == MODE_CONTIG)
+            ok = ok && rowg[t] == g;
+        if (ok)
+            *reinterpret_cast<v4i *>(D + (int64_t)row * N + col) = piece[t];
     }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
-    gemm_tile<BM, BN, WM, WN, MODE>(p, tiles_m, tiles_n);
+    gemm_tile<BM, BN, WM, WN, DEPTH, MODE>(p, tiles_m, tiles_n);
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -622,7 +681,7 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     return g;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int DEPTH = 2>
 static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
 {
     int tiles_m, tiles_n;
@@ -637,15 +696,15 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     dim3 g((unsigned)grid), b(cfg_threads);
     switch (mode) {
     case MODE_DENSE:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_DENSE>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_CONTIG>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, MODE_MASKED>), g, b, 0, stream, a,
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED>), g, b, 0, stream, a,
                            tiles_m, tiles_n);
         break;
     }
@@ -665,6 +724,10 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
         return launch_cfg<64, 32, 2, 2>(mode, a, stream);
     case CFG_256x128:
         return launch_cfg<256, 128, 4, 2>(mode, a, stream);
+    case CFG_128x128d4:
+        return launch_cfg<128, 128, 2, 2, 4>(mode, a, stream);
+    case CFG_128x128w8d4:
+        return launch_cfg<128, 128, 2, 4, 4>(mode, a, stream);
     case CFG_STREAM64:
         return mode == MODE_DENSE ? launch_stream(a, stream) : hipErrorInvalidValue;
     default:

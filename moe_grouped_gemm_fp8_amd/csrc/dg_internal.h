@@ -10,7 +10,8 @@ enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 
 // Tile configurations compiled ahead of time.  Each is (BM x BN) output rows x columns per
 // workgroup, split over WM x WN waves of 64 lanes; every wave owns a (BM/WM) x (BN/WN) block
-// built from 16x16 MFMA sub-tiles.
+// built from 16x16 MFMA sub-tiles.  Copies run two K blocks ahead of the MFMAs unless the
+// name says otherwise (d4: four, for shapes bound by HBM latency).
 enum TileCfg : int {
     CFG_256x224 = 0,  // 8 waves (4x2), wave tile 64x112: large dense GEMMs, N % 224 friendly
     CFG_128x256 = 1,  // 4 waves (2x2), wave tile 64x128: contiguous MoE (128-row segments)
@@ -18,6 +19,8 @@ enum TileCfg : int {
     CFG_64x32 = 3,    // 4 waves (2x2), wave tile 32x16: skinny M with split-K
     CFG_256x128 = 4,  // 8 waves (4x2), wave tile 64x64: masked decode, one tile spans m_max
     CFG_STREAM64 = 5, // split-K streaming kernel, 64x64 tiles, <= 8 K blocks per split: skinny M
+    CFG_128x128d4 = 6,   // 4 waves (2x2), wave tile 64x64, copies four K blocks ahead
+    CFG_128x128w8d4 = 7, // 8 waves (2x4), wave tile 64x32, copies four K blocks ahead
     CFG_COUNT
 };
 

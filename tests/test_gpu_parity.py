@@ -14,10 +14,13 @@ import oracle
 import workloads as W
 from gpu_util import (DEV, assert_parity, bits, dense_rows_ref, dev, run_contiguous, run_dense,
                       run_masked, sentinel_like)
+from tolerance import bf16_bits_to_f64
 
 pytestmark = pytest.mark.gpu
 
-TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "stream64"]
+TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "stream64",
+                "128x128w4d4", "128x128w8d4"]
+DEEP_CONFIGS = ["128x128w4d4", "128x128w8d4"]
 
 
 def _say(msg):
@@ -52,6 +55,60 @@ def test_dense_c_stream_boundaries(k, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x224w8")
     p = W.make_dense(256, 448, k, seed=26, with_c=True, c_std=2.0)
     assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"k={k}")
+
+
+@pytest.mark.parametrize("cfg", DEEP_CONFIGS)
+@pytest.mark.parametrize("k", [128, 512, 640, 1152, 2048])
+def test_deep_pipeline_k_blocks(cfg, k, monkeypatch):
+    # copies four K blocks ahead: fewer blocks than the depth, the depth itself, and counts
+    # that wrap the four A slots and five B slots unevenly
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_dense(192, 272, k, seed=27, with_c=True)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"{cfg} k={k}")
+    q = W.make_masked(3, 256, 256, k, seed=44, masked_m=[256, 129, 17])
+    ref = oracle.m_grouped_masked(q.a, q.sfa, q.b, q.sfb, q.masked_m)
+    assert_parity(run_masked(q), ref, f"masked {cfg} k={k}")
+
+
+# f32 bit patterns of C whose bf16 rounding is decided by nearest-even: exact ties both ways,
+# one ulp either side of a tie, the overflow boundary, infinities, quiet and signalling NaN,
+# and subnormals (ties at the smallest bf16 subnormal included)
+_ROUNDING_SPECIALS = np.array([
+    0x3F808000, 0x3F818000, 0xBF808000, 0x3F808001, 0x3F807FFF, 0x3F800000,
+    0x7F7F0000, 0x7F7F7FFF, 0x7F7F8000, 0xFF7F8000, 0x7F800000, 0xFF800000,
+    0x7FC00000, 0x7F800001, 0xFFC12345,
+    0x00000001, 0x00008000, 0x00018000, 0x00008001, 0x807FFFFF, 0x00800000,
+], dtype=np.uint32)
+
+
+@pytest.mark.parametrize("cfg,k,splits", [("256x224w8", 2048, None), ("256x224w8", 128, None),
+                                          ("128x128w4", 256, None), ("stream64", 512, "1"),
+                                          ("stream64", 512, "4")])
+def test_dense_bf16_rounding_of_special_values(cfg, k, splits, monkeypatch):
+    # A = 0 makes D = round_bf16(C) exactly (the oracle's value is C itself); the rounding is
+    # nearest-even with NaN kept NaN, compared bit for bit with torch's CPU conversion
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if splits:
+        monkeypatch.setenv("DG_FORCE_SPLITS", splits)
+    p = W.make_dense(256, 448, k, seed=28, with_c=True)
+    p.a[:] = 0
+    rng = np.random.default_rng(29)
+    cbits = rng.standard_normal(p.c.shape).astype(np.float32).view(np.uint32)
+    sel = rng.random(p.c.shape) < 0.5
+    cbits[sel] = rng.choice(_ROUNDING_SPECIALS, int(sel.sum()))
+    p.c = cbits.view(np.float32)
+    ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    fin = np.isfinite(p.c)
+    assert np.array_equal(ref[fin], p.c[fin].astype(np.float64))
+    got = run_dense(p)
+    want = torch.from_numpy(p.c).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(p.c)
+    assert np.all(np.isnan(bf16_bits_to_f64(got[nan]))), "a NaN of C did not stay NaN"
+    bad = got[~nan] != want[~nan]
+    assert not bad.any(), (f"{int(bad.sum())} roundings differ; first C bits "
+                           f"{[hex(x) for x in cbits[~nan][bad][:4]]}: got "
+                           f"{[hex(x) for x in got[~nan][bad][:4]]} want "
+                           f"{[hex(x) for x in want[~nan][bad][:4]]}")
 
 
 def test_dense_stress_scales():
@@ -110,7 +167,7 @@ def test_dense_prefill_workload_sampled_rows():
 
 # ------------------------------------------------------------------------------ contiguous
 
-@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4"])
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4"])
 def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -153,7 +210,8 @@ def test_contiguous_workload_sampled_rows():
 
 # ------------------------------------------------------------------------------ masked
 
-@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4"])
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
+                                 "256x128w8"])
 def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
