@@ -278,7 +278,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
         return rc;
     int cfg = forced_config();
     if (cfg < 0 || cfg == dg::CFG_STREAM64 || 128 % dg::kTiles[cfg].bm != 0)
-        cfg = (n % 256 == 0) ? dg::CFG_128x256 : dg::CFG_128x128;
+        cfg = (n % 256 == 0) ? dg::CFG_128x256w8 : dg::CFG_128x128;
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;
     args.sfa = sfa;

@@ -56,6 +56,7 @@ const TileInfo kTiles[CFG_COUNT] = {
     {64, 64, 256, "stream64"},
     {128, 128, 256, "128x128w4d4"},
     {128, 128, 512, "128x128w8d4"},
+    {128, 256, 512, "128x256w8"},
 };
 
 // True when 8 consecutive rows `stride` bytes apart start in 8 distinct 32-byte bank groups
@@ -331,6 +332,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         psc[i] = 0.f;
     }
     float sb_cur[SN];
+    // When every wave's columns lie in one 128-column scale block (BN a multiple of 128 and
+    // TN dividing 128), a row's promotion scale is the same for all of its sub-tiles in a
+    // block: scb[i] = sa[i] * sb, formed once per block instead of once per MFMA.
+    constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0);
+    float scb[SM];
     auto take_sfb = [&]() {
         tie(vsb_lo);
         tie(vsb_hi);
@@ -458,6 +464,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
             tie(Bf[1][1]);
         }
         take_sfb();
+        if constexpr (ONE_NB) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                scb[i] = Sf[i] * sb_cur[0];
+        }
         // every wave holds this block's A: its A slot may take block j+DEPTH, whose B slot
         // (block j-1's) was released at the previous block's second barrier
         bare_barrier();
@@ -496,7 +507,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
             if constexpr (jj == 0)
                 mfma_step(JJ, Bf[0], [&](int i) { return psc[i]; }, extra);
             else
-                mfma_step(JJ, Bf[bbuf(jj, SN)], [&](int i) { return Sf[i] * sb_cur[jj - 1]; },
+                mfma_step(JJ, Bf[bbuf(jj, SN)],
+                          [&](int i) { return ONE_NB ? scb[i] : Sf[i] * sb_cur[jj - 1]; },
                           extra);
         });
         // last step: the next block's copies have landed everywhere (past the last block the
@@ -534,8 +546,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         } else {
             mfma_step(std::integral_constant<int, SN - 1>{}, Bf[bbuf(SN - 1, SN)],
                       [&](int i) {
-                          psc[i] = Sf[i] * sb_cur[SN - 1];
-                          return Sf[i] * sb_cur[SN - 2];
+                          psc[i] = ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 1];
+                          return ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 2];
                       },
                       [&](auto I) {
                           constexpr int i = decltype(I)::value;
@@ -728,6 +740,8 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
         return launch_cfg<128, 128, 2, 2, 4>(mode, a, stream);
     case CFG_128x128w8d4:
         return launch_cfg<128, 128, 2, 4, 4>(mode, a, stream);
+    case CFG_128x256w8:
+        return launch_cfg<128, 256, 2, 4>(mode, a, stream);
     case CFG_STREAM64:
         return mode == MODE_DENSE ? launch_stream(a, stream) : hipErrorInvalidValue;
     default:

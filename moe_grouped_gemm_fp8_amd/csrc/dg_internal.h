@@ -21,6 +21,7 @@ enum TileCfg : int {
     CFG_STREAM64 = 5, // split-K streaming kernel, 64x64 tiles, <= 8 K blocks per split: skinny M
     CFG_128x128d4 = 6,   // 4 waves (2x2), wave tile 64x64, copies four K blocks ahead
     CFG_128x128w8d4 = 7, // 8 waves (2x4), wave tile 64x32, copies four K blocks ahead
+    CFG_128x256w8 = 8,   // 8 waves (2x4), wave tile 64x64: contiguous MoE, two waves per SIMD
     CFG_COUNT
 };
 

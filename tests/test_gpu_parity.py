@@ -19,7 +19,7 @@ from tolerance import bf16_bits_to_f64
 pytestmark = pytest.mark.gpu
 
 TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "stream64",
-                "128x128w4d4", "128x128w8d4"]
+                "128x128w4d4", "128x128w8d4", "128x256w8"]
 DEEP_CONFIGS = ["128x128w4d4", "128x128w8d4"]
 
 
@@ -167,7 +167,8 @@ def test_dense_prefill_workload_sampled_rows():
 
 # ------------------------------------------------------------------------------ contiguous
 
-@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4"])
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
+                                 "128x256w8", "128x256w4"])
 def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
