@@ -128,6 +128,20 @@ int forced_config()
     return -1;
 }
 
+// Workgroups a persistent tile configuration may launch: one per CU.  DG_NO_PERSIST=1
+// launches one per tile (for comparisons); DG_PERSIST_WGS=n caps them at n (tests: many
+// tiles per workgroup on small problems).
+int persistent_wgs(int cus)
+{
+    const char *s = getenv("DG_NO_PERSIST");
+    if (s && *s && *s != '0')
+        return 0;
+    const char *w = getenv("DG_PERSIST_WGS");
+    if (w && *w && atoi(w) > 0)
+        return atoi(w);
+    return cus;
+}
+
 int forced_splits()
 {
     const char *s = getenv("DG_FORCE_SPLITS");
@@ -203,6 +217,7 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     args.k = k;
     args.num_groups = 1;
     args.splits = 1;
+    args.max_wgs = persistent_wgs(cus);
 
     // Pipelined tiles for shapes that fill the CUs; the split-K streaming kernel for skinny M
     // and for shapes whose big tiles would leave most CUs idle.
@@ -292,6 +307,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
     args.k = k;
     args.num_groups = num_groups;
     args.splits = 1;
+    args.max_wgs = persistent_wgs(cus);
     print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
 }
@@ -332,6 +348,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
     args.k = k;
     args.num_groups = num_groups;
     args.splits = 1;
+    args.max_wgs = persistent_wgs(cus);
     print_config("m_grouped_masked", m_max, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_MASKED, cfg, args, (hipStream_t)stream);
 }

@@ -179,7 +179,10 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm,
 // whose offset falls outside the range reads zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
-    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    // clamp to [0, 2^31 - 1] with 32-bit compares on the two halves (the scalar unit has no
+    // 64-bit signed compare, so an int64 compare would move to the vector unit)
+    const uint32_t hi = (uint32_t)((uint64_t)bytes >> 32), lo = (uint32_t)bytes;
+    const int n = (int)hi < 0 ? 0 : ((hi != 0 || lo > 0x7fffffffu) ? 0x7fffffff : (int)lo);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 

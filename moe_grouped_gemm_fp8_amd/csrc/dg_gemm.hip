@@ -48,15 +48,18 @@
 namespace dg {
 
 const TileInfo kTiles[CFG_COUNT] = {
-    {256, 224, 512, "256x224w8"},
-    {128, 256, 256, "128x256w4"},
-    {128, 128, 256, "128x128w4"},
-    {64, 32, 256, "64x32w4"},
-    {256, 128, 512, "256x128w8"},
-    {64, 64, 256, "stream64"},
-    {128, 128, 256, "128x128w4d4"},
-    {128, 128, 512, "128x128w8d4"},
-    {128, 256, 512, "128x256w8"},
+    // the 256x224 tile runs one workgroup per tile: with the loop over tiles its registers
+    // spill (it needs nearly all 256 VGPRs for one tile)
+    {256, 224, 512, "256x224w8", false},
+    {128, 256, 256, "128x256w4", true},
+    {128, 128, 256, "128x128w4", true},
+    {64, 32, 256, "64x32w4", true},
+    {256, 128, 512, "256x128w8", false},
+    {64, 64, 256, "stream64", false},
+    {128, 128, 256, "128x128w4d4", true},
+    {128, 128, 512, "128x128w8d4", true},
+    {128, 256, 512, "128x256w8", true},
+    {256, 128, 512, "256x128w8p", true},
 };
 
 // True when 8 consecutive rows `stride` bytes apart start in 8 distinct 32-byte bank groups
@@ -73,16 +76,34 @@ constexpr bool rows_on_distinct_banks(int stride)
     return true;
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH, int MODE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int tiles_n)
+// Largest value over the wave's 64 lanes (a few lane permutes; used once per tile)
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = max(v, __shfl_xor(v, off));
+    return v;
+}
+
+// 8-byte global store issued as inline asm: the compiler then does not count it among the
+// wave's outstanding vector-memory operations, so its own waits for later register loads (the
+// streamed C) stay exact counts instead of draining everything in flight; every explicit wait
+// of the kernel counts it (it is older than the copies issued after it).
+__device__ __forceinline__ void store8_async(uint16_t *dst, uint32_t lo, uint32_t hi)
+{
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(dst), "v"(make_uint2(lo, hi))
+                 : "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST>
+__device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int tiles_n)
 {
     constexpr int NW = WM * WN;
-    constexpr int NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
     constexpr int NBUF = bbuf_count(SN);
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be 16-aligned");
-    static_assert(BM % 8 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
+    static_assert(BM % 64 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
     // LDS: DEPTH A slots (BM rows of one K block), DEPTH + 1 B slots (BN rows of one K
     // block), and per A slot a 1 KB area for its A scales and a 256-byte area for the B scales
     // of the 128-column blocks the tile touches.  Block j + DEPTH is copied while block j is
@@ -105,8 +126,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     static_assert(DEPTH * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-    __shared__ int s_flag;
-    __shared__ int s_grp[MODE == MODE_CONTIG ? BM : 1];  // contiguous: the tile's row groups
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -114,125 +133,186 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     const int wm = (wave / WN) * TM;  // wave's row offset inside the tile
     const int wn = (wave % WN) * TN;  // wave's column offset inside the tile
 
-    const int K = p.k, N = p.n;
-    const int KB = K / KBLK;
-    const int NB = (N + KBLK - 1) / KBLK;
-    const int64_t ld = p.ld_sfa;
+    // problem sizes; set again (through an opaque copy) at every tile, so that what the
+    // compiler derives from them is recomputed per tile instead of being held in scalar
+    // registers for the whole kernel
+    int M, K, N, KB, NB, nkb;
+    int64_t ld;
+    auto set_dims = [&]() {
+        M = p.m;
+        K = p.k;
+        N = p.n;
+        asm volatile("" : "+s"(M), "+s"(K), "+s"(N));
+        KB = K / KBLK;
+        NB = (N + KBLK - 1) / KBLK;
+        nkb = KB;
+        ld = p.ld_sfa;
+    };
+    set_dims();
 
-    // ---- which tile, which group, which rows are valid
-    int t = xcd_remap(blockIdx.x, gridDim.x);
-    int tm, tn, g = 0, row_limit;
-    const int kb0 = 0, kb1 = KB;
-    const uint8_t *A = p.a;
-    const float *SFA = p.sfa;
-    uint16_t *D = p.d;
-    if constexpr (MODE == MODE_MASKED) {
-        int per_g = tiles_m * tiles_n;
-        g = t / per_g;
-        int rem = t - g * per_g;
-        tn = rem / tiles_m;
-        tm = rem - tn * tiles_m;
-        int valid = p.grp[g];
-        valid = valid < 0 ? 0 : (valid > p.m ? p.m : valid);
-        if (tm * BM >= valid)
-            return;
-        row_limit = valid;
-        A += (int64_t)g * p.m * K;
-        SFA += (int64_t)g * KB * ld;
-        D += (int64_t)g * p.m * N;
-    } else if constexpr (MODE == MODE_CONTIG) {
-        raster(t, tiles_m, tiles_n, tm, tn);
-        if (tid == 0)
-            s_flag = -1;
-        __syncthreads();
-        for (int i = tid; i < BM; i += NT) {
-            int v = p.grp[tm * BM + i];
-            s_grp[i] = v;
-            if (v >= 0 && v < p.num_groups)
-                atomicMax(&s_flag, v);
+    // ---- this workgroup's tiles.  Workgroup ids are dealt round-robin over the 8 XCDs; XCD x
+    // owns a contiguous range [s0, s1) of tile ids (in proportion to its workgroups) and its
+    // workgroups stride through it together, so the tiles in flight on one XCD are neighbours
+    // in the raster and share A rows and B columns in that XCD's L2.  With one workgroup per
+    // tile this is the plain XCD-contiguous remap.
+    const int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
+    int tile_id, tile_end, tile_step;
+    {
+        const int G = gridDim.x, q = G >> 3, r = G & 7, x = blockIdx.x & 7;
+        const int px = q + (x < r ? 1 : 0);
+        const int wx = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+        // 32-bit products: the host launches fewer workgroups than tiles only while
+        // total * G < 2^31
+        tile_id = (int)((uint32_t)(total * wx) / (uint32_t)G) + (blockIdx.x >> 3);
+        tile_end = (int)((uint32_t)(total * (wx + px)) / (uint32_t)G);
+        tile_step = px;
+    }
+    if (tile_id >= tile_end)
+        return;
+
+    // Tile bookkeeping, wave-uniform: coordinates, group, the rows that are computed, and
+    // whether it has none (a contiguous block of padding rows, a masked tile past masked_m).
+    struct Tile {
+        int m0, n0, g, row_limit;
+        bool empty;
+    };
+    // raw per-tile data that comes from device memory: masked_m of the tile's group, or the
+    // contiguous row groups (lane l: rows m0 + l + 64 r for the group, and the lane's own
+    // epilogue rows)
+    int raw_cnt = 0;
+    int raw_max[BM / 64];
+    int raw_row[SM];
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
+    auto coords = [&](int t, int &tm, int &tn, int &g) {
+        if constexpr (MODE == MODE_MASKED) {
+            const int per_g = tiles_m * tiles_n;
+            g = t / per_g;
+            const int rem = t - g * per_g;
+            tn = rem / tiles_m;
+            tm = rem - tn * tiles_m;
+        } else {
+            raster(t, tiles_m, tiles_n, tm, tn);
+            g = 0;
         }
-        __syncthreads();
-        g = s_flag;
-        if (g < 0)
-            return;  // a block of padding rows only
-        row_limit = p.m;
-    } else {
-        raster(t, tiles_m, tiles_n, tm, tn);
-        row_limit = p.m;
-    }
-    const int m0 = tm * BM, n0 = tn * BN;
-    // masked form: the wave's row sub-tiles that hold a valid row (the others are never
-    // stored, so their MFMAs and promotions are skipped; copies and barriers are not)
-    int sm_act = SM;
-    if constexpr (MODE == MODE_MASKED) {
-        const int v = (row_limit - m0 - wm + 15) >> 4;
-        sm_act = __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > SM ? SM : v));
-    }
-    const uint8_t *B = p.b + (int64_t)g * N * K;
-    const float *SFB = p.sfb + (int64_t)g * NB * KB;
-    const int nkb = kb1 - kb0;
+    };
+    // a tile's place (its coordinates and group; the integer divisions of the tile mapping
+    // run here, outside the K loop), then its data from device memory
+    auto place = [&](int t) {
+        Tile u;
+        int tm, tn, g;
+        coords(t, tm, tn, g);
+        u.m0 = tm * BM;
+        u.n0 = tn * BN;
+        u.g = g;
+        u.row_limit = M;
+        u.empty = false;
+        return u;
+    };
+    auto load_meta = [&](const Tile &u) {
+        if constexpr (MODE == MODE_MASKED) {
+            raw_cnt = p.grp[u.g];
+        } else if constexpr (MODE == MODE_CONTIG) {
+#pragma unroll
+            for (int r = 0; r < BM / 64; ++r)
+                raw_max[r] = p.grp[u.m0 + lane + 64 * r];
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                raw_row[i] = p.grp[u.m0 + wm + 16 * i + fr];
+        }
+    };
+    int rowg_next[SM];  // contiguous: the epilogue rows' groups of the tile being prepared
+    auto finish_meta = [&](Tile u) {
+        if constexpr (MODE == MODE_MASKED) {
+            const int v = raw_cnt < 0 ? 0 : (raw_cnt > M ? M : raw_cnt);
+            u.row_limit = __builtin_amdgcn_readfirstlane(v);
+            u.empty = u.m0 >= u.row_limit;
+        } else if constexpr (MODE == MODE_CONTIG) {
+            int best = -1;
+#pragma unroll
+            for (int r = 0; r < BM / 64; ++r) {
+                const int v = raw_max[r];
+                best = max(best, (v >= 0 && v < p.num_groups) ? v : -1);
+            }
+            u.g = __builtin_amdgcn_readfirstlane(wave_max(best));
+            u.empty = u.g < 0;
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                rowg_next[i] = raw_row[i];
+        }
+        return u;
+    };
+
+    // copy resources of a tile: operands through buffer resources that end at the last valid
+    // row (rows past it read as zeros; an empty tile's are empty); the tile's offsets are in
+    // the resource bases, so the lane offsets below are the same for every tile.  They are
+    // rebuilt from the tile (scalar arithmetic) where used rather than kept for two tiles.
+    struct CopySrc {
+        __amdgpu_buffer_rsrc_t a, b, sa, sb;
+    };
+    auto copy_src = [&](const Tile &u) {
+        const int64_t ga = MODE == MODE_MASKED ? (int64_t)u.g * M : 0;
+        const uint8_t *A = p.a + ga * K;
+        const float *SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * KB * ld : 0);
+        const uint8_t *B = p.b + (int64_t)u.g * N * K;
+        const float *SFB = p.sfb + (int64_t)u.g * NB * KB;
+        const int nbf = u.n0 / KBLK;
+        CopySrc s;
+        s.a = make_rsrc(A + (int64_t)u.m0 * K, u.empty ? 0 : (int64_t)(u.row_limit - u.m0) * K);
+        s.b = make_rsrc(B + (int64_t)u.n0 * K, u.empty ? 0 : (int64_t)(N - u.n0) * K);
+        s.sa = make_rsrc(SFA + u.m0, u.empty ? 0 : ((int64_t)KB * ld - u.m0) * 4);
+        s.sb = make_rsrc(SFB + (int64_t)nbf * KB, u.empty ? 0 : (int64_t)(NB - nbf) * KB * 4);
+        return s;
+    };
 
     // ---- copies.  Wave w's copy c < CA of a block is A rows [8q, 8q+8) with q = w + c*NW;
     // copy CA + c is B rows [8q, 8q+8) with q = min(w + c*NW, IB-1) (a wave past the last B
-    // rows repeats it: same bytes to the same place); wave 0 also copies the block's A
-    // scales.  Lane l of a row copy fetches row 8q + l/8, logical chunk (l & 7) ^ h(row), so
-    // the contiguous 1 KB that the copy writes is the swizzled layout; h(row) = (q & 1) ^
-    // 2(l >> 4) because row bits 1, 2 are lane bits 4, 5 and row bit 3 is q's bit 0.  Operands are read through buffer resources that
-    // end at the last valid row, so rows past it read as zeros (their outputs are never
-    // stored); past the last K block the resources are empty and the copies only write
-    // zeros into slots nobody reads, which keeps the per-wave copy count constant.
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * K, (int64_t)(row_limit - m0) * K);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA, (int64_t)KB * ld * 4);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(SFB, (int64_t)NB * KB * 4);
-    // B scales of the tile's 128-column blocks nb_first + lane (lanes past the last block read
-    // zeros, never used): one float per lane, 256 bytes per K block
-    const int nb_first = n0 / KBLK;
-    const uint32_t lane_sfb = (uint32_t)((nb_first + lane) * KB) * 4u;
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(SFA, 0);
-    const uint32_t lane_even = (uint32_t)(lane >> 3) * (uint32_t)K +
-                               (uint32_t)((((lane & 7) ^ ((lane >> 4) << 1))) << 4);
-    const uint32_t lane_sfa = (uint32_t)(m0 + 4 * lane) * 4u;
+    // rows repeats it: same bytes to the same place); wave 0 also copies the block's A scales
+    // and the B scales of the tile's 128-column blocks.  Lane l of a row copy fetches row
+    // 8q + l/8, logical chunk (l & 7) ^ h(row), so the contiguous 1 KB that the copy writes is
+    // the swizzled layout; h(row) = (q & 1) ^ 2(l >> 4) because row bits 1, 2 are lane bits
+    // 4, 5 and row bit 3 is q's bit 0.  Copies of blocks past a workgroup's last come from
+    // empty resources and only write zeros into slots nobody reads, which keeps the per-wave
+    // copy count constant.
     const uint32_t lds_base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)lds;
     DG_LDS uint8_t *ldsp = (DG_LDS uint8_t *)lds;
-
-    // Per-copy lane offsets, fixed for the tile (the K block goes into the scalar offset):
-    // copy c's row group q and its lanes' byte offsets.  Held in registers, so issuing a copy
-    // costs no vector arithmetic.
+    // Per-copy lane offsets (the K block goes into the scalar offset): copy c's row group q
+    // and its lanes' byte offsets.  Held in registers during a tile's K loop, so issuing a
+    // copy costs no vector arithmetic.  These and the fragment addresses below are set again
+    // at every tile from an opaque copy of the lane id (set_lane_consts), so that they are
+    // dead, not held, through the epilogue, where the accumulators and C need the registers.
     int cq[MAXI];
-    uint32_t voff[MAXI];
 #pragma unroll
-    for (int c = 0; c < MAXI; ++c) {
+    for (int c = 0; c < MAXI; ++c)
         cq[c] = c < CA ? wave + c * NW : min(wave + (c - CA) * NW, IB - 1);
-        voff[c] = (lane_even ^ (uint32_t)((cq[c] & 1) << 4)) + (uint32_t)(8 * cq[c]) * (uint32_t)K;
-        asm volatile("" : "+v"(voff[c]));  // kept, not recomputed at each copy
-    }
+    uint32_t voff[MAXI];
+    uint32_t lane_sfa, lane_sfb;  // 4 A scales per lane; B scale block `lane`
     // issue copy c (a constant after unrolling) of K block kb into A slot aslot or B slot bslot
     // (a plain int parameter: a generic lambda here keeps the host pass from emitting the
     // kernel's launch stub)
-    auto issue_copy = [&](int c, int kb, int aslot, int bslot, __amdgpu_buffer_rsrc_t rA,
-                          __amdgpu_buffer_rsrc_t rB) {
+    auto issue_copy = [&](int c, int kb, int aslot, int bslot, const CopySrc &s) {
         if (c < CA)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rA, (DG_LDS void *)(ldsp + aslot * A_SLOT + cq[c] * 1024), 16, voff[c],
+                s.a, (DG_LDS void *)(ldsp + aslot * A_SLOT + cq[c] * 1024), 16, voff[c],
                 (uint32_t)kb * KBLK, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rB, (DG_LDS void *)(ldsp + B_BASE + bslot * B_SLOT + cq[c] * 1024), 16, voff[c],
+                s.b, (DG_LDS void *)(ldsp + B_BASE + bslot * B_SLOT + cq[c] * 1024), 16, voff[c],
                 (uint32_t)kb * KBLK, 0, 0);
     };
-    auto issue_scales = [&](int kb, int aslot, __amdgpu_buffer_rsrc_t rS,
-                            __amdgpu_buffer_rsrc_t rSB) {
+    auto issue_scales = [&](int kb, int aslot, const CopySrc &s) {
         if (wave == 0) {
+            // the K block's row offset goes into the range-checked lane offset: rows past the
+            // last scale row read zeros
             uint32_t vo = lane_sfa;
             asm volatile("" : "+v"(vo));
             vo += (uint32_t)((int64_t)kb * ld * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rS, (DG_LDS void *)(ldsp + SA_BASE + aslot * 1024), 16, vo, 0, 0, 0);
+                s.sa, (DG_LDS void *)(ldsp + SA_BASE + aslot * 1024), 16, vo, 0, 0, 0);
             uint32_t vb = lane_sfb;
             asm volatile("" : "+v"(vb));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rSB, (DG_LDS void *)(ldsp + SB_BASE + aslot * 256), 4, vb, (uint32_t)kb * 4u, 0,
+                s.sb, (DG_LDS void *)(ldsp + SB_BASE + aslot * 256), 4, vb, (uint32_t)kb * 4u, 0,
                 0);
         }
     };
@@ -247,54 +327,78 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
 
     // per-lane fragment offsets inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32) of
     // 16 consecutive rows, i.e. logical chunks 2g and 2g+1
-    const int fr = lane & 15;
-    const int fg = lane >> 4;
-    const int fh = ((fr >> 3) & 1) | (fr & 2) | (((fr >> 2) & 1) << 2);  // h(fr)
-    const uint32_t f_lo = (uint32_t)(fr * KBLK + (((2 * fg) ^ fh) << 4));
-    const uint32_t f_hi = (uint32_t)(fr * KBLK + (((2 * fg + 1) ^ fh) << 4));
-    const uint32_t a_lo = lds_base + (uint32_t)(wm * KBLK) + f_lo;
-    const uint32_t a_hi = lds_base + (uint32_t)(wm * KBLK) + f_hi;
-    const uint32_t sa_lane = lds_base + SA_BASE + (uint32_t)(wm + fr) * 4;
-    const uint32_t b_lo = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_lo;
-    const uint32_t b_hi = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_hi;
+    uint32_t a_lo, a_hi, sa_lane, b_lo, b_hi;
+    auto set_lane_consts = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int r = l & 15, gq = l >> 4;
+        const uint32_t lane_even =
+            (uint32_t)(l >> 3) * (uint32_t)K + (uint32_t)((((l & 7) ^ ((l >> 4) << 1))) << 4);
+#pragma unroll
+        for (int c = 0; c < MAXI; ++c)
+            voff[c] = (lane_even ^ (uint32_t)((cq[c] & 1) << 4)) + (uint32_t)(8 * cq[c]) * (uint32_t)K;
+        lane_sfa = (uint32_t)l * 16u;
+        lane_sfb = (uint32_t)l * (uint32_t)KB * 4u;
+        const int h = ((r >> 3) & 1) | (r & 2) | (((r >> 2) & 1) << 2);  // h(r)
+        const uint32_t f_lo = (uint32_t)(r * KBLK + (((2 * gq) ^ h) << 4));
+        const uint32_t f_hi = (uint32_t)(r * KBLK + (((2 * gq + 1) ^ h) << 4));
+        a_lo = lds_base + (uint32_t)(wm * KBLK) + f_lo;
+        a_hi = lds_base + (uint32_t)(wm * KBLK) + f_hi;
+        sa_lane = lds_base + SA_BASE + (uint32_t)(wm + r) * 4;
+        b_lo = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_lo;
+        b_hi = lds_base + B_BASE + (uint32_t)(wn * KBLK) + f_hi;
+    };
 
     // B scales.  A wave's columns touch at most two 128-column blocks, nb_lo and nb_lo + 1
     // (TN <= 128); each K block's two scales come from the LDS copy of the block's B scales
     // (read with the block's A fragments, so the main loop issues no global or scalar loads of
-    // its own: a scalar load would share the LDS reads' completion counter).
+    // its own: a scalar load would share the LDS reads' completion counter).  The LDS copy of
+    // a tile starts at its first block nb_first = n0 / 128.
     static_assert(TN <= KBLK, "a wave's columns must span at most two scale blocks");
-    const int nb_lo = min(n0 + wn, N - 1) / KBLK;
-    const int nb_hi = min(nb_lo + 1, NB - 1);
-    bool sb_hi[SN];  // sub-tile jj takes nb_hi's scale
+    struct ScaleSel {
+        uint32_t lo, hi;   // LDS byte offsets of the wave's two B scales in a block's area
+        uint32_t hi_mask;  // bit jj: sub-tile column jj takes the second one
+    };
+    auto scale_sel = [&](const Tile &u) {
+        ScaleSel s;
+        const int nbf = u.n0 / KBLK;
+        const int nb_lo = min(u.n0 + wn, N - 1) / KBLK;
+        const int nb_hi = min(nb_lo + 1, NB - 1);
+        s.lo = (uint32_t)(nb_lo - nbf) * 4;
+        s.hi = (uint32_t)(nb_hi - nbf) * 4;
+        s.hi_mask = 0;
 #pragma unroll
-    for (int j = 0; j < SN; ++j)
-        sb_hi[j] = min(n0 + wn + 16 * j, N - 1) / KBLK != nb_lo;
-    const uint32_t sb_lo_addr = lds_base + SB_BASE + (uint32_t)(nb_lo - nb_first) * 4;
-    const uint32_t sb_hi_addr = lds_base + SB_BASE + (uint32_t)(nb_hi - nb_first) * 4;
+        for (int j = 0; j < SN; ++j)
+            s.hi_mask |= (min(u.n0 + wn + 16 * j, N - 1) / KBLK != nb_lo ? 1u : 0u) << j;
+        return s;
+    };
     float vsb_lo, vsb_hi;  // this block's two B scales (all lanes equal)
+    auto read_sfb = [&](int aslot, const ScaleSel &s) {
+        vsb_lo = lds_read4(lds_base + SB_BASE + s.lo + (uint32_t)(aslot * 256));
+        vsb_hi = lds_read4(lds_base + SB_BASE + s.hi + (uint32_t)(aslot * 256));
+    };
 
-    // C, streamed into the accumulators (dense form).  Half h of column jj of the wave's
-    // sub-tiles (acc[i][jj] for the SM/2 row sub-tiles i of that half) takes its C values at
-    // step jj of block c_j0 + 2 jj + h, from registers cb loaded one block earlier (right
-    // after the previous half's add; the first half in the prologue).  The C traffic is thus
-    // spread over the K loop instead of arriving in one burst in the epilogue, with a block of
-    // compute to hide each load, and every add uses a compile-time accumulator index.
-    // Columns whose blocks lie past the last K block (short K) take C in the epilogue.
-    bool stream_c = false;
-    int c_j0 = 0;
-    __amdgpu_buffer_rsrc_t rc = rz;
-    uint32_t c_lane = 0;
-    if constexpr (MODE == MODE_DENSE) {
-        stream_c = p.c != nullptr;
-        c_j0 = max(0, nkb - 2 * SN);  // all columns streamed when nkb >= 2 SN
-        if (stream_c)
-            rc = make_rsrc(p.c + (int64_t)m0 * N, (int64_t)(row_limit - m0) * N * 4);
-        c_lane = (uint32_t)(((wm + fr) * N + n0 + wn + 4 * fg) * 4);
-    }
+    // C, streamed into the accumulators (dense form).  Block c_j0 + 2 jj + h loads half h of
+    // column jj of the wave's sub-tiles (acc[h*SM/2 + i][jj], i < SM/2) right after its opening
+    // barrier and adds it after its end-of-block wait for the next block's copies, which were
+    // issued after the load, so that wait already covers it and the compiler's own wait for the
+    // registers (within one iteration, where it can count) stalls nothing.  The C traffic is
+    // spread over the K loop instead of arriving in one burst in the epilogue.  Columns whose
+    // blocks lie past the last K block (short K) take C in the epilogue.
+    const bool stream_c = MODE == MODE_DENSE && p.c != nullptr;
+    auto c_first = [&]() { return max(0, nkb - 2 * SN); };  // all columns streamed when nkb >= 2 SN
+    const uint32_t c_lane = (uint32_t)(((wm + fr) * N + wn + 4 * fg) * 4);
+    auto c_src = [&](const Tile &u) {
+        if (!stream_c && MODE == MODE_DENSE && p.c == nullptr)
+            return make_rsrc(p.sfa, 0);
+        // C rows from m0 on, columns from n0 on; rows past the last valid one read zeros
+        return make_rsrc(p.c + (int64_t)u.m0 * N + u.n0,
+                         ((int64_t)(u.row_limit - u.m0) * N - u.n0) * 4);
+    };
     static_assert(SM % 2 == 0, "C is streamed in halves of the row sub-tiles");
     constexpr int HM = SM / 2;
     v4f cb[HM];
-    auto load_c_half = [&](int jj, int h) {
+    auto load_c_half = [&](const __amdgpu_buffer_rsrc_t &rc, int jj, int h) {
 #pragma unroll
         for (int i = 0; i < HM; ++i)
             cb[i] = __builtin_bit_cast(
@@ -302,19 +406,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
                          rc, c_lane + (uint32_t)((16 * (h * HM + i) * N + 16 * jj) * 4), 0, 0));
     };
     // both halves of column jj were streamed (the second half's block is the later one)
-    auto c_streamed = [&](int jj) { return stream_c && c_j0 + 2 * jj + 1 < nkb; };
-    auto read_sfb = [&](int aslot) {
-        vsb_lo = lds_read4(sb_lo_addr + (uint32_t)(aslot * 256));
-        vsb_hi = lds_read4(sb_hi_addr + (uint32_t)(aslot * 256));
-    };
+    auto c_streamed = [&](int jj) { return stream_c && c_first() + 2 * jj + 1 < nkb; };
 
     v4f acc[SM][SN];
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
     // Fragments.  A (all SM row sub-tiles) and its scales S are held for a whole block; during
     // the block's last step each A[i] / S[i] is replaced by the next block's right after the
     // last MFMA that reads it.  B fragments are read two steps ahead; the next block's B(0)
@@ -323,28 +417,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
     float Sf[SM];
     v4i Bf[NBUF][2];
     // MFMA partials of the previous step, promoted during the next one, and (across a block
-    // boundary) the scales of the last step's partials.  Zero before the first step: a no-op.
+    // boundary) the scales of the last step's partials.  Zero before a tile's first step.
     v4f pend[SM];
     float psc[SM];
+    auto clear_tile_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        pend[i] = v4f{0.f, 0.f, 0.f, 0.f};
-        psc[i] = 0.f;
-    }
+        for (int i = 0; i < SM; ++i) {
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+                acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            pend[i] = v4f{0.f, 0.f, 0.f, 0.f};
+            psc[i] = 0.f;
+        }
+    };
     float sb_cur[SN];
     // When every wave's columns lie in one 128-column scale block (BN a multiple of 128 and
     // TN dividing 128), a row's promotion scale is the same for all of its sub-tiles in a
     // block: scb[i] = sa[i] * sb, formed once per block instead of once per MFMA.
     constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0);
     float scb[SM];
-    auto take_sfb = [&]() {
+    auto take_sfb = [&](uint32_t hi_mask) {
         tie(vsb_lo);
         tie(vsb_hi);
         const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_lo)));
         const float hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_hi)));
 #pragma unroll
         for (int jj = 0; jj < SN; ++jj)
-            sb_cur[jj] = sb_hi[jj] ? hi : lo;
+            sb_cur[jj] = ((hi_mask >> jj) & 1) ? hi : lo;
     };
 
     // fragment reads from slot bases (a_lo/a_hi/sa of an A slot, b_lo/b_hi of a B slot) with
@@ -360,6 +459,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         bf[0] = lds_read16_at<jj * 16 * KBLK>(blo);
         bf[1] = lds_read16_at<jj * 16 * KBLK>(bhi);
     };
+
+    // the current tile and what depends on it
+    Tile cur = place(tile_id);
+    load_meta(cur);
+    cur = finish_meta(cur);
+    int rowg[SM];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+        rowg[i] = rowg_next[i];
+    ScaleSel sel = scale_sel(cur);
+    // masked form: the wave's row sub-tiles that hold a valid row (the others are never
+    // stored, so their MFMAs and promotions are skipped; copies and barriers are not).  The
+    // contiguous form computes every row sub-tile (an all-padding tile, rare, multiplies the
+    // zeros its empty copies wrote and stores nothing).
+    auto active_rows = [&](const Tile &u) {
+        if constexpr (MODE == MODE_MASKED) {
+            const int v = (u.row_limit - u.m0 - wm + 15) >> 4;
+            return __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > SM ? SM : v));
+        } else {
+            return u.empty ? 0 : SM;
+        }
+    };
+    int sm_act = active_rows(cur);
+    // the next tile, placed before the current one's K loop and completed during its first
+    // block; its first DEPTH blocks are copied during the current one's last DEPTH blocks
+    // when the K loop is long enough to hold them (else its prologue runs after the current
+    // tile's epilogue)
+    bool has_next = PERSIST && tile_id + tile_step < tile_end;
+    const bool overlap = nkb >= DEPTH + 1;
+    Tile nxt = cur;
+    ScaleSel nsel = sel;
 
     // One MFMA step: for each row sub-tile i, first promote the previous step's partial of row
     // i (issued SM MFMAs earlier, so it is ready) with scale `scale(i)`, then issue MFMA
@@ -387,70 +517,286 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
         });
     };
 
-    // C of column JJ's half added when block j is that half's block, then the next half loaded
-    auto c_step = [&](int j, auto JJ) {
-        constexpr int jj = decltype(JJ)::value;
-        if constexpr (MODE == MODE_DENSE) {
-            // only columns whose two halves both fall inside the K loop; the others take all
-            // of their C in the epilogue
-            if (c_streamed(jj) && j == c_j0 + 2 * jj) {
+    // C half-column q = j - c_j0 of block j: column q / 2, row half q % 2, added at the end of
+    // the block whose start loaded it (compile-time accumulator indices behind a uniform
+    // switch on the column)
+    auto add_c_half = [&](int q) {
+        static_for<SN>([&](auto JJ) {
+            constexpr int jj = decltype(JJ)::value;
+            // each arm ends in an asm statement with its own constant: without it the compiler
+            // merges the arms into one add through a runtime accumulator index and moves the
+            // accumulators to scratch memory
+            if (q == 2 * jj) {
 #pragma unroll
                 for (int i = 0; i < HM; ++i)
                     acc[i][jj] += cb[i];
-                load_c_half(jj, 1);
+                asm volatile("; C half %0" ::"n"(2 * jj));
             }
-            if (c_streamed(jj) && j == c_j0 + 2 * jj + 1) {
+            if (q == 2 * jj + 1) {
 #pragma unroll
                 for (int i = 0; i < HM; ++i)
                     acc[HM + i][jj] += cb[i];
-                if constexpr (jj + 1 < SN) {
-                    if (c_streamed(jj + 1))
-                        load_c_half(jj + 1, 0);
-                }
+                asm volatile("; C half %0" ::"n"(2 * jj + 1));
             }
-        }
+        });
     };
 
-    // ---- prologue: blocks 0 .. DEPTH-1 in flight, block 0's fragments read
-    if constexpr (MODE == MODE_DENSE) {
-        if (c_streamed(0))
-            load_c_half(0, 0);  // older than every copy: landed once the first copies have
-    }
-    // (blocks past the last are copied from empty resources, which keeps the per-wave copy
-    // count constant)
+    // A slot of the current block (block j of the workgroup's stream of blocks, tiles end to
+    // end): j % DEPTH; its B slot: j % (DEPTH + 1).  They run on across tiles.
+    int aslot = 0;
+    int bslot = 0;
+    // block 0's fragments of the current tile, from the current slots (landed and past a
+    // barrier)
+    auto read_first = [&]() {
+        const uint32_t ao = (uint32_t)(aslot * A_SLOT), bo = (uint32_t)(bslot * B_SLOT);
+        static_for<SM>(
+            [&](auto I) { read_a(a_lo + ao, a_hi + ao, sa_lane + (uint32_t)(aslot * 1024), I); });
+        read_sfb(aslot, sel);
+        read_b(b_lo + bo, b_hi + bo, std::integral_constant<int, 0>{}, Bf[0]);
+        if constexpr (SN > 1)
+            read_b(b_lo + bo, b_hi + bo, std::integral_constant<int, 1>{}, Bf[1]);
+    };
+    // prologue of a tile: its blocks 0 .. DEPTH-1 in flight (blocks past the last are copied
+    // from empty resources), block 0's fragments read
+    auto start_tile = [&]() {
+        int as = aslot, bs = bslot;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-        const bool in = d < nkb;
-        issue_scales(in ? kb0 + d : kb0, d, in ? rs : rz, in ? rsb : rz);
+        for (int d = 0; d < DEPTH; ++d) {
+            const bool in = d < nkb;
+            Tile u = cur;
+            u.empty = u.empty || !in;
+            const CopySrc s = copy_src(u);
+            issue_scales(in ? d : 0, as, s);
 #pragma unroll
-        for (int c = 0; c < MAXI; ++c)
-            issue_copy(c, in ? kb0 + d : kb0, d, d, in ? ra : rz, in ? rb : rz);
-    }
-    wait_older_copies();
-    bare_barrier();
-    static_for<SM>([&](auto I) { read_a(a_lo, a_hi, sa_lane, I); });
-    read_sfb(0);
-    read_b(b_lo, b_hi, std::integral_constant<int, 0>{}, Bf[0]);
-    if constexpr (SN > 1)
-        read_b(b_lo, b_hi, std::integral_constant<int, 1>{}, Bf[1]);
+            for (int c = 0; c < MAXI; ++c)
+                issue_copy(c, in ? d : 0, as, bs, s);
+            as = as == DEPTH - 1 ? 0 : as + 1;
+            bs = bs == DEPTH ? 0 : bs + 1;
+        }
+        wait_older_copies();
+        bare_barrier();
+        read_first();
+    };
 
-    int aslot = 0;  // A slot of the current block: j % DEPTH
-    int bslot = 0;  // B slot of the current block: j % (DEPTH + 1)
-    for (int j = 0; j < nkb; ++j) {
-        const bool refill = j + DEPTH < nkb;
-        const int kb_fill = refill ? kb0 + j + DEPTH : kb0;
-        const __amdgpu_buffer_rsrc_t fa = refill ? ra : rz;
-        const __amdgpu_buffer_rsrc_t fb = refill ? rb : rz;
-        const __amdgpu_buffer_rsrc_t fs = refill ? rs : rz;
-        const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
-        const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
-        const int an = aslot == DEPTH - 1 ? 0 : aslot + 1;
-        // slot bases of this block's B reads and of the next block's A and B reads
-        const uint32_t blo_c = b_lo + (uint32_t)(bslot * B_SLOT);
-        const uint32_t bhi_c = b_hi + (uint32_t)(bslot * B_SLOT);
-        // this block's A fragments and scales and its B(0), B(1) were read during the last
-        // step of the previous block
+    bool first = true;
+    for (;;) {
+        set_dims();
+        const int c_j0 = c_first();
+        // a tile with nothing to compute (a masked group with masked_m past its rows, a
+        // contiguous block of padding) is skipped; the tile after it starts the pipeline anew
+        if (cur.empty) {
+            if (!has_next)
+                break;
+            tile_id += tile_step;
+            cur = place(tile_id);
+            load_meta(cur);
+            cur = finish_meta(cur);
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                rowg[i] = rowg_next[i];
+            sel = scale_sel(cur);
+            sm_act = active_rows(cur);
+            has_next = PERSIST && tile_id + tile_step < tile_end;
+            first = true;
+            continue;
+        }
+        set_lane_consts();
+        clear_tile_state();
+        // a tile's first blocks were copied during the previous tile when it overlapped
+        if (first || !overlap)
+            start_tile();
+        else
+            read_first();
+        first = false;
+        const bool prefetch = has_next && overlap;
+        if (has_next)
+            nxt = place(tile_id + tile_step);
+        const __amdgpu_buffer_rsrc_t rc = c_src(cur);
+        // K block j of the tile, whose refill copies (block kb_fill of the tile behind fs) go
+        // out during its steps
+        auto block = [&](int j, const CopySrc &fs, int kb_fill) {
+            const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
+            const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
+            const int an = aslot == DEPTH - 1 ? 0 : aslot + 1;
+            // slot bases of this block's B reads and of the next block's A and B reads
+            const uint32_t blo_c = b_lo + (uint32_t)(bslot * B_SLOT);
+            const uint32_t bhi_c = b_hi + (uint32_t)(bslot * B_SLOT);
+            // this block's A fragments and scales and its B(0), B(1) were read during the
+            // last step of the previous block (or the tile's prologue)
+            lds_wait();
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                tie(Af[i][0]);
+                tie(Af[i][1]);
+                tie(Sf[i]);
+            }
+            tie(Bf[0][0]);
+            tie(Bf[0][1]);
+            if constexpr (SN > 1) {
+                tie(Bf[1][0]);
+                tie(Bf[1][1]);
+            }
+            take_sfb(sel.hi_mask);
+            if constexpr (ONE_NB) {
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+                    scb[i] = Sf[i] * sb_cur[0];
+            }
+            // every wave holds this block's A: its A slot may take block j+DEPTH, whose B
+            // slot (block j-1's) was released at the previous block's second barrier
+            bare_barrier();
+            // this block's half-column of C: loaded now, added after the end-of-block wait
+            // for the next block's copies, which it precedes (so that wait covers it); only
+            // columns whose two halves both fall inside the loop are streamed
+            const int cq = j - c_j0;
+            const bool c_now = stream_c && cq >= 0 && c_j0 + 2 * (cq >> 1) + 1 < nkb;
+            if constexpr (MODE == MODE_DENSE) {
+                if (c_now)
+                    load_c_half(rc, cq >> 1, cq & 1);
+            }
+            // the next tile's data from device memory, loaded at the first block's start and
+            // used at its end
+            if constexpr (MODE != MODE_DENSE) {
+                if (j == 0 && has_next)
+                    load_meta(nxt);
+            }
+            issue_scales(kb_fill, aslot, fs);
+            if constexpr (SN == 1)
+#pragma unroll
+                for (int c = 0; c < MAXI; ++c)
+                    issue_copy(c, kb_fill, aslot, bslot_fill, fs);
+            // steps 0 .. SN-2, with this block's refill copies spread over them
+            static_for<SN - 1>([&](auto JJ) {
+                constexpr int jj = decltype(JJ)::value;
+                auto extra = [&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (i == 0 && jj + 2 < SN)
+                        read_b(blo_c, bhi_c, std::integral_constant<int, jj + 2>{},
+                               Bf[bbuf(jj + 2, SN)]);
+                    // copies c with c * (SN - 1) / MAXI == jj, after MFMAs 0, 2, ...
+#pragma unroll
+                    for (int c = 0; c < MAXI; ++c) {
+                        if ((c * (SN - 1)) / MAXI == jj) {
+                            const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
+                            const int pos = c - first;
+                            if (i == (SM == 1 ? 0 : (pos * 2) % SM))
+                                issue_copy(c, kb_fill, aslot, bslot_fill, fs);
+                        }
+                    }
+                };
+                if constexpr (jj >= 2) {
+                    // B(jj) was read two steps ago; only B(jj+1), read one step ago, may be in
+                    // flight (LDS reads retire in order)
+                    lds_wait_n<2>();
+                    tie(Bf[bbuf(jj, SN)][0]);
+                    tie(Bf[bbuf(jj, SN)][1]);
+                }
+                if constexpr (jj == 0)
+                    mfma_step(JJ, Bf[0], [&](int i) { return psc[i]; }, extra);
+                else
+                    mfma_step(JJ, Bf[bbuf(jj, SN)],
+                              [&](int i) { return ONE_NB ? scb[i] : Sf[i] * sb_cur[jj - 1]; },
+                              extra);
+            });
+            // last step: the next block's copies have landed everywhere (past the last block
+            // of the workgroup the reads below are harmless and unused)
+            wait_older_copies();
+            bare_barrier();
+            lds_wait();
+            if constexpr (SN >= 2) {
+                tie(Bf[bbuf(SN - 1, SN)][0]);
+                tie(Bf[bbuf(SN - 1, SN)][1]);
+            }
+            if constexpr (MODE == MODE_DENSE) {
+                if (c_now)
+                    add_c_half(cq);
+            }
+            if (j == 0 && has_next) {
+                nxt = finish_meta(nxt);
+                nsel = scale_sel(nxt);
+            }
+            // the next block's fragments; after a tile's last block they are dropped (waited
+            // for right after the loop) and the next tile's first block is read again after
+            // the epilogue, so that no fragments are live next to the accumulators and the
+            // epilogue's C (reading them under a condition instead would keep both the old
+            // and the new fragments live across the branch)
+            const uint32_t alo_n = a_lo + (uint32_t)(an * A_SLOT);
+            const uint32_t ahi_n = a_hi + (uint32_t)(an * A_SLOT);
+            const uint32_t sa_n = sa_lane + (uint32_t)(an * 1024);
+            const uint32_t blo_n = b_lo + (uint32_t)(bslot_next * B_SLOT);
+            const uint32_t bhi_n = b_hi + (uint32_t)(bslot_next * B_SLOT);
+            constexpr auto C0 = std::integral_constant<int, 0>{};
+            constexpr auto C1 = std::integral_constant<int, 1>{};
+            if constexpr (SN == 1) {
+                mfma_step(C0, Bf[0],
+                          [&](int i) {
+                              const float prev = psc[i];
+                              psc[i] = Sf[i] * sb_cur[0];
+                              return prev;
+                          },
+                          [&](auto I) {
+                              constexpr int i = decltype(I)::value;
+                              read_a(alo_n, ahi_n, sa_n, I);
+                              if constexpr (i == 0)
+                                  read_sfb(an, sel);
+                              if constexpr (i == SM - 1)  // after the last MFMA reading B(0)
+                                  read_b(blo_n, bhi_n, C0, Bf[0]);
+                          });
+            } else {
+                mfma_step(std::integral_constant<int, SN - 1>{}, Bf[bbuf(SN - 1, SN)],
+                          [&](int i) {
+                              psc[i] = ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 1];
+                              return ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 2];
+                          },
+                          [&](auto I) {
+                              constexpr int i = decltype(I)::value;
+                              // B(0) (and B(1) when SN > 2) were last read steps ago; with
+                              // SN == 2, B(1) is this step's and is replaced after its last MFMA
+                              if constexpr (i == 0) {
+                                  read_b(blo_n, bhi_n, C0, Bf[0]);
+                                  read_sfb(an, sel);
+                              }
+                              if constexpr (i == (SN > 2 ? (SM > 1 ? 1 : 0) : SM - 1))
+                                  read_b(blo_n, bhi_n, C1, Bf[1]);
+                              read_a(alo_n, ahi_n, sa_n, I);
+                          });
+            }
+            aslot = an;
+            bslot = bslot_next;
+        };
+        // Blocks whose refills belong to this tile, then the last DEPTH blocks, whose refills
+        // are the next tile's first blocks when it is prefetched (else nothing): each phase
+        // holds one set of copy resources.
+        // (One workgroup per tile: one loop, whose last DEPTH blocks refill from empty
+        // resources.)
+        if constexpr (PERSIST) {
+            const int j_sw = nkb > DEPTH ? nkb - DEPTH : 0;
+            {
+                const CopySrc s1 = copy_src(cur);
+                for (int j = 0; j < j_sw; ++j)
+                    block(j, s1, j + DEPTH);
+            }
+            {
+                Tile u = nxt;
+                u.empty = u.empty || !prefetch;
+                const CopySrc s2 = copy_src(u);
+                for (int j = j_sw; j < nkb; ++j)
+                    block(j, s2, prefetch ? j + DEPTH - nkb : 0);
+            }
+        } else {
+            const CopySrc s1 = copy_src(cur);
+            Tile e = cur;
+            e.empty = true;
+            const CopySrc s0 = copy_src(e);
+            for (int j = 0; j < nkb; ++j) {
+                const bool own = j + DEPTH < nkb;
+                block(j, own ? s1 : s0, own ? j + DEPTH : 0);
+            }
+        }
+        // the fragments read during the last step land before their registers can be reused
         lds_wait();
+        tie(vsb_lo);
+        tie(vsb_hi);
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
             tie(Af[i][0]);
@@ -463,210 +809,127 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, int tiles_m, int ti
             tie(Bf[1][0]);
             tie(Bf[1][1]);
         }
-        take_sfb();
-        if constexpr (ONE_NB) {
+        // the tile's last partials
 #pragma unroll
-            for (int i = 0; i < SM; ++i)
-                scb[i] = Sf[i] * sb_cur[0];
+        for (int i = 0; i < SM; ++i)
+            if (MODE != MODE_MASKED || i < sm_act)
+                acc[i][SN - 1] += pend[i] * psc[i];
+
+        // ---- epilogue: + C (columns not streamed), round to bf16, store the valid rows from
+        // registers (the LDS holds the next tile's first blocks)
+        if constexpr (MODE == MODE_DENSE) {
+            if (p.c) {
+                v4f cv[SM][SN];
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+#pragma unroll
+                    for (int j = 0; j < SN; ++j)
+                        cv[i][j] = c_streamed(j)
+                                       ? v4f{0.f, 0.f, 0.f, 0.f}
+                                       : __builtin_bit_cast(
+                                             v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rc, c_lane + (uint32_t)((16 * i * N + 16 * j) * 4),
+                                                      0, 0));
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+#pragma unroll
+                    for (int j = 0; j < SN; ++j)
+                        acc[i][j] += cv[i][j];
+            }
         }
-        // every wave holds this block's A: its A slot may take block j+DEPTH, whose B slot
-        // (block j-1's) was released at the previous block's second barrier
-        bare_barrier();
-        issue_scales(kb_fill, aslot, fs, refill ? rsb : rz);
-        if constexpr (SN == 1)
+        uint16_t *D = p.d + (MODE == MODE_MASKED ? (int64_t)cur.g * M * N : 0);
+        if constexpr (PERSIST) {
+            // from registers: the LDS holds the next tile's first blocks
+            if (!cur.empty) {
 #pragma unroll
-            for (int c = 0; c < MAXI; ++c)
-                issue_copy(c, kb_fill, aslot, bslot_fill, fa, fb);
-        // steps 0 .. SN-2, with this block's refill copies spread over them
-        static_for<SN - 1>([&](auto JJ) {
-            constexpr int jj = decltype(JJ)::value;
-            auto extra = [&](auto I) {
-                constexpr int i = decltype(I)::value;
-                if constexpr (i == 0 && jj + 2 < SN)
-                    read_b(blo_c, bhi_c, std::integral_constant<int, jj + 2>{},
-                           Bf[bbuf(jj + 2, SN)]);
-                // copies c with c * (SN - 1) / MAXI == jj, after MFMAs 0, 2, ...
+                for (int i = 0; i < SM; ++i) {
+                    const int row = cur.m0 + wm + 16 * i + fr;
+                    bool ok = row < cur.row_limit;
+                    if constexpr (MODE == MODE_CONTIG)
+                        ok = ok && rowg[i] == cur.g;
 #pragma unroll
-                for (int c = 0; c < MAXI; ++c) {
-                    if ((c * (SN - 1)) / MAXI == jj) {
-                        const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
-                        const int pos = c - first;
-                        if (i == (SM == 1 ? 0 : (pos * 2) % SM))
-                            issue_copy(c, kb_fill, aslot, bslot_fill, fa, fb);
+                    for (int j = 0; j < SN; ++j) {
+                        const int col = cur.n0 + wn + 16 * j + 4 * fg;
+                        if (ok && col < N)
+                            store8_async(D + (int64_t)row * N + col,
+                                         pack_bf16x2(acc[i][j].x, acc[i][j].y),
+                                         pack_bf16x2(acc[i][j].z, acc[i][j].w));
                     }
                 }
-            };
-            if constexpr (jj >= 2) {
-                // B(jj) was read two steps ago; only B(jj+1), read one step ago, may be in
-                // flight (LDS reads retire in order)
-                lds_wait_n<2>();
-                tie(Bf[bbuf(jj, SN)][0]);
-                tie(Bf[bbuf(jj, SN)][1]);
             }
-            c_step(j, JJ);
-            if constexpr (jj == 0)
-                mfma_step(JJ, Bf[0], [&](int i) { return psc[i]; }, extra);
-            else
-                mfma_step(JJ, Bf[bbuf(jj, SN)],
-                          [&](int i) { return ONE_NB ? scb[i] : Sf[i] * sb_cur[jj - 1]; },
-                          extra);
-        });
-        // last step: the next block's copies have landed everywhere (past the last block the
-        // reads below are harmless and unused)
-        wait_older_copies();
-        bare_barrier();
-        lds_wait();
-        if constexpr (SN >= 2) {
-            tie(Bf[bbuf(SN - 1, SN)][0]);
-            tie(Bf[bbuf(SN - 1, SN)][1]);
-        }
-        const uint32_t alo_n = a_lo + (uint32_t)(an * A_SLOT);
-        const uint32_t ahi_n = a_hi + (uint32_t)(an * A_SLOT);
-        const uint32_t sa_n = sa_lane + (uint32_t)(an * 1024);
-        const uint32_t blo_n = b_lo + (uint32_t)(bslot_next * B_SLOT);
-        const uint32_t bhi_n = b_hi + (uint32_t)(bslot_next * B_SLOT);
-        c_step(j, std::integral_constant<int, SN - 1>{});
-        constexpr auto C0 = std::integral_constant<int, 0>{};
-        constexpr auto C1 = std::integral_constant<int, 1>{};
-        if constexpr (SN == 1) {
-            mfma_step(C0, Bf[0],
-                      [&](int i) {
-                          const float prev = psc[i];
-                          psc[i] = Sf[i] * sb_cur[0];
-                          return prev;
-                      },
-                      [&](auto I) {
-                          constexpr int i = decltype(I)::value;
-                          read_a(alo_n, ahi_n, sa_n, I);
-                          if constexpr (i == 0)
-                              read_sfb(an);
-                          if constexpr (i == SM - 1)  // after the last MFMA that reads B(0)
-                              read_b(blo_n, bhi_n, C0, Bf[0]);
-                      });
         } else {
-            mfma_step(std::integral_constant<int, SN - 1>{}, Bf[bbuf(SN - 1, SN)],
-                      [&](int i) {
-                          psc[i] = ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 1];
-                          return ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 2];
-                      },
-                      [&](auto I) {
-                          constexpr int i = decltype(I)::value;
-                          // B(0) (and B(1) when SN > 2) were last read steps ago; with
-                          // SN == 2, B(1) is this step's and is replaced after its last MFMA
-                          if constexpr (i == 0) {
-                              read_b(blo_n, bhi_n, C0, Bf[0]);
-                              read_sfb(an);
-                          }
-                          if constexpr (i == (SN > 2 ? (SM > 1 ? 1 : 0) : SM - 1))
-                              read_b(blo_n, bhi_n, C1, Bf[1]);
-                          read_a(alo_n, ahi_n, sa_n, I);
-                      });
-        }
-        aslot = an;
-        bslot = bslot_next;
-    }
-    // the last block also read (unused) fragments: they must land before their registers
-    // can be reused
-    lds_wait();
-    tie(vsb_lo);
-    tie(vsb_hi);
-#pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        tie(Af[i][0]);
-        tie(Af[i][1]);
-        tie(Sf[i]);
-    }
-    tie(Bf[0][0]);
-    tie(Bf[0][1]);
-    if constexpr (SN > 1) {
-        tie(Bf[1][0]);
-        tie(Bf[1][1]);
-    }
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-        acc[i][SN - 1] += pend[i] * psc[i];
-    wait_vm<0>();  // no copy may still be writing LDS past this point
-
-    // ---- epilogue: + C, round to bf16, store the valid rows.  All of the wave's C values (and
-    // row groups) are requested before any is used, so the loads overlap instead of each
-    // waiting for the one before; C goes through a buffer resource bounded by the valid rows,
-    // which returns zeros past them (only valid rows are stored).
-    if constexpr (MODE == MODE_DENSE) {
-        if (p.c) {
-            const __amdgpu_buffer_rsrc_t rcc =
-                make_rsrc(p.c + (int64_t)m0 * N, (int64_t)(row_limit - m0) * N * 4);
-            v4f cv[SM][SN];
+            // Through LDS, free once every copy has landed (one tile per workgroup): each wave
+            // writes its sub-tiles there as bf16 (8 bytes per lane), then every thread stores
+            // whole 16-byte pieces of rows, so a wave's store covers contiguous row segments
+            // instead of sixteen 32-byte pieces.  Output rows are OS bytes apart in LDS; OS = 32
+            // (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct banks.
+            constexpr int NT = 64 * NW;
+            constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
+            static_assert(rows_on_distinct_banks(OS), "output row stride");
+            static_assert(BM * OS <= LDS_BYTES, "output tile fits the operand slots");
+            constexpr int CPR = BN / 8;  // 16-byte pieces per output row
+            static_assert((BM * CPR) % NT == 0, "output pieces split evenly over the threads");
+            constexpr int PPT = BM * CPR / NT;  // pieces per thread
+            wait_vm<0>();
+            bare_barrier();  // every wave is past its last fragment read and copy
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
                 for (int j = 0; j < SN; ++j)
-                    cv[i][j] = c_streamed(j)
-                                   ? v4f{0.f, 0.f, 0.f, 0.f}
-                                   : __builtin_bit_cast(
-                                         v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rcc, c_lane + (uint32_t)((16 * i * N + 16 * j) * 4),
-                                                  0, 0));
+                    lds_write8(lds_base + (uint32_t)((wm + 16 * i + fr) * OS +
+                                                     (wn + 16 * j + 4 * fg) * 2),
+                               pack_bf16x2(acc[i][j].x, acc[i][j].y),
+                               pack_bf16x2(acc[i][j].z, acc[i][j].w));
+            lds_wait();
+            bare_barrier();
+            v4i piece[PPT];
 #pragma unroll
-            for (int i = 0; i < SM; ++i)
+            for (int t = 0; t < PPT; ++t) {
+                const int q = tid + t * NT;
+                piece[t] = lds_read16(lds_base + (uint32_t)((q / CPR) * OS + (q % CPR) * 16));
+            }
+            int prow[PPT];
+            if constexpr (MODE == MODE_CONTIG) {
 #pragma unroll
-                for (int j = 0; j < SN; ++j)
-                    acc[i][j] += cv[i][j];
+                for (int t = 0; t < PPT; ++t)
+                    prow[t] = p.grp[cur.m0 + (tid + t * NT) / CPR];
+            }
+            lds_wait();
+            if (!cur.empty) {
+#pragma unroll
+                for (int t = 0; t < PPT; ++t) {
+                    const int q = tid + t * NT;
+                    const int row = cur.m0 + q / CPR;
+                    const int col = cur.n0 + (q % CPR) * 8;
+                    bool ok = row < cur.row_limit && col < N;
+                    if constexpr (MODE == MODE_CONTIG)
+                        ok = ok && prow[t] == cur.g;
+                    if (ok)
+                        *reinterpret_cast<v4i *>(D + (int64_t)row * N + col) = piece[t];
+                }
+            }
         }
+        if (!has_next)
+            break;
+        // ---- on to the next tile
+        tile_id += tile_step;
+        cur = nxt;
+        sel = nsel;
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+            rowg[i] = rowg_next[i];
+        sm_act = active_rows(cur);
+        has_next = PERSIST && tile_id + tile_step < tile_end;
     }
-    // The tile goes out through LDS: each wave writes its sub-tiles there as bf16 (8 bytes per
-    // lane), then every thread stores whole 16-byte pieces of rows, so a wave's store covers
-    // contiguous row segments instead of sixteen 32-byte pieces.  Output rows are OS bytes
-    // apart in LDS; OS = 32 (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct
-    // banks (two 256-byte halves).
-    constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
-    static_assert(rows_on_distinct_banks(OS), "output row stride");
-    static_assert(BM * OS <= LDS_BYTES, "output tile fits the operand slots");
-    constexpr int CPR = BN / 8;  // 16-byte pieces per output row
-    static_assert((BM * CPR) % NT == 0, "output pieces split evenly over the threads");
-    constexpr int PPT = BM * CPR / NT;  // pieces per thread
-    bare_barrier();  // every wave is past its last fragment read and copy: LDS is free
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j) {
-            const uint32_t lo = pack_bf16x2(acc[i][j].x, acc[i][j].y);
-            const uint32_t hi = pack_bf16x2(acc[i][j].z, acc[i][j].w);
-            lds_write8(lds_base + (uint32_t)((wm + 16 * i + fr) * OS + (wn + 16 * j + 4 * fg) * 2),
-                       lo, hi);
-        }
-    lds_wait();
-    bare_barrier();
-    v4i piece[PPT];
-#pragma unroll
-    for (int t = 0; t < PPT; ++t) {
-        const int q = tid + t * NT;
-        piece[t] = lds_read16(lds_base + (uint32_t)((q / CPR) * OS + (q % CPR) * 16));
-    }
-    int rowg[PPT];
-    if constexpr (MODE == MODE_CONTIG) {
-#pragma unroll
-        for (int t = 0; t < PPT; ++t)
-            rowg[t] = s_grp[(tid + t * NT) / CPR];
-    }
-    lds_wait();
-#pragma unroll
-    for (int t = 0; t < PPT; ++t) {
-        const int q = tid + t * NT;
-        const int row = m0 + q / CPR;
-        const int col = n0 + (q % CPR) * 8;
-        bool ok = row < row_limit && col < N;
-        if constexpr (MODE == MODE_CONTIG)
-            ok = ok && rowg[t] == g;
-        if (ok)
-            *reinterpret_cast<v4i *>(D + (int64_t)row * N + col) = piece[t];
-    }
+    // no copy may still be writing LDS (or store still reading registers) past this point
+    wait_vm<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH, int MODE>
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST>
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
-    gemm_tile<BM, BN, WM, WN, DEPTH, MODE>(p, tiles_m, tiles_n);
+    gemm_tiles<BM, BN, WM, WN, DEPTH, MODE, PERSIST>(p, tiles_m, tiles_n);
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -681,6 +944,17 @@ static void tiles_for(int mode, int cfg, const GemmArgs &a, int &tiles_m, int &t
         tiles_m = (a.m + ti.bm - 1) / ti.bm;
 }
 
+// Workgroups for `total` tiles: one per tile, or for a persistent tile configuration at most
+// one per CU (each then loops over its share), as long as the kernel's 32-bit tile-range
+// arithmetic (total * workgroups < 2^31) holds.
+static int64_t workgroups(int64_t total, bool persistent, const GemmArgs &a)
+{
+    if (persistent && a.max_wgs > 0 && total > a.max_wgs &&
+        total * (int64_t)a.max_wgs < ((int64_t)1 << 31))
+        return a.max_wgs;
+    return total;
+}
+
 int64_t grid_size(int mode, int cfg, const GemmArgs &a)
 {
     if (cfg == CFG_STREAM64)
@@ -690,34 +964,35 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     int64_t g = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         g *= a.num_groups;
-    return g;
+    return workgroups(g, kTiles[cfg].persistent, a);
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH = 2>
+template <int BM, int BN, int WM, int WN, int DEPTH = 2, bool PERSIST = true>
 static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
 {
     int tiles_m, tiles_n;
     const int cfg_threads = 64 * WM * WN;
     tiles_n = (a.n + BN - 1) / BN;
     tiles_m = mode == MODE_CONTIG ? a.m / BM : (a.m + BM - 1) / BM;
-    int64_t grid = (int64_t)tiles_m * tiles_n;
+    int64_t total = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
-        grid *= a.num_groups;
-    if (grid <= 0 || grid > 0x7fffffff)
+        total *= a.num_groups;
+    if (total <= 0 || total > 0x7fffffff)
         return hipErrorInvalidConfiguration;
+    const int64_t grid = workgroups(total, PERSIST, a);
     dim3 g((unsigned)grid), b(cfg_threads);
     switch (mode) {
     case MODE_DENSE:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE>), g, b, 0, stream, a,
-                           tiles_m, tiles_n);
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE, PERSIST>), g, b, 0,
+                           stream, a, tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG>), g, b, 0, stream, a,
-                           tiles_m, tiles_n);
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST>), g, b, 0,
+                           stream, a, tiles_m, tiles_n);
         break;
     default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED>), g, b, 0, stream, a,
-                           tiles_m, tiles_n);
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST>), g, b, 0,
+                           stream, a, tiles_m, tiles_n);
         break;
     }
     return hipGetLastError();
@@ -727,7 +1002,7 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
 {
     switch (cfg) {
     case CFG_256x224:
-        return launch_cfg<256, 224, 4, 2>(mode, a, stream);
+        return launch_cfg<256, 224, 4, 2, 2, false>(mode, a, stream);
     case CFG_128x256:
         return launch_cfg<128, 256, 2, 2>(mode, a, stream);
     case CFG_128x128:
@@ -735,11 +1010,13 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
     case CFG_64x32:
         return launch_cfg<64, 32, 2, 2>(mode, a, stream);
     case CFG_256x128:
-        return launch_cfg<256, 128, 4, 2>(mode, a, stream);
+        return launch_cfg<256, 128, 4, 2, 2, false>(mode, a, stream);
+    case CFG_256x128p:
+        return launch_cfg<256, 128, 4, 2, 2, true>(mode, a, stream);
     case CFG_128x128d4:
-        return launch_cfg<128, 128, 2, 2, 4>(mode, a, stream);
+        return launch_cfg<128, 128, 2, 2, 4, true>(mode, a, stream);
     case CFG_128x128w8d4:
-        return launch_cfg<128, 128, 2, 4, 4>(mode, a, stream);
+        return launch_cfg<128, 128, 2, 4, 4, true>(mode, a, stream);
     case CFG_128x256w8:
         return launch_cfg<128, 256, 2, 4>(mode, a, stream);
     case CFG_STREAM64:

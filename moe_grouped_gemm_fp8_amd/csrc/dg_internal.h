@@ -22,12 +22,14 @@ enum TileCfg : int {
     CFG_128x128d4 = 6,   // 4 waves (2x2), wave tile 64x64, copies four K blocks ahead
     CFG_128x128w8d4 = 7, // 8 waves (2x4), wave tile 64x32, copies four K blocks ahead
     CFG_128x256w8 = 8,   // 8 waves (2x4), wave tile 64x64: contiguous MoE, two waves per SIMD
+    CFG_256x128p = 9,    // CFG_256x128 with workgroups looping over tiles
     CFG_COUNT
 };
 
 struct TileInfo {
     int bm, bn, threads;
     const char *name;
+    bool persistent;  // workgroups loop over tiles (at most one per CU), else one per tile
 };
 extern const TileInfo kTiles[CFG_COUNT];
 
@@ -45,6 +47,8 @@ struct GemmArgs {
     int num_groups;
     int splits;           // split-K factor of the streaming kernel (1 = none)
     float *ws;            // split-K partial tiles (streaming kernel, splits > 1)
+    int max_wgs;          // persistent tiles: workgroups to launch at most (the CU count);
+                          // <= 0 launches one workgroup per tile
 };
 
 // Grid size in workgroups for a launch (host-side, no HIP call).

@@ -18,7 +18,7 @@ from tolerance import bf16_bits_to_f64
 
 pytestmark = pytest.mark.gpu
 
-TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "stream64",
+TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "256x128w8p", "stream64",
                 "128x128w4d4", "128x128w8d4", "128x256w8"]
 DEEP_CONFIGS = ["128x128w4d4", "128x128w8d4"]
 
@@ -109,6 +109,31 @@ def test_dense_bf16_rounding_of_special_values(cfg, k, splits, monkeypatch):
                            f"{[hex(x) for x in cbits[~nan][bad][:4]]}: got "
                            f"{[hex(x) for x in got[~nan][bad][:4]]} want "
                            f"{[hex(x) for x in want[~nan][bad][:4]]}")
+
+
+PERSISTENT_CONFIGS = ["128x256w8", "128x128w4", "64x32w4", "256x128w8p", "128x128w8d4"]
+
+
+@pytest.mark.parametrize("cfg", PERSISTENT_CONFIGS)
+@pytest.mark.parametrize("wgs", ["3", "10"])
+@pytest.mark.parametrize("k", [256, 1280])
+def test_persistent_workgroups_loop_over_tiles(cfg, wgs, k, monkeypatch):
+    # few workgroups for many tiles: each walks a run of tiles, prefetching the next tile's
+    # first K blocks during the current one's last (k=1280), or restarting its pipeline per
+    # tile when K is too short for that (k=256); 3 workgroups leave 5 XCD slots without one
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    monkeypatch.setenv("DG_PERSIST_WGS", wgs)
+    p = W.make_dense(456, 784, k, seed=51, with_c=True)
+    assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c),
+                  f"dense {cfg} wgs={wgs} k={k}")
+    # (a forced tile taller than 128 rows falls back to the library's contiguous choice)
+    q = W.make_contiguous(5, 970, 400, k, seed=52, counts=[0, 300, 41, 500, 129], pad_nan=True)
+    ref = oracle.m_grouped_contiguous(q.a, q.sfa, q.b, q.sfb, q.m_indices)
+    assert_parity(run_contiguous(q), ref, f"contiguous {cfg} wgs={wgs} k={k}")
+    r = W.make_masked(6, 256, 400, k, seed=53, masked_m=[0, 256, 7, 0, 129, 200],
+                      tail_nan=True)
+    ref = oracle.m_grouped_masked(r.a, r.sfa, r.b, r.sfb, r.masked_m)
+    assert_parity(run_masked(r), ref, f"masked {cfg} wgs={wgs} k={k}")
 
 
 def test_dense_stress_scales():
@@ -212,7 +237,7 @@ def test_contiguous_workload_sampled_rows():
 # ------------------------------------------------------------------------------ masked
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
-                                 "256x128w8"])
+                                 "256x128w8", "256x128w8p"])
 def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
