@@ -118,6 +118,12 @@ def _capture(torch, sets, call, per_graph=1):
     return singles, multi
 
 
+def _steps_per_graph(nsets):
+    """Steps per multi-step graph: the largest count up to GRAPH_STEPS that divides the
+    number of input copies, so step i always runs on copy i % nsets."""
+    return max(d for d in range(1, min(nsets, GRAPH_STEPS) + 1) if nsets % d == 0)
+
+
 def _graph_launcher(c, singles, multi, per_graph):
     """launch(i, n) runs steps i .. i+n-1: one single-step replay, or (n == per_graph) one
     replay of a multi-step graph."""
@@ -142,7 +148,7 @@ def make_dense_case(torch, dg, W, name):
     nbytes = (p.m * p.k + p.n * p.k + 4 * p.m * kb + 4 * nb * kb + 2 * p.m * p.n
               + (4 * p.m * p.n if p.c is not None else 0))
     c.sets = _copies(torch, t, nbytes)
-    per_graph = min(len(c.sets), GRAPH_STEPS)
+    per_graph = _steps_per_graph(len(c.sets))
 
     def call(s):
         dg.fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["c"])
@@ -169,7 +175,7 @@ def make_contiguous_case(torch, dg, W):
     nbytes = (valid * p.k + used * p.n * p.k + 4 * valid * kb + 4 * used * nb * kb
               + 2 * valid * p.n + 4 * p.m_total)
     c.sets = _copies(torch, t, nbytes)
-    per_graph = min(len(c.sets), GRAPH_STEPS)
+    per_graph = _steps_per_graph(len(c.sets))
 
     def call(s):
         dg.m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["idx"])
@@ -189,25 +195,22 @@ def make_masked_case(torch, dg, W):
     c = Case("moe_masked")
     g, m_max, n, k = p.num_groups, p.m_max, p.n, p.k
     t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
-             mm=_dev(torch, p.masked_m),
              d=torch.empty(g, m_max, n, dtype=torch.bfloat16, device="cuda"))
     kb, nb = k // 128, (n + 127) // 128
     set_bytes = g * m_max * k + g * n * k + 2 * g * m_max * n
     c.sets = _copies(torch, t, set_bytes)
-    table = [W.masked_counts(g, m_max, seed=0, replay=r) for r in range(16)]
-    table_dev = [_dev(torch, x) for x in table]
-    graphs, _ = _capture(torch, c.sets, lambda s: dg.m_grouped_fp8_gemm_nt_masked(
-        s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["mm"]))
+    # one masked_m draw per input copy, resident on the device before timing: every step of a
+    # replayed graph reads its own draw, so nothing is updated inside the timed region
+    table = [W.masked_counts(g, m_max, seed=0, replay=r) for r in range(len(c.sets))]
+    for s_, mm in zip(c.sets, table):
+        s_["mm"] = _dev(torch, mm)
+    per_graph = _steps_per_graph(len(c.sets))
+    _graph_launcher(c, *_capture(torch, c.sets, lambda s_: dg.m_grouped_fp8_gemm_nt_masked(
+        s_["a"], s_["sfa"], s_["b"], s_["sfb"], s_["d"], s_["mm"]), per_graph), per_graph)
     c.config = dict(workload="moe_masked", groups=g, m_max=m_max, n=n, k=k,
-                    masked_m="U{0..256} per group, a new draw per replay (16 draws)",
-                    launched_as="captured graph replay", rotating_copies=len(c.sets))
-
-    def prepare(i):
-        s = c.sets[i % len(c.sets)]
-        s["mm"].copy_(table_dev[i % len(table)])   # device-side update between replays
-
-    def launch(i, n=1):
-        graphs[i % len(graphs)].replay()
+                    masked_m=f"U{{0..256}} per group, a new draw per step ({len(table)} draws)",
+                    launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
 
     def flops(i):
         return 2.0 * float(table[i % len(table)].sum()) * n * k
@@ -218,8 +221,6 @@ def make_masked_case(torch, dg, W):
         used = float((mm > 0).sum())
         return (rows * k + used * n * k + 4 * rows * kb + 4 * used * nb * kb + 2 * rows * n + 4 * g)
 
-    c.prepare = prepare
-    c.launch = launch
     c.flops = flops
     c.bytes = nbytes
     return c
