@@ -88,7 +88,9 @@ __device__ __forceinline__ int wave_max(int v)
 // 8-byte global store issued as inline asm: the compiler then does not count it among the
 // wave's outstanding vector-memory operations, so its own waits for later register loads (the
 // streamed C) stay exact counts instead of draining everything in flight; every explicit wait
-// of the kernel counts it (it is older than the copies issued after it).
+// of the kernel counts it (it is older than the copies issued after it).  (Not
+// non-temporal: a row's 32-byte pieces from neighbouring stores merge into whole lines in the
+// L2 before they are written out.)
 __device__ __forceinline__ void store8_async(uint16_t *dst, uint32_t lo, uint32_t hi)
 {
     asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(dst), "v"(make_uint2(lo, hi))
@@ -109,13 +111,21 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // of the 128-column blocks the tile touches.  Block j + DEPTH is copied while block j is
     // multiplied.  Rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ h(r)
     // (header comment).
+    //
+    // With one more A slot where the LDS holds it (NA = DEPTH + 1), block j's refill goes to
+    // the slots of block j - 1 (A and B alike), which every wave is done with once it is past
+    // the end-of-block barrier of block j - 1: one barrier per block.  Otherwise (NA = DEPTH)
+    // the refill takes block j's own A slot, freed only once every wave holds block j's A
+    // fragments, which takes a second barrier at the block's start.
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
-    constexpr int B_BASE = DEPTH * A_SLOT;
+    constexpr bool ONE_BAR = (DEPTH + 1) * (A_SLOT + B_SLOT + 1024 + 256) <= 160 * 1024;
+    constexpr int NA = ONE_BAR ? DEPTH + 1 : DEPTH;  // A slots (and scale areas)
+    constexpr int B_BASE = NA * A_SLOT;
     constexpr int SA_BASE = B_BASE + (DEPTH + 1) * B_SLOT;
-    constexpr int SB_BASE = SA_BASE + DEPTH * 1024;
-    constexpr int LDS_BYTES = SB_BASE + DEPTH * 256;
+    constexpr int SB_BASE = SA_BASE + NA * 1024;
+    constexpr int LDS_BYTES = SB_BASE + NA * 256;
     static_assert(A_SLOT % 4096 == 0 && B_SLOT % 4096 == 0, "slots start on 4 KB boundaries");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
@@ -570,7 +580,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
 #pragma unroll
             for (int c = 0; c < MAXI; ++c)
                 issue_copy(c, in ? d : 0, as, bs, s);
-            as = as == DEPTH - 1 ? 0 : as + 1;
+            as = as == NA - 1 ? 0 : as + 1;
             bs = bs == DEPTH ? 0 : bs + 1;
         }
         wait_older_copies();
@@ -617,7 +627,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         auto block = [&](int j, const CopySrc &fs, int kb_fill) {
             const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
             const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
-            const int an = aslot == DEPTH - 1 ? 0 : aslot + 1;
+            const int an = aslot == NA - 1 ? 0 : aslot + 1;
+            // the refill's A slot (and scale areas): block j-1's with NA = DEPTH + 1, else
+            // block j's own
+            const int afill = ONE_BAR ? (aslot == 0 ? NA - 1 : aslot - 1) : aslot;
             // slot bases of this block's B reads and of the next block's A and B reads
             const uint32_t blo_c = b_lo + (uint32_t)(bslot * B_SLOT);
             const uint32_t bhi_c = b_hi + (uint32_t)(bslot * B_SLOT);
@@ -642,9 +655,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 for (int i = 0; i < SM; ++i)
                     scb[i] = Sf[i] * sb_cur[0];
             }
-            // every wave holds this block's A: its A slot may take block j+DEPTH, whose B
-            // slot (block j-1's) was released at the previous block's second barrier
-            bare_barrier();
+            // two-barrier form: every wave holds this block's A, so its A slot may take block
+            // j+DEPTH, whose B slot (block j-1's) was released at the previous block's end
+            if constexpr (!ONE_BAR)
+                bare_barrier();
             // this block's half-column of C: loaded now, added after the end-of-block wait
             // for the next block's copies, which it precedes (so that wait covers it); only
             // columns whose two halves both fall inside the loop are streamed
@@ -660,11 +674,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 if (j == 0 && has_next)
                     load_meta(nxt);
             }
-            issue_scales(kb_fill, aslot, fs);
+            issue_scales(kb_fill, afill, fs);
             if constexpr (SN == 1)
 #pragma unroll
                 for (int c = 0; c < MAXI; ++c)
-                    issue_copy(c, kb_fill, aslot, bslot_fill, fs);
+                    issue_copy(c, kb_fill, afill, bslot_fill, fs);
             // steps 0 .. SN-2, with this block's refill copies spread over them
             static_for<SN - 1>([&](auto JJ) {
                 constexpr int jj = decltype(JJ)::value;
@@ -680,7 +694,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                             const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
                             const int pos = c - first;
                             if (i == (SM == 1 ? 0 : (pos * 2) % SM))
-                                issue_copy(c, kb_fill, aslot, bslot_fill, fs);
+                                issue_copy(c, kb_fill, afill, bslot_fill, fs);
                         }
                     }
                 };
@@ -699,8 +713,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                               extra);
             });
             // last step: the next block's copies have landed everywhere (past the last block
-            // of the workgroup the reads below are harmless and unused)
+            // of the workgroup the reads below are harmless and unused); in the one-barrier
+            // form every wave has also finished reading this block's slots, which the next
+            // block's refill takes
             wait_older_copies();
+            if constexpr (ONE_BAR)
+                lds_wait();
             bare_barrier();
             lds_wait();
             if constexpr (SN >= 2) {
@@ -861,7 +879,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             // Through LDS, free once every copy has landed (one tile per workgroup): each wave
             // writes its sub-tiles there as bf16 (8 bytes per lane), then every thread stores
             // whole 16-byte pieces of rows, so a wave's store covers contiguous row segments
-            // instead of sixteen 32-byte pieces.  Output rows are OS bytes apart in LDS; OS = 32
+            // instead of sixteen 32-byte pieces.  D is written once and never read here: the
+            // stores are non-temporal, so they do not push A and B out of the L2.  Output rows are OS bytes apart in LDS; OS = 32
             // (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct banks.
             constexpr int NT = 64 * NW;
             constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
@@ -905,7 +924,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     if constexpr (MODE == MODE_CONTIG)
                         ok = ok && prow[t] == cur.g;
                     if (ok)
-                        *reinterpret_cast<v4i *>(D + (int64_t)row * N + col) = piece[t];
+                        __builtin_nontemporal_store(
+                            piece[t], reinterpret_cast<v4i *>(D + (int64_t)row * N + col));
                 }
             }
         }
