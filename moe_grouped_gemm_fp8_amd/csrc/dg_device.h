@@ -156,13 +156,6 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Workgroup id -> tile id such that XCD x (ids x, x+8, x+16, ...) gets one contiguous range.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk)
-{
-    int q = nblk >> 3, r = nblk & 7, xcd = bid & 7, loc = bid >> 3;
-    return (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
-}
-
 // Tile id -> (tm, tn) in groups of GROUP_M M-tiles, N fastest within a group column.
 __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm, int &tn)
 {

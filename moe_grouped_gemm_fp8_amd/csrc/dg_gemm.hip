@@ -31,9 +31,11 @@
 //    Every LDS slot starts on a 4 KB boundary.  Fragment reads are inline-asm
 //    ds_read_b128 with explicit lgkmcnt waits, so the compiler never pairs an LDS read with
 //    the in-flight copies and drains them.
-//  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
+//  * Workgroup ids are mapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
 //    runs a contiguous range of tiles, rastered in groups of 4 M-tiles, so tiles that run
-//    together on one XCD share A rows and B columns in that XCD's L2.
+//    together on one XCD share A rows and B columns in that XCD's L2.  Most tile shapes run
+//    persistent workgroups (one per CU) that walk their XCD's range; the next tile's first K
+//    blocks are copied while the current tile finishes, hiding the per-tile prologue.
 //  * Shapes too small to fill the CUs with these tiles go to the split-K streaming kernel
 //    (dg_stream.hip) instead.
 #include <hip/hip_runtime.h>
