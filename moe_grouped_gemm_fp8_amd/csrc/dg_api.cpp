@@ -223,7 +223,7 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     // and for shapes whose big tiles would leave most CUs idle.
     int cfg = forced_config();
     if (cfg < 0) {
-        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256, dg::CFG_128x128};
+        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
         double best = 0;
         int64_t best_tiles = 0;
         for (int cnd : cands) {
@@ -332,9 +332,19 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
     if ((rc = device_cus(&cus)) != DG_OK)
         return rc;
     (void)expected_m;
+    // 256-row tiles cover a group's m_max rows at once (the rows past masked_m skip their
+    // MFMAs and read zeros); of the two widths, the one with less column padding, the wider
+    // on a tie (each N-tile re-reads the group's A from L2, so fewer, wider tiles read less)
     int cfg = forced_config();
-    if (cfg < 0 || cfg == dg::CFG_STREAM64)
-        cfg = m_max > 128 ? dg::CFG_256x128 : dg::CFG_128x128;
+    if (cfg < 0 || cfg == dg::CFG_STREAM64) {
+        if (m_max > 128) {
+            const int64_t pad224 = (int64_t)((n + 223) / 224) * 224 - n;
+            const int64_t pad128 = (int64_t)((n + 127) / 128) * 128 - n;
+            cfg = pad224 <= pad128 ? dg::CFG_256x224 : dg::CFG_256x128;
+        } else {
+            cfg = dg::CFG_128x128;
+        }
+    }
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;
     args.sfa = sfa;

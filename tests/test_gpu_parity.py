@@ -237,7 +237,7 @@ def test_contiguous_workload_sampled_rows():
 # ------------------------------------------------------------------------------ masked
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
-                                 "256x128w8", "256x128w8p"])
+                                 "256x128w8", "256x128w8p", "256x224w8"])
 def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
