@@ -294,6 +294,7 @@ def summarize(res):
     gbs = float(res["bytes"].mean() / avg / 1e9)
     return dict(avg_kernel_us=avg * 1e6, timing=res["timing"],
                 per_launch_event_us=float(per.mean() * 1e6),
+                p50_us=float(np.percentile(per, 50) * 1e6),
                 p10_us=float(np.percentile(per, 10) * 1e6),
                 p90_us=float(np.percentile(per, 90) * 1e6), tflops=tflops, hbm_gbs=gbs,
                 frac_fp8_peak=tflops / PEAK_FP8_TFLOPS, frac_hbm_peak=gbs / PEAK_HBM_GBS)
@@ -390,7 +391,9 @@ def main():
     for name in order:
         log(f"preparing {name}")
         case = makers[name]()
-        steps = args.steps if name == args.workload else max(20, args.steps // 2)
+        # the short workloads take many steps (their spread matters); the long ones fewer
+        steps = args.steps if name == args.workload else (
+            200 if name in ("dense_small", "dense_skinny", "moe_masked") else max(20, args.steps // 2))
         log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
         res = time_case(torch, case, steps, args.warmup)
         summ = summarize(res)

@@ -123,3 +123,43 @@ def m_grouped_masked(a, sfa, b, sfb, masked_m) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle: unsupported masked shape")
     return d
+
+
+# ---------------------------------------------------------------------------------------------
+# UE8M0 scales: the packed power-of-two format of the method's newer hardware generation
+# (pt.news.hada.io, "Interface GEMM e restrições de layout": four UE8M0 values packed into one
+# 32-bit integer).  The reading taken: the four are consecutive K blocks of one row (or one
+# 128-row B block), least significant byte first, in the same layouts as the FP32 scales
+# with the K-block axis shortened to ceil(K/512); a byte e means 2^(e-127), and 0xFF is NaN.
+# The result is then the plain definition above with those scales.
+
+def ue8m0_decode(packed, axis: int, num_kblocks: int) -> np.ndarray:
+    """Packed UE8M0 int32 array -> float32 scales with ``num_kblocks`` entries along
+    ``axis``: entry 4q + j is byte j (least significant first) of packed entry q."""
+    p = np.moveaxis(np.asarray(packed), axis, -1).astype(np.int64) & 0xFFFFFFFF
+    kq = p.shape[-1]
+    shifts = 8 * np.arange(4, dtype=np.int64)
+    e = (p[..., :, None] >> shifts) & 0xFF                      # [..., kq, 4]
+    e = e.reshape(p.shape[:-1] + (kq * 4,))[..., :num_kblocks]
+    out = np.ldexp(np.float64(1.0), (e - 127).astype(np.int64))
+    out[e == 255] = np.nan
+    return np.moveaxis(out.astype(np.float32), -1, axis)       # every 2^e is exact in float32
+
+
+def fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c=None) -> np.ndarray:
+    """``fp8_gemm_nt`` with packed UE8M0 scales (``sfa`` int32 [ceil(K/512), ld],
+    ``sfb`` int32 [ceil(N/128), ceil(K/512)])."""
+    kb = np.asarray(a).shape[1] // 128
+    return fp8_gemm_nt(a, ue8m0_decode(sfa, 0, kb), b, ue8m0_decode(sfb, 1, kb), c)
+
+
+def m_grouped_contiguous_ue8m0(a, sfa, b, sfb, m_indices) -> np.ndarray:
+    kb = np.asarray(a).shape[1] // 128
+    return m_grouped_contiguous(a, ue8m0_decode(sfa, 0, kb), b, ue8m0_decode(sfb, 2, kb),
+                                m_indices)
+
+
+def m_grouped_masked_ue8m0(a, sfa, b, sfb, masked_m) -> np.ndarray:
+    kb = np.asarray(a).shape[2] // 128
+    return m_grouped_masked(a, ue8m0_decode(sfa, 1, kb), b, ue8m0_decode(sfb, 2, kb),
+                            masked_m)

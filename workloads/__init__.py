@@ -51,10 +51,20 @@ def _cast(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return to_e4m3_bits(y)
 
 
-def quantize_rows(x: np.ndarray, seg_mult: Optional[np.ndarray] = None):
+def _scale_of(amax: np.ndarray, pow2: bool) -> np.ndarray:
+    """Scale for a block with absolute maximum ``amax``: amax/448, or (``pow2``, for UE8M0
+    scales) the next power of two at or above it, so the cast never saturates."""
+    s = np.maximum(amax, AMAX_FLOOR) / E4M3_MAX
+    if pow2:
+        s = np.exp2(np.ceil(np.log2(s)))
+    return s.astype(np.float32)
+
+
+def quantize_rows(x: np.ndarray, seg_mult: Optional[np.ndarray] = None, pow2: bool = False):
     """1x128 row-segment cast. x: float32 [M, K] -> (bits uint8 [M, K], scales float32 [M, K/128]).
 
-    ``seg_mult`` (float32 [M, K/128]) multiplies each segment before the cast (stress inputs).
+    ``seg_mult`` (float32 [M, K/128]) multiplies each segment before the cast (stress inputs);
+    ``pow2`` rounds every scale up to a power of two (UE8M0-representable).
     """
     m, k = x.shape
     assert k % BLOCK == 0
@@ -63,12 +73,12 @@ def quantize_rows(x: np.ndarray, seg_mult: Optional[np.ndarray] = None):
     if seg_mult is not None:
         xs = xs * seg_mult[:, :, None].astype(np.float32)
     amax = np.abs(xs).max(axis=2)
-    scale = (np.maximum(amax, AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+    scale = _scale_of(amax, pow2)
     bits = _cast(xs, scale[:, :, None]).reshape(m, k)
     return bits, scale
 
 
-def quantize_blocks(x: np.ndarray, blk_mult: Optional[np.ndarray] = None):
+def quantize_blocks(x: np.ndarray, blk_mult: Optional[np.ndarray] = None, pow2: bool = False):
     """128x128 block cast. x: float32 [N, K] -> (bits uint8 [N, K], scales float32 [ceil(N/128), K/128]).
 
     The last block row may be partial (N % 128 != 0): its amax is over the rows that exist.
@@ -84,7 +94,7 @@ def quantize_blocks(x: np.ndarray, blk_mult: Optional[np.ndarray] = None):
         if blk_mult is not None:
             rows = rows * blk_mult[i][None, :, None].astype(np.float32)
         amax = np.abs(rows).max(axis=(0, 2))
-        s = (np.maximum(amax, AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+        s = _scale_of(amax, pow2)
         scale[i] = s
         bits[i * BLOCK:(i + 1) * BLOCK] = _cast(rows, s[None, :, None]).reshape(-1, k)
     return bits, scale
@@ -97,6 +107,25 @@ def mn_major(scales_mk: np.ndarray, ld: Optional[int] = None) -> np.ndarray:
     out = np.zeros((kb, ld), dtype=np.float32)
     out[:, :m] = scales_mk.T
     return out
+
+
+def pack_ue8m0(scales: np.ndarray, axis: int) -> np.ndarray:
+    """Power-of-two FP32 scales -> packed UE8M0: along ``axis`` (the K-block axis), K blocks
+    4q .. 4q+3 become the bytes 0..3 (least significant first) of int32 number q; a byte is
+    the biased exponent e with scale 2^(e-127), NaN scales become 0xFF, and the bytes past the
+    last K block hold 127 (scale 1).  Zero scales (padding columns of MN-major arrays) also
+    become 127."""
+    s = np.moveaxis(np.asarray(scales, dtype=np.float32), axis, -1)
+    kb = s.shape[-1]
+    kq = (kb + 3) // 4
+    e = np.full(s.shape[:-1] + (kq * 4,), 127, dtype=np.uint8)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m, ex = np.frexp(s.astype(np.float64))
+    ok = np.isfinite(s) & (s > 0)
+    assert np.all(m[ok] == 0.5), "UE8M0 scales must be powers of two"
+    e[..., :kb] = np.where(np.isnan(s), 255, np.where(ok, ex - 1 + 127, 127)).astype(np.uint8)
+    packed = e.reshape(s.shape[:-1] + (kq, 4)).copy().view("<u4")[..., 0].astype(np.uint32)
+    return np.moveaxis(packed.view(np.int32), -1, axis).copy()
 
 
 def _pow2_mult(rng: np.random.Generator, shape) -> np.ndarray:
@@ -116,8 +145,12 @@ class Dense:
 
 
 def make_dense(m: int, n: int, k: int, seed: int = 0, with_c: bool = False,
-               c_std: float = 0.1, stress: bool = False) -> Dense:
-    """Dense problem; draw order A, B, C, then (stress) segment and block multipliers."""
+               c_std: float = 0.1, stress: bool = False, ue8m0: bool = False) -> Dense:
+    """Dense problem; draw order A, B, C, then (stress) segment and block multipliers.
+
+    ``ue8m0``: power-of-two scales, returned packed (``pack_ue8m0``): ``sfa`` int32
+    [ceil(K/512), ld] and ``sfb`` int32 [ceil(N/128), ceil(K/512)].
+    """
     rng = np.random.default_rng(seed)
     xa = rng.standard_normal((m, k), dtype=np.float32)
     xb = rng.standard_normal((n, k), dtype=np.float32)
@@ -126,9 +159,12 @@ def make_dense(m: int, n: int, k: int, seed: int = 0, with_c: bool = False,
     if stress:
         seg = _pow2_mult(rng, (m, k // BLOCK))
         blk = _pow2_mult(rng, ((n + BLOCK - 1) // BLOCK, k // BLOCK))
-    a, sa = quantize_rows(xa, seg)
-    b, sb = quantize_blocks(xb, blk)
-    return Dense(a=a, sfa=mn_major(sa), b=b, sfb=sb, c=c, m=m, n=n, k=k)
+    a, sa = quantize_rows(xa, seg, pow2=ue8m0)
+    b, sb = quantize_blocks(xb, blk, pow2=ue8m0)
+    sfa = mn_major(sa)
+    if ue8m0:
+        sfa, sb = pack_ue8m0(sfa, 0), pack_ue8m0(sb, 1)
+    return Dense(a=a, sfa=sfa, b=b, sfb=sb, c=c, m=m, n=n, k=k)
 
 
 @dataclasses.dataclass
@@ -146,7 +182,8 @@ class Contiguous:
 
 
 def make_contiguous(num_groups: int, total_rows: int, n: int, k: int, seed: int = 0,
-                    counts=None, stress: bool = False, pad_nan: bool = False) -> Contiguous:
+                    counts=None, stress: bool = False, pad_nan: bool = False,
+                    ue8m0: bool = False) -> Contiguous:
     """Contiguous M-grouped layout.
 
     Draw order: the ``total_rows`` valid token rows of A, then B for every group, then the
@@ -170,7 +207,7 @@ def make_contiguous(num_groups: int, total_rows: int, n: int, k: int, seed: int 
         # a distinct power-of-two magnitude per group, so a misrouted row is a >= 2x error
         gmag = np.exp2(np.arange(num_groups) % 5 - 2).astype(np.float32)
         blk = _pow2_mult(rng, (num_groups, nb, k // BLOCK)) * gmag[:, None, None]
-    qa, sa = quantize_rows(xa, seg)
+    qa, sa = quantize_rows(xa, seg, pow2=ue8m0)
     padded = (counts + BLOCK - 1) // BLOCK * BLOCK
     m_total = int(padded.sum())
     a = np.full((m_total, k), E4M3_NAN if pad_nan else 0, dtype=np.uint8)
@@ -187,8 +224,11 @@ def make_contiguous(num_groups: int, total_rows: int, n: int, k: int, seed: int 
     b = np.empty((num_groups, n, k), dtype=np.uint8)
     sfb = np.empty((num_groups, nb, k // BLOCK), dtype=np.float32)
     for g in range(num_groups):
-        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g])
-    return Contiguous(a=a, sfa=mn_major(sa_full), b=b, sfb=sfb, m_indices=m_indices,
+        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g], pow2=ue8m0)
+    sfa = mn_major(sa_full)
+    if ue8m0:
+        sfa, sfb = pack_ue8m0(sfa, 0), pack_ue8m0(sfb, 2)
+    return Contiguous(a=a, sfa=sfa, b=b, sfb=sfb, m_indices=m_indices,
                       counts=counts, m_total=m_total, n=n, k=k, num_groups=num_groups)
 
 
@@ -212,7 +252,8 @@ def masked_counts(num_groups: int, m_max: int, seed: int, replay: Optional[int] 
 
 
 def make_masked(num_groups: int, m_max: int, n: int, k: int, seed: int = 0,
-                masked_m=None, stress: bool = False, tail_nan: bool = False) -> Masked:
+                masked_m=None, stress: bool = False, tail_nan: bool = False,
+                ue8m0: bool = False) -> Masked:
     """Masked M-grouped layout. Draw order: A [G, M_max, K], B [G, N, K], masked_m, (stress).
 
     Every row of A is drawn; rows at or beyond masked_m[g] are ignored by the method and are
@@ -236,13 +277,15 @@ def make_masked(num_groups: int, m_max: int, n: int, k: int, seed: int = 0,
     b = np.empty((num_groups, n, k), dtype=np.uint8)
     sfb = np.empty((num_groups, nb, k // BLOCK), dtype=np.float32)
     for g in range(num_groups):
-        a[g], sa = quantize_rows(xa[g], None if seg is None else seg[g])
+        a[g], sa = quantize_rows(xa[g], None if seg is None else seg[g], pow2=ue8m0)
         sfa[g] = mn_major(sa, ld)
-        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g])
+        b[g], sfb[g] = quantize_blocks(xb[g], None if blk is None else blk[g], pow2=ue8m0)
         if tail_nan:
             lim = min(max(int(mm[g]), 0), m_max)
             a[g, lim:] = E4M3_NAN
             sfa[g, :, lim:m_max] = np.nan
+    if ue8m0:
+        sfa, sfb = pack_ue8m0(sfa, 1), pack_ue8m0(sfb, 2)
     return Masked(a=a, sfa=sfa, b=b, sfb=sfb, masked_m=mm, num_groups=num_groups,
                   m_max=m_max, n=n, k=k)
 
@@ -260,6 +303,7 @@ CONFIGS = {
 
 
 def make_config(name: str, seed: int = 0, **overrides):
+    """One of CONFIGS; ``ue8m0=True`` gives the same shapes with packed UE8M0 scales."""
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
     kind = cfg.pop("kind")
