@@ -138,23 +138,32 @@ def _graph_launcher(c, singles, multi, per_graph):
     c.launch = launch
 
 
-def make_dense_case(torch, dg, W, name):
-    p = W.make_config(name, seed=0)
-    c = Case(name)
+def _scale_words(k, ue8m0):
+    """4-byte scale words per row (or B block) along K: one per K block, or (UE8M0) one per
+    four K blocks."""
+    kb = k // 128
+    return (kb + 3) // 4 if ue8m0 else kb
+
+
+def make_dense_case(torch, dg, W, name, ue8m0=False):
+    p = W.make_config(name, seed=0, ue8m0=ue8m0)
+    c = Case(name + ("_ue8m0" if ue8m0 else ""))
     t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
              c=None if p.c is None else _dev(torch, p.c),
              d=torch.empty(p.m, p.n, dtype=torch.bfloat16, device="cuda"))
-    kb, nb = p.k // 128, (p.n + 127) // 128
+    kb, nb = _scale_words(p.k, ue8m0), (p.n + 127) // 128
     nbytes = (p.m * p.k + p.n * p.k + 4 * p.m * kb + 4 * nb * kb + 2 * p.m * p.n
               + (4 * p.m * p.n if p.c is not None else 0))
+    fn = dg.fp8_gemm_nt_ue8m0 if ue8m0 else dg.fp8_gemm_nt
     c.sets = _copies(torch, t, nbytes)
     per_graph = _steps_per_graph(len(c.sets))
 
     def call(s):
-        dg.fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["c"])
+        fn(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["c"])
 
     _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
-    c.config = dict(workload=name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
+    c.config = dict(workload=c.name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
+                    scales="ue8m0" if ue8m0 else "fp32",
                     d="bf16", launched_as=f"captured graph replay, {c.cycle} steps per graph",
                     rotating_copies=len(c.sets))
     c.flops = lambda i: 2.0 * p.m * p.n * p.k
@@ -163,13 +172,13 @@ def make_dense_case(torch, dg, W, name):
     return c
 
 
-def make_contiguous_case(torch, dg, W):
-    p = W.make_config("moe_contiguous", seed=0)
-    c = Case("moe_contiguous")
+def make_contiguous_case(torch, dg, W, ue8m0=False):
+    p = W.make_config("moe_contiguous", seed=0, ue8m0=ue8m0)
+    c = Case("moe_contiguous" + ("_ue8m0" if ue8m0 else ""))
     t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
              idx=_dev(torch, p.m_indices),
              d=torch.empty(p.m_total, p.n, dtype=torch.bfloat16, device="cuda"))
-    kb, nb = p.k // 128, (p.n + 127) // 128
+    kb, nb = _scale_words(p.k, ue8m0), (p.n + 127) // 128
     valid = int(p.counts.sum())
     used = int((p.counts > 0).sum())
     nbytes = (valid * p.k + used * p.n * p.k + 4 * valid * kb + 4 * used * nb * kb
@@ -177,11 +186,14 @@ def make_contiguous_case(torch, dg, W):
     c.sets = _copies(torch, t, nbytes)
     per_graph = _steps_per_graph(len(c.sets))
 
+    fn = dg.m_grouped_fp8_gemm_nt_contiguous_ue8m0 if ue8m0 else dg.m_grouped_fp8_gemm_nt_contiguous
+
     def call(s):
-        dg.m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["idx"])
+        fn(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], s["idx"])
 
     _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
-    c.config = dict(workload="moe_contiguous", groups=p.num_groups, valid_rows=valid,
+    c.config = dict(workload=c.name, groups=p.num_groups, valid_rows=valid,
+                    scales="ue8m0" if ue8m0 else "fp32",
                     padded_rows=p.m_total, n=p.n, k=p.k,
                     launched_as=f"captured graph replay, {c.cycle} steps per graph",
                     rotating_copies=len(c.sets))
@@ -190,13 +202,13 @@ def make_contiguous_case(torch, dg, W):
     return c
 
 
-def make_masked_case(torch, dg, W):
-    p = W.make_config("moe_masked", seed=0)
-    c = Case("moe_masked")
+def make_masked_case(torch, dg, W, ue8m0=False):
+    p = W.make_config("moe_masked", seed=0, ue8m0=ue8m0)
+    c = Case("moe_masked" + ("_ue8m0" if ue8m0 else ""))
     g, m_max, n, k = p.num_groups, p.m_max, p.n, p.k
     t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
              d=torch.empty(g, m_max, n, dtype=torch.bfloat16, device="cuda"))
-    kb, nb = k // 128, (n + 127) // 128
+    kb, nb = _scale_words(k, ue8m0), (n + 127) // 128
     set_bytes = g * m_max * k + g * n * k + 2 * g * m_max * n
     c.sets = _copies(torch, t, set_bytes)
     # one masked_m draw per input copy, resident on the device before timing: every step of a
@@ -205,9 +217,11 @@ def make_masked_case(torch, dg, W):
     for s_, mm in zip(c.sets, table):
         s_["mm"] = _dev(torch, mm)
     per_graph = _steps_per_graph(len(c.sets))
-    _graph_launcher(c, *_capture(torch, c.sets, lambda s_: dg.m_grouped_fp8_gemm_nt_masked(
+    fn = dg.m_grouped_fp8_gemm_nt_masked_ue8m0 if ue8m0 else dg.m_grouped_fp8_gemm_nt_masked
+    _graph_launcher(c, *_capture(torch, c.sets, lambda s_: fn(
         s_["a"], s_["sfa"], s_["b"], s_["sfb"], s_["d"], s_["mm"]), per_graph), per_graph)
-    c.config = dict(workload="moe_masked", groups=g, m_max=m_max, n=n, k=k,
+    c.config = dict(workload=c.name, groups=g, m_max=m_max, n=n, k=k,
+                    scales="ue8m0" if ue8m0 else "fp32",
                     masked_m=f"U{{0..256}} per group, a new draw per step ({len(table)} draws)",
                     launched_as=f"captured graph replay, {c.cycle} steps per graph",
                     rotating_copies=len(c.sets))
@@ -305,11 +319,15 @@ def cpu_baseline(W, case, target_s):
     grown until one call takes a good part of `target_s`, then repeated to about `target_s`."""
     import oracle
     p = case.problem
+    sfa, sfb = p.sfa, p.sfb
+    if sfa.dtype == np.int32:                         # packed UE8M0: the oracle decodes them
+        sfa = oracle.ue8m0_decode(sfa, 0, p.k // 128)
+        sfb = oracle.ue8m0_decode(sfb, 1, p.k // 128)
     log("timing the CPU oracle on a row sample of the workload")
     rows = 2
     while True:
         t0 = time.perf_counter()
-        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(p.sfa[:, :rows].T), p.b, p.sfb,
+        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(sfa[:, :rows].T), p.b, sfb,
                            None if p.c is None else p.c[:rows])
         dt = time.perf_counter() - t0
         if dt >= target_s / 4 or rows >= p.m:
@@ -318,7 +336,7 @@ def cpu_baseline(W, case, target_s):
     reps, total = 1, dt
     while total < target_s:
         t0 = time.perf_counter()
-        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(p.sfa[:, :rows].T), p.b, p.sfb,
+        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(sfa[:, :rows].T), p.b, sfb,
                            None if p.c is None else p.c[:rows])
         total += time.perf_counter() - t0
         reps += 1
@@ -354,7 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dense_prefill",
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
-                             "moe_masked"])
+                             "moe_masked", "dense_prefill_ue8m0", "moe_contiguous_ue8m0",
+                             "moe_masked_ue8m0"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -384,6 +403,9 @@ def main():
         "dense_skinny": lambda: make_dense_case(torch, dg, W, "dense_skinny"),
         "moe_contiguous": lambda: make_contiguous_case(torch, dg, W),
         "moe_masked": lambda: make_masked_case(torch, dg, W),
+        "dense_prefill_ue8m0": lambda: make_dense_case(torch, dg, W, "dense_prefill", True),
+        "moe_contiguous_ue8m0": lambda: make_contiguous_case(torch, dg, W, True),
+        "moe_masked_ue8m0": lambda: make_masked_case(torch, dg, W, True),
     }
     order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
     results = {}
@@ -393,7 +415,8 @@ def main():
         case = makers[name]()
         # the short workloads take many steps (their spread matters); the long ones fewer
         steps = args.steps if name == args.workload else (
-            200 if name in ("dense_small", "dense_skinny", "moe_masked") else max(20, args.steps // 2))
+            200 if name in ("dense_small", "dense_skinny", "moe_masked", "moe_masked_ue8m0")
+            else max(20, args.steps // 2))
         log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
         res = time_case(torch, case, steps, args.warmup)
         summ = summarize(res)
@@ -418,7 +441,7 @@ def main():
                     frac=achieved / PEAK_FP8_TFLOPS, traffic=traffic,
                     kernel_avg_us=summ["avg_kernel_us"], hbm_gbs_algorithmic=summ["hbm_gbs"],
                     hbm_frac_algorithmic=summ["hbm_gbs"] / PEAK_HBM_GBS)
-    if dom in ("dense_skinny", "moe_masked"):
+    if dom in ("dense_skinny", "moe_masked", "moe_masked_ue8m0"):
         roofline.update(bound="hbm", achieved=summ["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=summ["hbm_gbs"] / PEAK_HBM_GBS)
     out = {

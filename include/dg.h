@@ -104,6 +104,33 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
                                     const int32_t *masked_m, int num_groups, int m_max, int n,
                                     int k, int expected_m, void *stream);
 
+/*
+ * The three calls above with packed UE8M0 scales instead of FP32 ones (pt.news.hada.io,
+ * "Interface GEMM e restrições de layout": the newer hardware generation takes the scaling
+ * factors as UE8M0, four packed into one 32-bit integer).  Same granularity (1x128 A
+ * segments, 128x128 B blocks) and layouts, with the K-block axis packed: word q of a row
+ * holds the scales of K blocks 4q .. 4q+3 in its bytes 0..3 (least significant first), and a
+ * byte e means 2^(e-127) (0xFF: NaN).  So
+ *   sfa  int32 [ceil(k/512)][ld_sfa]                      (dense, contiguous)
+ *        int32 [num_groups][ceil(k/512)][ld_sfa]          (masked)
+ *   sfb  int32 [ceil(n/128)][ceil(k/512)]                 (dense)
+ *        int32 [num_groups][ceil(n/128)][ceil(k/512)]     (grouped)
+ * Every other argument, precondition and behaviour is that of the FP32 call; the MFMA applies
+ * the exponents itself.  Dense shapes too small for the pipelined tiles run on them anyway
+ * (the streaming split-K path takes FP32 scales only).
+ */
+int dg_fp8_gemm_nt_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa, const void *b,
+                         const int32_t *sfb, const float *c, void *d, int m, int n, int k,
+                         void *stream);
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa,
+                                              const void *b, const int32_t *sfb, void *d,
+                                              const int32_t *m_indices, int m_total, int n,
+                                              int k, int num_groups, void *stream);
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa,
+                                          const void *b, const int32_t *sfb, void *d,
+                                          const int32_t *masked_m, int num_groups, int m_max,
+                                          int n, int k, int expected_m, void *stream);
+
 /* Row alignment of each group segment in the contiguous layout: 128 (the M block size). */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

@@ -20,6 +20,8 @@ import torch
 
 __all__ = [
     "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+    "m_grouped_fp8_gemm_nt_masked_ue8m0",
     "get_mk_alignment_for_contiguous_layout", "get_sf_aligned_m", "set_num_cus", "get_num_cus",
     "library_path",
 ]
@@ -58,6 +60,11 @@ def _load():
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_masked.restype = i32
+    for name in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous",
+                 "dg_m_grouped_fp8_gemm_nt_masked"):
+        fn = getattr(lib, name + "_ue8m0")
+        fn.argtypes = getattr(lib, name).argtypes
+        fn.restype = i32
     lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
     lib.dg_get_sf_aligned_m.argtypes = [i64]
     lib.dg_get_sf_aligned_m.restype = i64
@@ -97,69 +104,119 @@ def _dev(t: torch.Tensor, name: str, dtypes, ndim: int):
     return t.data_ptr()
 
 
-def fp8_gemm_nt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
-    """D = C + A @ B.T.  a [M,K] e4m3, sfa [K/128, ld>=M] f32, b [N,K] e4m3,
-    sfb [ceil(N/128), K/128] f32, d [M,N] bf16 (written), c [M,N] f32 or None."""
+def _scale_spec(k: int, ue8m0: bool):
+    """dtype and K-axis length of the scale tensors: one FP32 per 128-wide K block, or one
+    int32 per four K blocks holding their UE8M0 exponents (least significant byte first)."""
+    kb = k // 128
+    return (torch.int32, (kb + 3) // 4, "ceil(K/512)") if ue8m0 else (torch.float32, kb, "K/128")
+
+
+def _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, ue8m0):
     pa = _dev(a, "a", _FP8_DTYPES, 2)
     m, k = a.shape
     pb = _dev(b, "b", _FP8_DTYPES, 2)
     n = b.shape[0]
     _need(b.shape[1] == k, "a and b disagree on K")
-    psfa = _dev(sfa, "sfa", torch.float32, 2)
-    _need(sfa.shape[0] * 128 == k, "sfa must be [K/128, ld]")
-    psfb = _dev(sfb, "sfb", torch.float32, 2)
-    _need(tuple(sfb.shape) == ((n + 127) // 128, k // 128), "sfb must be [ceil(N/128), K/128]")
+    _need(k % 128 == 0, "K must be a multiple of 128")
+    sdt, ks, kname = _scale_spec(k, ue8m0)
+    psfa = _dev(sfa, "sfa", sdt, 2)
+    _need(sfa.shape[0] == ks, f"sfa must be [{kname}, ld]")
+    psfb = _dev(sfb, "sfb", sdt, 2)
+    _need(tuple(sfb.shape) == ((n + 127) // 128, ks), f"sfb must be [ceil(N/128), {kname}]")
     pd = _dev(d, "d", torch.bfloat16, 2)
     _need(tuple(d.shape) == (m, n), "d must be [M, N]")
     pc = None
     if c is not None:
         pc = _dev(c, "c", torch.float32, 2)
         _need(tuple(c.shape) == (m, n), "c must be [M, N]")
-    _check(_load().dg_fp8_gemm_nt(pa, psfa, sfa.shape[1], pb, psfb, pc, pd, m, n, k,
-                                  _stream(stream)))
+    lib = _load()
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if ue8m0 else lib.dg_fp8_gemm_nt
+    _check(fn(pa, psfa, sfa.shape[1], pb, psfb, pc, pd, m, n, k, _stream(stream)))
+    return d
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """D = C + A @ B.T.  a [M,K] e4m3, sfa [K/128, ld>=M] f32, b [N,K] e4m3,
+    sfb [ceil(N/128), K/128] f32, d [M,N] bf16 (written), c [M,N] f32 or None."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False)
+
+
+def fp8_gemm_nt_ue8m0(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """fp8_gemm_nt with packed UE8M0 scales: sfa int32 [ceil(K/512), ld>=M],
+    sfb int32 [ceil(N/128), ceil(K/512)]; byte j of word q is the exponent of K block 4q+j."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, True)
+
+
+def _contiguous(a, sfa, b, sfb, d, m_indices, stream, ue8m0):
+    pa = _dev(a, "a", _FP8_DTYPES, 2)
+    m_total, k = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 3)
+    g, n, kb_ = b.shape
+    _need(kb_ == k, "a and b disagree on K")
+    _need(k % 128 == 0, "K must be a multiple of 128")
+    sdt, ks, kname = _scale_spec(k, ue8m0)
+    psfa = _dev(sfa, "sfa", sdt, 2)
+    _need(sfa.shape[0] == ks, f"sfa must be [{kname}, ld]")
+    psfb = _dev(sfb, "sfb", sdt, 3)
+    _need(tuple(sfb.shape) == (g, (n + 127) // 128, ks), f"sfb must be [G, ceil(N/128), {kname}]")
+    pd = _dev(d, "d", torch.bfloat16, 2)
+    _need(tuple(d.shape) == (m_total, n), "d must be [M_total, N]")
+    pi = _dev(m_indices, "m_indices", torch.int32, 1)
+    _need(m_indices.shape[0] == m_total, "m_indices must be [M_total]")
+    lib = _load()
+    fn = (lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if ue8m0
+          else lib.dg_m_grouped_fp8_gemm_nt_contiguous)
+    _check(fn(pa, psfa, sfa.shape[1], pb, psfb, pd, pi, m_total, n, k, g, _stream(stream)))
     return d
 
 
 def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, stream=None):
     """Contiguous M-grouped GEMM.  a [M_total,K], sfa [K/128, ld>=M_total], b [G,N,K],
     sfb [G, ceil(N/128), K/128], d [M_total,N] bf16, m_indices int32 [M_total] (-1 = padding)."""
-    pa = _dev(a, "a", _FP8_DTYPES, 2)
-    m_total, k = a.shape
+    return _contiguous(a, sfa, b, sfb, d, m_indices, stream, False)
+
+
+def m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, d, m_indices, stream=None):
+    """m_grouped_fp8_gemm_nt_contiguous with packed UE8M0 scales: sfa int32
+    [ceil(K/512), ld>=M_total], sfb int32 [G, ceil(N/128), ceil(K/512)]."""
+    return _contiguous(a, sfa, b, sfb, d, m_indices, stream, True)
+
+
+def _masked(a, sfa, b, sfb, d, masked_m, expected_m, stream, ue8m0):
+    pa = _dev(a, "a", _FP8_DTYPES, 3)
+    g, m_max, k = a.shape
     pb = _dev(b, "b", _FP8_DTYPES, 3)
-    g, n, kb_ = b.shape
-    _need(kb_ == k, "a and b disagree on K")
-    psfa = _dev(sfa, "sfa", torch.float32, 2)
-    _need(sfa.shape[0] * 128 == k, "sfa must be [K/128, ld]")
-    psfb = _dev(sfb, "sfb", torch.float32, 3)
-    _need(tuple(sfb.shape) == (g, (n + 127) // 128, k // 128), "sfb must be [G, ceil(N/128), K/128]")
-    pd = _dev(d, "d", torch.bfloat16, 2)
-    _need(tuple(d.shape) == (m_total, n), "d must be [M_total, N]")
-    pi = _dev(m_indices, "m_indices", torch.int32, 1)
-    _need(m_indices.shape[0] == m_total, "m_indices must be [M_total]")
-    _check(_load().dg_m_grouped_fp8_gemm_nt_contiguous(pa, psfa, sfa.shape[1], pb, psfb, pd, pi,
-                                                       m_total, n, k, g, _stream(stream)))
+    _need(b.shape[0] == g and b.shape[2] == k, "a and b disagree on G or K")
+    _need(k % 128 == 0, "K must be a multiple of 128")
+    n = b.shape[1]
+    sdt, ks, kname = _scale_spec(k, ue8m0)
+    psfa = _dev(sfa, "sfa", sdt, 3)
+    _need(sfa.shape[0] == g and sfa.shape[1] == ks, f"sfa must be [G, {kname}, ld]")
+    psfb = _dev(sfb, "sfb", sdt, 3)
+    _need(tuple(sfb.shape) == (g, (n + 127) // 128, ks), f"sfb must be [G, ceil(N/128), {kname}]")
+    pd = _dev(d, "d", torch.bfloat16, 3)
+    _need(tuple(d.shape) == (g, m_max, n), "d must be [G, M_max, N]")
+    pm = _dev(masked_m, "masked_m", torch.int32, 1)
+    _need(masked_m.shape[0] == g, "masked_m must be [G]")
+    lib = _load()
+    fn = (lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if ue8m0
+          else lib.dg_m_grouped_fp8_gemm_nt_masked)
+    _check(fn(pa, psfa, sfa.shape[2], pb, psfb, pd, pm, g, m_max, n, k, int(expected_m),
+              _stream(stream)))
     return d
 
 
 def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
     """Masked M-grouped GEMM.  a [G,M_max,K], sfa [G, K/128, ld>=M_max], b [G,N,K],
     sfb [G, ceil(N/128), K/128], d [G,M_max,N] bf16, masked_m int32 [G] on the device."""
-    pa = _dev(a, "a", _FP8_DTYPES, 3)
-    g, m_max, k = a.shape
-    pb = _dev(b, "b", _FP8_DTYPES, 3)
-    _need(b.shape[0] == g and b.shape[2] == k, "a and b disagree on G or K")
-    n = b.shape[1]
-    psfa = _dev(sfa, "sfa", torch.float32, 3)
-    _need(sfa.shape[0] == g and sfa.shape[1] * 128 == k, "sfa must be [G, K/128, ld]")
-    psfb = _dev(sfb, "sfb", torch.float32, 3)
-    _need(tuple(sfb.shape) == (g, (n + 127) // 128, k // 128), "sfb must be [G, ceil(N/128), K/128]")
-    pd = _dev(d, "d", torch.bfloat16, 3)
-    _need(tuple(d.shape) == (g, m_max, n), "d must be [G, M_max, N]")
-    pm = _dev(masked_m, "masked_m", torch.int32, 1)
-    _need(masked_m.shape[0] == g, "masked_m must be [G]")
-    _check(_load().dg_m_grouped_fp8_gemm_nt_masked(pa, psfa, sfa.shape[2], pb, psfb, pd, pm, g,
-                                                   m_max, n, k, int(expected_m), _stream(stream)))
-    return d
+    return _masked(a, sfa, b, sfb, d, masked_m, expected_m, stream, False)
+
+
+def m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m: int = 0,
+                                       stream=None):
+    """m_grouped_fp8_gemm_nt_masked with packed UE8M0 scales: sfa int32
+    [G, ceil(K/512), ld>=M_max], sfb int32 [G, ceil(N/128), ceil(K/512)]."""
+    return _masked(a, sfa, b, sfb, d, masked_m, expected_m, stream, True)
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

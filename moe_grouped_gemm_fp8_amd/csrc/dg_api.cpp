@@ -182,12 +182,11 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
     return ok();
 }
 
-}  // namespace
 
-extern "C" {
 
-int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
-                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+// The three forms, for either scale format (UE8M0: the scale pointers hold int32 words).
+int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
 {
     int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m, n, k);
     if (rc != DG_OK)
@@ -218,15 +217,19 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     args.num_groups = 1;
     args.splits = 1;
     args.max_wgs = persistent_wgs(cus);
+    args.sf_fmt = sf_fmt;
 
     // Pipelined tiles for shapes that fill the CUs; the split-K streaming kernel for skinny M
     // and for shapes whose big tiles would leave most CUs idle.
     int cfg = forced_config();
     if (cfg < 0) {
-        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
+        // (UE8M0 scales have no streaming split-K tile: its small shapes take 64x32 tiles)
+        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128, dg::CFG_64x32};
+        const int ncands = sf_fmt == dg::SF_FP32 ? 3 : 4;
         double best = 0;
         int64_t best_tiles = 0;
-        for (int cnd : cands) {
+        for (int ci = 0; ci < ncands; ++ci) {
+            const int cnd = cands[ci];
             const dg::TileInfo &t = dg::kTiles[cnd];
             int64_t tiles = (int64_t)((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
             double cost = tile_cost(t.bm, t.bn, tiles, cus);
@@ -236,9 +239,12 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
                 best_tiles = tiles;
             }
         }
-        if (m <= 64 || 2 * best_tiles < cus)
+        // (the streaming kernel takes FP32 scales only)
+        if ((m <= 64 || 2 * best_tiles < cus) && sf_fmt == dg::SF_FP32)
             cfg = dg::CFG_STREAM64;
     }
+    if (cfg == dg::CFG_STREAM64 && sf_fmt != dg::SF_FP32)
+        return fail(DG_ERR_UNSUPPORTED, "the streaming split-K tile takes FP32 scales only");
     if (cfg == dg::CFG_STREAM64) {
         // one workgroup per (64x64 tile, split): enough splits to cover the CUs, never more
         // than stream_max_kblocks() K blocks in one split, every split non-empty
@@ -270,10 +276,9 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
     return launch(dg::MODE_DENSE, cfg, args, s);
 }
 
-int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,
-                                        const void *b, const float *sfb, void *d,
-                                        const int32_t *m_indices, int m_total, int n, int k,
-                                        int num_groups, void *stream)
+int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa,
+                       const void *b, const float *sfb, void *d, const int32_t *m_indices,
+                       int m_total, int n, int k, int num_groups, void *stream)
 {
     int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m_total, n, k);
     if (rc != DG_OK)
@@ -308,14 +313,14 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
     args.num_groups = num_groups;
     args.splits = 1;
     args.max_wgs = persistent_wgs(cus);
+    args.sf_fmt = sf_fmt;
     print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
 }
 
-int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_sfa,
-                                    const void *b, const float *sfb, void *d,
-                                    const int32_t *masked_m, int num_groups, int m_max, int n,
-                                    int k, int expected_m, void *stream)
+int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, void *d, const int32_t *masked_m, int num_groups, int m_max,
+                   int n, int k, int expected_m, void *stream)
 {
     int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m_max, n, k);
     if (rc != DG_OK)
@@ -359,8 +364,66 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
     args.num_groups = num_groups;
     args.splits = 1;
     args.max_wgs = persistent_wgs(cus);
+    args.sf_fmt = sf_fmt;
     print_config("m_grouped_masked", m_max, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_MASKED, cfg, args, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    return gemm_nt(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,
+                                        const void *b, const float *sfb, void *d,
+                                        const int32_t *m_indices, int m_total, int n, int k,
+                                        int num_groups, void *stream)
+{
+    return grouped_contiguous(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, d, m_indices, m_total, n, k,
+                              num_groups, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_sfa,
+                                    const void *b, const float *sfb, void *d,
+                                    const int32_t *masked_m, int num_groups, int m_max, int n,
+                                    int k, int expected_m, void *stream)
+{
+    return grouped_masked(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, d, masked_m, num_groups, m_max, n,
+                          k, expected_m, stream);
+}
+
+// UE8M0 scales: int32 words of four biased exponents, 4-byte elements like the FP32 scales
+int dg_fp8_gemm_nt_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa, const void *b,
+                         const int32_t *sfb, const float *c, void *d, int m, int n, int k,
+                         void *stream)
+{
+    return gemm_nt(dg::SF_UE8M0, a, reinterpret_cast<const float *>(sfa), ld_sfa, b,
+                   reinterpret_cast<const float *>(sfb), c, d, m, n, k, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa,
+                                              const void *b, const int32_t *sfb, void *d,
+                                              const int32_t *m_indices, int m_total, int n,
+                                              int k, int num_groups, void *stream)
+{
+    return grouped_contiguous(dg::SF_UE8M0, a, reinterpret_cast<const float *>(sfa), ld_sfa, b,
+                              reinterpret_cast<const float *>(sfb), d, m_indices, m_total, n, k,
+                              num_groups, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa,
+                                          const void *b, const int32_t *sfb, void *d,
+                                          const int32_t *masked_m, int num_groups, int m_max,
+                                          int n, int k, int expected_m, void *stream)
+{
+    return grouped_masked(dg::SF_UE8M0, a, reinterpret_cast<const float *>(sfa), ld_sfa, b,
+                          reinterpret_cast<const float *>(sfb), d, masked_m, num_groups, m_max,
+                          n, k, expected_m, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

@@ -99,9 +99,15 @@ __device__ __forceinline__ void store8_async(uint16_t *dst, uint32_t lo, uint32_
                  : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST>
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int SF>
 __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int tiles_n)
 {
+    // Scale format.  FP32 scales are applied on the vector unit: every MFMA result is one K
+    // block's partial, promoted into the FP32 accumulators with sa * sb.  Packed UE8M0 scales
+    // (powers of two, four K blocks per int32) are applied by the MFMA itself
+    // (v_mfma_scale_f32_16x16x128_f8f6f4 multiplies by 2^(ea-127) * 2^(eb-127)), which then
+    // accumulates straight into the accumulators: no partials, no promotion.
+    constexpr bool UE8 = SF == SF_UE8M0;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
@@ -148,7 +154,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // problem sizes; set again (through an opaque copy) at every tile, so that what the
     // compiler derives from them is recomputed per tile instead of being held in scalar
     // registers for the whole kernel
-    int M, K, N, KB, NB, nkb;
+    int M, K, N, KB, NB, nkb, KS;  // KS: scale columns per row (K blocks, or packed words)
     int64_t ld;
     auto set_dims = [&]() {
         M = p.m;
@@ -158,6 +164,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         KB = K / KBLK;
         NB = (N + KBLK - 1) / KBLK;
         nkb = KB;
+        KS = UE8 ? (KB + 3) / 4 : KB;
         ld = p.ld_sfa;
     };
     set_dims();
@@ -265,15 +272,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     auto copy_src = [&](const Tile &u) {
         const int64_t ga = MODE == MODE_MASKED ? (int64_t)u.g * M : 0;
         const uint8_t *A = p.a + ga * K;
-        const float *SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * KB * ld : 0);
+        const float *SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * KS * ld : 0);
         const uint8_t *B = p.b + (int64_t)u.g * N * K;
-        const float *SFB = p.sfb + (int64_t)u.g * NB * KB;
+        const float *SFB = p.sfb + (int64_t)u.g * NB * KS;
         const int nbf = u.n0 / KBLK;
         CopySrc s;
         s.a = make_rsrc(A + (int64_t)u.m0 * K, u.empty ? 0 : (int64_t)(u.row_limit - u.m0) * K);
         s.b = make_rsrc(B + (int64_t)u.n0 * K, u.empty ? 0 : (int64_t)(N - u.n0) * K);
-        s.sa = make_rsrc(SFA + u.m0, u.empty ? 0 : ((int64_t)KB * ld - u.m0) * 4);
-        s.sb = make_rsrc(SFB + (int64_t)nbf * KB, u.empty ? 0 : (int64_t)(NB - nbf) * KB * 4);
+        s.sa = make_rsrc(SFA + u.m0, u.empty ? 0 : ((int64_t)KS * ld - u.m0) * 4);
+        s.sb = make_rsrc(SFB + (int64_t)nbf * KS, u.empty ? 0 : (int64_t)(NB - nbf) * KS * 4);
         return s;
     };
 
@@ -318,13 +325,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             // last scale row read zeros
             uint32_t vo = lane_sfa;
             asm volatile("" : "+v"(vo));
-            vo += (uint32_t)((int64_t)kb * ld * 4);
+            const int ks = UE8 ? kb >> 2 : kb;  // the scale column holding block kb
+            vo += (uint32_t)((int64_t)ks * ld * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 s.sa, (DG_LDS void *)(ldsp + SA_BASE + aslot * 1024), 16, vo, 0, 0, 0);
             uint32_t vb = lane_sfb;
             asm volatile("" : "+v"(vb));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                s.sb, (DG_LDS void *)(ldsp + SB_BASE + aslot * 256), 4, vb, (uint32_t)kb * 4u, 0,
+                s.sb, (DG_LDS void *)(ldsp + SB_BASE + aslot * 256), 4, vb, (uint32_t)ks * 4u, 0,
                 0);
         }
     };
@@ -350,7 +358,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         for (int c = 0; c < MAXI; ++c)
             voff[c] = (lane_even ^ (uint32_t)((cq[c] & 1) << 4)) + (uint32_t)(8 * cq[c]) * (uint32_t)K;
         lane_sfa = (uint32_t)l * 16u;
-        lane_sfb = (uint32_t)l * (uint32_t)KB * 4u;
+        lane_sfb = (uint32_t)l * (uint32_t)KS * 4u;
         const int h = ((r >> 3) & 1) | (r & 2) | (((r >> 2) & 1) << 2);  // h(r)
         const uint32_t f_lo = (uint32_t)(r * KBLK + (((2 * gq) ^ h) << 4));
         const uint32_t f_hi = (uint32_t)(r * KBLK + (((2 * gq + 1) ^ h) << 4));
@@ -448,14 +456,29 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // block: scb[i] = sa[i] * sb, formed once per block instead of once per MFMA.
     constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0);
     float scb[SM];
-    auto take_sfb = [&](uint32_t hi_mask) {
+    // UE8M0: the block's exponents, for the MFMA's scale operands: eb[jj] for the B block of
+    // sub-tile column jj, ea[i] for this lane's row of sub-tile row i
+    int eb[SN], ea[SM];
+    auto take_sfb = [&](uint32_t hi_mask, int kb) {
         tie(vsb_lo);
         tie(vsb_hi);
-        const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_lo)));
-        const float hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_hi)));
+        if constexpr (UE8) {
+            const int sh = 8 * (kb & 3);  // byte of the packed word holding block kb
+            const int lo = (__builtin_amdgcn_readfirstlane(__float_as_int(vsb_lo)) >> sh) & 0xFF;
+            const int hi = (__builtin_amdgcn_readfirstlane(__float_as_int(vsb_hi)) >> sh) & 0xFF;
 #pragma unroll
-        for (int jj = 0; jj < SN; ++jj)
-            sb_cur[jj] = ((hi_mask >> jj) & 1) ? hi : lo;
+            for (int jj = 0; jj < SN; ++jj)
+                eb[jj] = ((hi_mask >> jj) & 1) ? hi : lo;
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                ea[i] = (__float_as_int(Sf[i]) >> sh) & 0xFF;
+        } else {
+            const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_lo)));
+            const float hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vsb_hi)));
+#pragma unroll
+            for (int jj = 0; jj < SN; ++jj)
+                sb_cur[jj] = ((hi_mask >> jj) & 1) ? hi : lo;
+        }
     };
 
     // fragment reads from slot bases (a_lo/a_hi/sa of an A slot, b_lo/b_hi of a B slot) with
@@ -511,18 +534,26 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const v8i bv = v8i{bf[0].x, bf[0].y, bf[0].z, bf[0].w, bf[1].x, bf[1].y, bf[1].z, bf[1].w};
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            if (MODE != MODE_MASKED || i < sm_act) {
-                {
-                    v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
-                    a += pend[i] * scale(i);
-                    // keep the promotion here: left free, the compiler hoists every MFMA of
-                    // the block above all promotions and holds SM*SN partials live at once
-                    asm volatile("" : "+v"(a));
-                }
+            // (UE8M0: every row sub-tile, since a skipped MFMA that carries its accumulator
+            // through a branch costs the 256x224 tile its registers)
+            if (MODE != MODE_MASKED || UE8 || i < sm_act) {
                 const v8i av = v8i{Af[i][0].x, Af[i][0].y, Af[i][0].z, Af[i][0].w,
                                    Af[i][1].x, Af[i][1].y, Af[i][1].z, Af[i][1].w};
-                pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if constexpr (UE8) {
+                    // first operand B (its block's exponent), second A (this lane's row's)
+                    acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bv, av, acc[i][jj], 0, 0, 0, eb[jj], 0, ea[i]);
+                } else {
+                    {
+                        v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
+                        a += pend[i] * scale(i);
+                        // keep the promotion here: left free, the compiler hoists every MFMA
+                        // of the block above all promotions and holds SM*SN partials live
+                        asm volatile("" : "+v"(a));
+                    }
+                    pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                }
             }
             extra(I);
             __builtin_amdgcn_sched_barrier(0);
@@ -651,8 +682,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 tie(Bf[1][0]);
                 tie(Bf[1][1]);
             }
-            take_sfb(sel.hi_mask);
-            if constexpr (ONE_NB) {
+            take_sfb(sel.hi_mask, j);
+            if constexpr (ONE_NB && !UE8) {
 #pragma unroll
                 for (int i = 0; i < SM; ++i)
                     scb[i] = Sf[i] * sb_cur[0];
@@ -830,10 +861,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             tie(Bf[1][1]);
         }
         // the tile's last partials
+        if constexpr (!UE8) {
 #pragma unroll
-        for (int i = 0; i < SM; ++i)
-            if (MODE != MODE_MASKED || i < sm_act)
-                acc[i][SN - 1] += pend[i] * psc[i];
+            for (int i = 0; i < SM; ++i)
+                if (MODE != MODE_MASKED || i < sm_act)
+                    acc[i][SN - 1] += pend[i] * psc[i];
+        }
 
         // ---- epilogue: + C (columns not streamed), round to bf16, store the valid rows from
         // registers (the LDS holds the next tile's first blocks)
@@ -947,11 +980,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     wait_vm<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST>
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int SF>
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
-    gemm_tiles<BM, BN, WM, WN, DEPTH, MODE, PERSIST>(p, tiles_m, tiles_n);
+    gemm_tiles<BM, BN, WM, WN, DEPTH, MODE, PERSIST, SF>(p, tiles_m, tiles_n);
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -989,6 +1022,26 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     return workgroups(g, kTiles[cfg].persistent, a);
 }
 
+template <int BM, int BN, int WM, int WN, int DEPTH, bool PERSIST, int SF>
+static void launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_m, int tiles_n,
+                         hipStream_t stream)
+{
+    switch (mode) {
+    case MODE_DENSE:
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE, PERSIST, SF>), g, b, 0,
+                           stream, a, tiles_m, tiles_n);
+        break;
+    case MODE_CONTIG:
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST, SF>), g, b,
+                           0, stream, a, tiles_m, tiles_n);
+        break;
+    default:
+        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST, SF>), g, b,
+                           0, stream, a, tiles_m, tiles_n);
+        break;
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int DEPTH = 2, bool PERSIST = true>
 static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
 {
@@ -1003,20 +1056,10 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     const int64_t grid = workgroups(total, PERSIST, a);
     dim3 g((unsigned)grid), b(cfg_threads);
-    switch (mode) {
-    case MODE_DENSE:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE, PERSIST>), g, b, 0,
-                           stream, a, tiles_m, tiles_n);
-        break;
-    case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST>), g, b, 0,
-                           stream, a, tiles_m, tiles_n);
-        break;
-    default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST>), g, b, 0,
-                           stream, a, tiles_m, tiles_n);
-        break;
-    }
+    if (a.sf_fmt == SF_UE8M0)
+        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0>(mode, g, b, a, tiles_m, tiles_n, stream);
+    else
+        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_FP32>(mode, g, b, a, tiles_m, tiles_n, stream);
     return hipGetLastError();
 }
 

@@ -8,6 +8,10 @@ namespace dg {
 
 enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 
+// Scale formats: FP32 (1x128 A segments, 128x128 B blocks), or the same granularity as packed
+// UE8M0 exponents (four K blocks per 32-bit word, least significant byte first).
+enum ScaleFmt : int { SF_FP32 = 0, SF_UE8M0 = 1 };
+
 // Tile configurations compiled ahead of time.  Each is (BM x BN) output rows x columns per
 // workgroup, split over WM x WN waves of 64 lanes; every wave owns a (BM/WM) x (BN/WN) block
 // built from 16x16 MFMA sub-tiles.  Copies run two K blocks ahead of the MFMAs unless the
@@ -49,6 +53,7 @@ struct GemmArgs {
     float *ws;            // split-K partial tiles (streaming kernel, splits > 1)
     int max_wgs;          // persistent tiles: workgroups to launch at most (the CU count);
                           // <= 0 launches one workgroup per tile
+    int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
 };
 
 // Grid size in workgroups for a launch (host-side, no HIP call).

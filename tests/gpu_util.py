@@ -27,18 +27,25 @@ def bits(d: torch.Tensor) -> np.ndarray:
     return d.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def _ue8m0(p) -> bool:
+    """Generator outputs carry packed UE8M0 scales as int32, FP32 scales as float32."""
+    return p.sfa.dtype == np.int32
+
+
 def run_dense(p: W.Dense, stream=None):
     d = sentinel_like((p.m, p.n))
-    dg.fp8_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d,
-                   None if p.c is None else dev(p.c), stream=stream)
+    fn = dg.fp8_gemm_nt_ue8m0 if _ue8m0(p) else dg.fp8_gemm_nt
+    fn(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d, None if p.c is None else dev(p.c),
+       stream=stream)
     torch.cuda.synchronize()
     return bits(d)
 
 
 def run_contiguous(p: W.Contiguous):
     d = sentinel_like((p.m_total, p.n))
-    dg.m_grouped_fp8_gemm_nt_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d,
-                                        dev(p.m_indices))
+    fn = (dg.m_grouped_fp8_gemm_nt_contiguous_ue8m0 if _ue8m0(p)
+          else dg.m_grouped_fp8_gemm_nt_contiguous)
+    fn(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d, dev(p.m_indices))
     torch.cuda.synchronize()
     return bits(d)
 
@@ -46,8 +53,8 @@ def run_contiguous(p: W.Contiguous):
 def run_masked(p: W.Masked, masked_m=None):
     d = sentinel_like((p.num_groups, p.m_max, p.n))
     mm = p.masked_m if masked_m is None else masked_m
-    dg.m_grouped_fp8_gemm_nt_masked(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d,
-                                    dev(np.asarray(mm, np.int32)))
+    fn = dg.m_grouped_fp8_gemm_nt_masked_ue8m0 if _ue8m0(p) else dg.m_grouped_fp8_gemm_nt_masked
+    fn(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d, dev(np.asarray(mm, np.int32)))
     torch.cuda.synchronize()
     return bits(d)
 
@@ -70,7 +77,18 @@ def assert_parity(d_bits: np.ndarray, ref: np.ndarray, what: str = ""):
                              f"{got[viol][:5].tolist()} want {ref[comp][viol][:5].tolist()}")
 
 
+def fp32_scales(p):
+    """(sfa, sfb) as FP32 arrays in the FP32 layouts: packed UE8M0 scales decoded by the
+    oracle, FP32 ones as they are."""
+    if not _ue8m0(p):
+        return p.sfa, p.sfb
+    kb = p.k // 128
+    ka = p.sfa.ndim - 2                                           # K axis: 0 flat, 1 per group
+    return oracle.ue8m0_decode(p.sfa, ka, kb), oracle.ue8m0_decode(p.sfb, p.sfb.ndim - 1, kb)
+
+
 def dense_rows_ref(p: W.Dense, rows):
     rows = np.asarray(rows)
-    sub = W.mn_major(p.sfa[:, rows].T)
-    return oracle.fp8_gemm_nt(p.a[rows], sub, p.b, p.sfb, None if p.c is None else p.c[rows])
+    sfa, sfb = fp32_scales(p)
+    sub = W.mn_major(sfa[:, rows].T)
+    return oracle.fp8_gemm_nt(p.a[rows], sub, p.b, sfb, None if p.c is None else p.c[rows])

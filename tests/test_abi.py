@@ -35,6 +35,7 @@ def test_header_declares_the_three_gemm_calls():
     for f in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous",
               "dg_m_grouped_fp8_gemm_nt_masked"):
         assert f in names
+        assert f + "_ue8m0" in names
 
 
 def test_library_exports_every_declared_function(lib):
@@ -81,6 +82,29 @@ def test_dense_rejects_bad_arguments_on_host(lib, kw, code):
     assert lib.dg_last_error().decode()
 
 
+def dense_ue8m0(lib, a=P, sfa=P, ld=128, b=P, sfb=P, c=None, d=P, m=128, n=256, k=512):
+    return lib.dg_fp8_gemm_nt_ue8m0(a, sfa, ld, b, sfb, c, d, m, n, k, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sfa=None), DG_ERR_INVALID_ARG),
+    (dict(k=500), DG_ERR_UNSUPPORTED),
+    (dict(ld=130), DG_ERR_MISALIGNED),
+    (dict(sfb=P + 2), DG_ERR_MISALIGNED),
+    (dict(c=P, d=P), DG_ERR_INVALID_ARG),
+])
+def test_ue8m0_calls_share_the_host_checks(lib, kw, code):
+    assert dense_ue8m0(lib, **kw) == code
+    args = dict(a=P, sfa=P, ld=256, b=P, sfb=P, d=P, idx=P, m=256, n=256, k=512, g=4)
+    args.update({k: v for k, v in kw.items() if k in args})
+    if "ld" in kw:
+        args["ld"] = kw["ld"] + 128      # same misalignment, at least M_total rows
+    if "c" not in kw:
+        assert lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
+            args["a"], args["sfa"], args["ld"], args["b"], args["sfb"], args["d"], args["idx"],
+            args["m"], args["n"], args["k"], args["g"], None) == code
+
+
 def contig(lib, a=P, sfa=P, ld=256, b=P, sfb=P, d=P, idx=P, m=256, n=256, k=512, g=4):
     return lib.dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, ld, b, sfb, d, idx, m, n, k, g, None)
 
@@ -119,3 +143,8 @@ def test_binding_rejects_host_tensors_before_the_library():
     with pytest.raises(ValueError):
         dg.fp8_gemm_nt(a, torch.zeros(4, 128), torch.zeros(256, 512, dtype=torch.uint8),
                        torch.zeros(2, 4), torch.zeros(128, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        dg.fp8_gemm_nt_ue8m0(a, torch.zeros(1, 128, dtype=torch.int32),
+                             torch.zeros(256, 512, dtype=torch.uint8),
+                             torch.zeros(2, 1, dtype=torch.int32),
+                             torch.zeros(128, 256, dtype=torch.bfloat16))

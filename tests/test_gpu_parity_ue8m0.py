@@ -1,0 +1,179 @@
+"""Parity of the UE8M0-scaled calls (packed power-of-two scales, four K blocks per int32,
+applied by the block-scaled MFMA) with the CPU oracle on the same seeded inputs: every
+pipelined tile configuration on ragged shapes, K-block counts that leave the last packed
+word partly used, persistent workgroups looping over tiles, NaN scales, the grouped forms
+with their padding and clamps, and the full-size workloads on sampled rows."""
+import sys
+
+import numpy as np
+import pytest
+
+import moe_grouped_gemm_fp8_amd as dg
+import oracle
+import workloads as W
+from gpu_util import (assert_parity, dense_rows_ref, fp32_scales, run_contiguous, run_dense,
+                      run_masked)
+from tolerance import bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+PIPELINED = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "256x128w8p",
+             "128x128w4d4", "128x128w8d4", "128x256w8"]
+
+
+def _say(msg):
+    print(f"[parity-ue8m0] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    _say(f"start {request.node.name}")
+    yield
+
+
+def dense_ref(p):
+    return oracle.fp8_gemm_nt_ue8m0(p.a, p.sfa, p.b, p.sfb, p.c)
+
+
+# ------------------------------------------------------------------------------ dense
+
+def test_dense_small_workload_full():
+    p = W.make_config("dense_small", seed=0, ue8m0=True)
+    assert_parity(run_dense(p), dense_ref(p), "dense_small ue8m0")
+
+
+@pytest.mark.parametrize("cfg", PIPELINED)
+def test_dense_ragged_every_tile_config(cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_dense(200, 336, 640, seed=51, with_c=True, ue8m0=True)   # 5 K blocks: 2 words
+    assert_parity(run_dense(p), dense_ref(p), cfg)
+
+
+def test_streaming_tile_rejects_ue8m0(monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "stream64")
+    p = W.make_dense(64, 256, 512, seed=52, ue8m0=True)
+    with pytest.raises(dg.DGError) as e:
+        run_dense(p)
+    assert e.value.code == -2
+
+
+@pytest.mark.parametrize("k", [128, 256, 384, 512, 1152, 2048])
+@pytest.mark.parametrize("cfg", ["256x224w8", "128x256w8"])
+def test_dense_k_blocks_across_packed_words(cfg, k, monkeypatch):
+    # every position of the last K block inside its packed word, with C added in the loop
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_dense(256, 448, k, seed=53, with_c=True, c_std=2.0, ue8m0=True)
+    assert_parity(run_dense(p), dense_ref(p), f"{cfg} k={k}")
+
+
+PERSISTENT = ["128x256w8", "128x128w4", "64x32w4", "256x128w8p", "128x128w8d4"]
+
+
+@pytest.mark.parametrize("cfg", PERSISTENT)
+@pytest.mark.parametrize("wgs", ["3", "10"])
+def test_persistent_workgroups_loop_over_tiles(cfg, wgs, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    monkeypatch.setenv("DG_PERSIST_WGS", wgs)
+    p = W.make_dense(300, 528, 1280, seed=54, with_c=True, ue8m0=True)
+    assert_parity(run_dense(p), dense_ref(p), f"{cfg} wgs={wgs}")
+
+
+def test_dense_stress_scales():
+    # power-of-two multipliers 2^-8 .. 2^8 per segment and block: exponents 112..142 apart
+    p = W.make_dense(256, 384, 1024, seed=55, stress=True, ue8m0=True)
+    assert_parity(run_dense(p), dense_ref(p), "ue8m0 stress")
+
+
+def test_dense_small_shapes_take_pipelined_tiles():
+    # the FP32 call streams these with split-K; the UE8M0 call picks a pipelined tile
+    for m, n, k in [(1, 128, 128), (16, 2112, 1024), (64, 256, 7168)]:
+        p = W.make_dense(m, n, k, seed=56 + m, ue8m0=True)
+        assert_parity(run_dense(p), dense_ref(p), f"{m}x{n}x{k}")
+
+
+def test_dense_nan_scale_poisons_its_row_or_block():
+    p = W.make_dense(128, 256, 512, seed=57, ue8m0=True)
+    sfa, sfb = p.sfa.copy(), p.sfb.copy()
+    sfa[0, 5] = (sfa[0, 5] & ~0xFF0000) | (0xFF << 16)          # row 5, K block 2
+    sfb[1, 0] = (sfb[1, 0] & ~0xFF) | 0xFF                      # columns 128..255, K block 0
+    p.sfa, p.sfb = sfa, sfb
+    ref = dense_ref(p)
+    assert np.isnan(ref[5]).all() and np.isnan(ref[:, 128:]).all()
+    got_bits = run_dense(p)
+    got = bf16_bits_to_f64(got_bits)
+    assert np.isnan(got[5]).all() and np.isnan(got[:, 128:]).all()
+    keep = np.arange(128) != 5
+    assert_parity(got_bits[keep][:, :128], ref[keep][:, :128], "finite part")
+
+
+def test_dense_prefill_workload_sampled_rows():
+    p = W.make_config("dense_prefill", seed=0, ue8m0=True)      # 4096 x 7168 x 2048 with C
+    got = run_dense(p)
+    assert not np.any(got == W.BF16_SENTINEL), "some outputs were never written"
+    rng = np.random.default_rng(110)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(p.m - 8, p.m),
+                                     rng.choice(p.m, 48, replace=False)]))
+    assert_parity(got[rows], dense_rows_ref(p, rows), "dense_prefill ue8m0")
+
+
+# ------------------------------------------------------------------------------ contiguous
+
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w8d4", "128x256w8"])
+def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_contiguous(5, 600, 256, 640, seed=61, counts=[0, 130, 41, 300, 129],
+                          pad_nan=True, ue8m0=True)
+    ref = oracle.m_grouped_contiguous_ue8m0(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(run_contiguous(p), ref, f"contiguous ue8m0 {cfg}")
+
+
+def test_contiguous_workload_sampled_rows():
+    p = W.make_config("moe_contiguous", seed=0, ue8m0=True)    # 8 experts, 32768 x 4096 x 7168
+    got = run_contiguous(p)
+    pad = p.m_indices < 0
+    assert np.all(got[pad] == W.BF16_SENTINEL), "padding rows were written"
+    sfa, sfb = fp32_scales(p)
+    rng = np.random.default_rng(111)
+    rows = []
+    for g in range(p.num_groups):
+        idx = np.nonzero(p.m_indices == g)[0]
+        if idx.size:
+            rows += [idx[0], idx[-1]] + list(rng.choice(idx, min(6, idx.size), replace=False))
+    rows = np.unique(np.array(rows))
+    ref = np.stack([oracle.fp8_gemm_nt(p.a[r:r + 1], W.mn_major(sfa[:, r:r + 1].T),
+                                       p.b[p.m_indices[r]], sfb[p.m_indices[r]])[0]
+                    for r in rows])
+    assert_parity(got[rows], ref, "moe_contiguous ue8m0")
+    assert not np.any(got[~pad] == W.BF16_SENTINEL), "valid rows were left unwritten"
+
+
+# ------------------------------------------------------------------------------ masked
+
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "256x128w8", "256x128w8p",
+                                 "256x224w8"])
+def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    mm = [0, 1, 255, 256, 130, 999, -3]
+    p = W.make_masked(7, 256, 384, 640, seed=71, masked_m=mm, tail_nan=True, ue8m0=True)
+    ref = oracle.m_grouped_masked_ue8m0(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(run_masked(p), ref, f"masked ue8m0 {cfg}")
+
+
+def test_masked_workload_sampled_rows():
+    p = W.make_config("moe_masked", seed=0, ue8m0=True)        # 16 x 256 x 7168 x 2048
+    got = run_masked(p)
+    sfa, sfb = fp32_scales(p)
+    rng = np.random.default_rng(112)
+    for g in range(p.num_groups):
+        valid = int(p.masked_m[g])
+        assert np.all(got[g, valid:] == W.BF16_SENTINEL), f"group {g}: tail written"
+        if valid == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, valid - 1], rng.choice(valid, min(4, valid),
+                                                                      replace=False)]))
+        ref = oracle.fp8_gemm_nt(p.a[g, rows], W.mn_major(sfa[g][:, rows].T), p.b[g], sfb[g])
+        assert_parity(got[g, rows], ref, f"moe_masked ue8m0 group {g}")
+        assert not np.any(got[g, :valid] == W.BF16_SENTINEL)
