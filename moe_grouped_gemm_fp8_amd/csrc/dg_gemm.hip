@@ -106,8 +106,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // block's partial, promoted into the FP32 accumulators with sa * sb.  Packed UE8M0 scales
     // (powers of two, four K blocks per int32) are applied by the MFMA itself
     // (v_mfma_scale_f32_16x16x128_f8f6f4 multiplies by 2^(ea-127) * 2^(eb-127)), which then
-    // accumulates straight into the accumulators: no partials, no promotion.
-    constexpr bool UE8 = SF == SF_UE8M0;
+    // accumulates straight into the accumulators: no partials, no promotion.  Where the vector
+    // unit also writes the accumulators inside the K loop (C added there) or MFMAs are skipped
+    // under a branch (masked rows), the UE8M0 partial variant keeps the FP32 path's partials
+    // and adds them unscaled: a VALU access to an accumulator that an MFMA has just written
+    // waits for that MFMA, and a branch around accumulating MFMAs makes the compiler copy the
+    // accumulators.
+    constexpr bool UE8 = SF != SF_FP32;
+    constexpr bool DIRECT = SF == SF_UE8M0;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
@@ -534,25 +540,30 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const v8i bv = v8i{bf[0].x, bf[0].y, bf[0].z, bf[0].w, bf[1].x, bf[1].y, bf[1].z, bf[1].w};
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            // (UE8M0: every row sub-tile, since a skipped MFMA that carries its accumulator
-            // through a branch costs the 256x224 tile its registers)
-            if (MODE != MODE_MASKED || UE8 || i < sm_act) {
+            if (MODE != MODE_MASKED || DIRECT || i < sm_act) {
                 const v8i av = v8i{Af[i][0].x, Af[i][0].y, Af[i][0].z, Af[i][0].w,
                                    Af[i][1].x, Af[i][1].y, Af[i][1].z, Af[i][1].w};
-                if constexpr (UE8) {
+                if constexpr (DIRECT) {
                     // first operand B (its block's exponent), second A (this lane's row's)
                     acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         bv, av, acc[i][jj], 0, 0, 0, eb[jj], 0, ea[i]);
                 } else {
                     {
                         v4f &a = acc[i][jj == 0 ? SN - 1 : jj - 1];
-                        a += pend[i] * scale(i);
+                        if constexpr (UE8)
+                            a += pend[i];  // already scaled by the MFMA
+                        else
+                            a += pend[i] * scale(i);
                         // keep the promotion here: left free, the compiler hoists every MFMA
                         // of the block above all promotions and holds SM*SN partials live
                         asm volatile("" : "+v"(a));
                     }
-                    pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    if constexpr (UE8)
+                        pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, eb[jj], 0, ea[i]);
+                    else
+                        pend[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                 }
             }
             extra(I);
@@ -861,11 +872,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             tie(Bf[1][1]);
         }
         // the tile's last partials
-        if constexpr (!UE8) {
+        if constexpr (!DIRECT) {
 #pragma unroll
             for (int i = 0; i < SM; ++i)
                 if (MODE != MODE_MASKED || i < sm_act)
-                    acc[i][SN - 1] += pend[i] * psc[i];
+                    acc[i][SN - 1] += UE8 ? pend[i] : pend[i] * psc[i];
         }
 
         // ---- epilogue: + C (columns not streamed), round to bf16, store the valid rows from
@@ -1026,18 +1037,22 @@ template <int BM, int BN, int WM, int WN, int DEPTH, bool PERSIST, int SF>
 static void launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_m, int tiles_n,
                          hipStream_t stream)
 {
+    // (the UE8M0 variants are built for the forms that use them: direct accumulation for
+    // dense and contiguous, partials for dense and masked)
     switch (mode) {
     case MODE_DENSE:
         hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE, PERSIST, SF>), g, b, 0,
                            stream, a, tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST, SF>), g, b,
-                           0, stream, a, tiles_m, tiles_n);
+        if constexpr (SF != SF_UE8M0_PARTIAL)
+            hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST, SF>), g,
+                               b, 0, stream, a, tiles_m, tiles_n);
         break;
     default:
-        hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST, SF>), g, b,
-                           0, stream, a, tiles_m, tiles_n);
+        if constexpr (SF != SF_UE8M0)
+            hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST, SF>), g,
+                               b, 0, stream, a, tiles_m, tiles_n);
         break;
     }
 }
@@ -1056,8 +1071,13 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     const int64_t grid = workgroups(total, PERSIST, a);
     dim3 g((unsigned)grid), b(cfg_threads);
-    if (a.sf_fmt == SF_UE8M0)
+    // UE8M0: MFMAs accumulate directly unless C is added inside the K loop or masked rows
+    // skip MFMAs
+    if (a.sf_fmt == SF_UE8M0 && (mode == MODE_CONTIG || (mode == MODE_DENSE && !a.c)))
         launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0>(mode, g, b, a, tiles_m, tiles_n, stream);
+    else if (a.sf_fmt == SF_UE8M0)
+        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0_PARTIAL>(mode, g, b, a, tiles_m,
+                                                                        tiles_n, stream);
     else
         launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_FP32>(mode, g, b, a, tiles_m, tiles_n, stream);
     return hipGetLastError();

@@ -11,6 +11,11 @@ enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 // Scale formats: FP32 (1x128 A segments, 128x128 B blocks), or the same granularity as packed
 // UE8M0 exponents (four K blocks per 32-bit word, least significant byte first).
 enum ScaleFmt : int { SF_FP32 = 0, SF_UE8M0 = 1 };
+// Kernel variant of UE8M0 scales that keeps per-block MFMA partials (added to the accumulators
+// on the vector unit, as with FP32 scales but without the multiply): for the masked form, which
+// skips the MFMAs of row sub-tiles past masked_m, and for dense calls with C, which add C to
+// the accumulators inside the K loop.
+constexpr int SF_UE8M0_PARTIAL = 2;
 
 // Tile configurations compiled ahead of time.  Each is (BM x BN) output rows x columns per
 // workgroup, split over WM x WN waves of 64 lanes; every wave owns a (BM/WM) x (BN/WN) block

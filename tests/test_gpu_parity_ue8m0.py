@@ -43,11 +43,14 @@ def test_dense_small_workload_full():
     assert_parity(run_dense(p), dense_ref(p), "dense_small ue8m0")
 
 
+# Without C the MFMAs accumulate directly; with C (added to the accumulators inside the K
+# loop) they produce per-block partials that the vector unit adds: both kernel variants.
+@pytest.mark.parametrize("with_c", [False, True])
 @pytest.mark.parametrize("cfg", PIPELINED)
-def test_dense_ragged_every_tile_config(cfg, monkeypatch):
+def test_dense_ragged_every_tile_config(cfg, with_c, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
-    p = W.make_dense(200, 336, 640, seed=51, with_c=True, ue8m0=True)   # 5 K blocks: 2 words
-    assert_parity(run_dense(p), dense_ref(p), cfg)
+    p = W.make_dense(200, 336, 640, seed=51, with_c=with_c, ue8m0=True)  # 5 K blocks: 2 words
+    assert_parity(run_dense(p), dense_ref(p), f"{cfg} c={with_c}")
 
 
 def test_streaming_tile_rejects_ue8m0(monkeypatch):
@@ -60,10 +63,11 @@ def test_streaming_tile_rejects_ue8m0(monkeypatch):
 
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 1152, 2048])
 @pytest.mark.parametrize("cfg", ["256x224w8", "128x256w8"])
-def test_dense_k_blocks_across_packed_words(cfg, k, monkeypatch):
-    # every position of the last K block inside its packed word, with C added in the loop
+@pytest.mark.parametrize("with_c", [False, True])
+def test_dense_k_blocks_across_packed_words(cfg, k, with_c, monkeypatch):
+    # every position of the last K block inside its packed word (with C: added in the loop)
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
-    p = W.make_dense(256, 448, k, seed=53, with_c=True, c_std=2.0, ue8m0=True)
+    p = W.make_dense(256, 448, k, seed=53, with_c=with_c, c_std=2.0, ue8m0=True)
     assert_parity(run_dense(p), dense_ref(p), f"{cfg} k={k}")
 
 
@@ -71,11 +75,11 @@ PERSISTENT = ["128x256w8", "128x128w4", "64x32w4", "256x128w8p", "128x128w8d4"]
 
 
 @pytest.mark.parametrize("cfg", PERSISTENT)
-@pytest.mark.parametrize("wgs", ["3", "10"])
-def test_persistent_workgroups_loop_over_tiles(cfg, wgs, monkeypatch):
+@pytest.mark.parametrize("wgs,with_c", [("3", True), ("10", False)])
+def test_persistent_workgroups_loop_over_tiles(cfg, wgs, with_c, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_PERSIST_WGS", wgs)
-    p = W.make_dense(300, 528, 1280, seed=54, with_c=True, ue8m0=True)
+    p = W.make_dense(300, 528, 1280, seed=54, with_c=with_c, ue8m0=True)
     assert_parity(run_dense(p), dense_ref(p), f"{cfg} wgs={wgs}")
 
 
