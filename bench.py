@@ -372,8 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dense_prefill",
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
-                             "moe_masked", "dense_prefill_ue8m0", "moe_contiguous_ue8m0",
-                             "moe_masked_ue8m0"])
+                             "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
+                             "moe_contiguous_ue8m0", "moe_masked_ue8m0"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -404,6 +404,7 @@ def main():
         "moe_contiguous": lambda: make_contiguous_case(torch, dg, W),
         "moe_masked": lambda: make_masked_case(torch, dg, W),
         "dense_prefill_ue8m0": lambda: make_dense_case(torch, dg, W, "dense_prefill", True),
+        "dense_skinny_ue8m0": lambda: make_dense_case(torch, dg, W, "dense_skinny", True),
         "moe_contiguous_ue8m0": lambda: make_contiguous_case(torch, dg, W, True),
         "moe_masked_ue8m0": lambda: make_masked_case(torch, dg, W, True),
     }
@@ -415,7 +416,8 @@ def main():
         case = makers[name]()
         # the short workloads take many steps (their spread matters); the long ones fewer
         steps = args.steps if name == args.workload else (
-            200 if name in ("dense_small", "dense_skinny", "moe_masked", "moe_masked_ue8m0")
+            200 if name in ("dense_small", "dense_skinny", "moe_masked", "dense_skinny_ue8m0",
+                            "moe_masked_ue8m0")
             else max(20, args.steps // 2))
         log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
         res = time_case(torch, case, steps, args.warmup)
@@ -441,7 +443,7 @@ def main():
                     frac=achieved / PEAK_FP8_TFLOPS, traffic=traffic,
                     kernel_avg_us=summ["avg_kernel_us"], hbm_gbs_algorithmic=summ["hbm_gbs"],
                     hbm_frac_algorithmic=summ["hbm_gbs"] / PEAK_HBM_GBS)
-    if dom in ("dense_skinny", "moe_masked", "moe_masked_ue8m0"):
+    if dom in ("dense_skinny", "moe_masked", "dense_skinny_ue8m0", "moe_masked_ue8m0"):
         roofline.update(bound="hbm", achieved=summ["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=summ["hbm_gbs"] / PEAK_HBM_GBS)
     out = {

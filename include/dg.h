@@ -115,9 +115,8 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
  *        int32 [num_groups][ceil(k/512)][ld_sfa]          (masked)
  *   sfb  int32 [ceil(n/128)][ceil(k/512)]                 (dense)
  *        int32 [num_groups][ceil(n/128)][ceil(k/512)]     (grouped)
- * Every other argument, precondition and behaviour is that of the FP32 call; the MFMA applies
- * the exponents itself.  Dense shapes too small for the pipelined tiles run on them anyway
- * (the streaming split-K path takes FP32 scales only).
+ * Every other argument, precondition and behaviour is that of the FP32 call (including the
+ * split-K path of skinny dense shapes and its workspace); the MFMA applies the exponents.
  */
 int dg_fp8_gemm_nt_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa, const void *b,
                          const int32_t *sfb, const float *c, void *d, int m, int n, int k,

@@ -223,9 +223,8 @@ int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const v
     // and for shapes whose big tiles would leave most CUs idle.
     int cfg = forced_config();
     if (cfg < 0) {
-        // (UE8M0 scales have no streaming split-K tile: its small shapes take 64x32 tiles)
-        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128, dg::CFG_64x32};
-        const int ncands = sf_fmt == dg::SF_FP32 ? 3 : 4;
+        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
+        const int ncands = 3;
         double best = 0;
         int64_t best_tiles = 0;
         for (int ci = 0; ci < ncands; ++ci) {
@@ -239,12 +238,9 @@ int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const v
                 best_tiles = tiles;
             }
         }
-        // (the streaming kernel takes FP32 scales only)
-        if ((m <= 64 || 2 * best_tiles < cus) && sf_fmt == dg::SF_FP32)
+        if (m <= 64 || 2 * best_tiles < cus)
             cfg = dg::CFG_STREAM64;
     }
-    if (cfg == dg::CFG_STREAM64 && sf_fmt != dg::SF_FP32)
-        return fail(DG_ERR_UNSUPPORTED, "the streaming split-K tile takes FP32 scales only");
     if (cfg == dg::CFG_STREAM64) {
         // one workgroup per (64x64 tile, split): enough splits to cover the CUs, never more
         // than stream_max_kblocks() K blocks in one split, every split non-empty

@@ -10,7 +10,8 @@
 //    soon as its own copies have landed, while the later blocks are still arriving.
 //  * Four waves, one 16-column slice of B each; a wave runs one v_mfma_f32_16x16x128_f8f6f4
 //    per (16-row A sub-tile, K block) and promotes the partial with sa * sb into FP32
-//    accumulators, exactly as the pipelined kernels do.
+//    accumulators, exactly as the pipelined kernels do.  With packed UE8M0 scales (four K
+//    blocks' exponents per int32) the block-scaled MFMA applies them and accumulates itself.
 //  * With several splits, each writes its FP32 partial tile to a workspace and a second
 //    kernel sums the partials in split order (deterministic), adds C, rounds to bf16 and
 //    stores the valid rows and columns.  The kernel boundary makes the partials visible; a
@@ -57,6 +58,7 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs &p, v4f (&acc)[4]
     }
 }
 
+template <bool UE8>
 __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m, int tiles_n)
 {
     constexpr int A_SLOT = ST_BM * KBLK;             // one K block of the tile's A rows
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m,
     const int K = p.k, N = p.n, M = p.m;
     const int KB = K / KBLK;
     const int NB = (N + KBLK - 1) / KBLK;
+    const int KS = UE8 ? (KB + 3) / 4 : KB;  // scale words per row (UE8M0: four blocks each)
     const int64_t ld = p.ld_sfa;
 
     // workgroup id -> (m tile, n tile, split); splits of one tile are adjacent ids, so they
@@ -94,8 +97,10 @@ __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m,
     // swizzled layout.  Rows past M or N read zeros (buffer range), never stored.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * K, (int64_t)(M - m0) * K);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * K, (int64_t)(N - n0) * K);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (int64_t)KB * ld * 4);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sfb, (int64_t)NB * KB * 4);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (int64_t)KS * ld * 4);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sfb, (int64_t)NB * KS * 4);
+    // the scale word holding K block kb (UE8M0: its byte kb % 4)
+    auto word = [](int kb) { return UE8 ? kb >> 2 : kb; };
     DG_LDS uint8_t *ldsp = (DG_LDS uint8_t *)lds;
     const uint32_t lane_even = (uint32_t)(lane >> 3) * (uint32_t)K +
                                (uint32_t)((((lane & 7) ^ ((lane >> 4) << 1))) << 4);
@@ -106,11 +111,12 @@ __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m,
     for (int kb = wave; kb < nk; kb += 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (DG_LDS void *)(ldsp + SA_BASE + kb * 256), 4,
-            (uint32_t)(((int64_t)(kb0 + kb) * ld + m0 + lane) * 4), 0, 0, 0);
+            (uint32_t)(((int64_t)word(kb0 + kb) * ld + m0 + lane) * 4), 0, 0, 0);
     if (wave == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsb, (DG_LDS void *)(ldsp + SB_BASE), 4,
-            lane < nk ? (uint32_t)(((n0 / KBLK) * KB + kb0 + lane) * 4) : 0x80000000u, 0, 0, 0);
+            lane < nk ? (uint32_t)(((n0 / KBLK) * KS + word(kb0 + lane)) * 4) : 0x80000000u, 0,
+            0, 0);
     // operands, K block by K block: block kb's 16 copies (8 of A rows, 8 of B rows) are four
     // per wave, copy 4u + wave of the block
     for (int kb = 0; kb < nk; ++kb) {
@@ -176,13 +182,20 @@ __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m,
         const v8i bv = v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         v8i av[4];
         float sc[4];
+        int ea[4], eb = 0;
+        const int sh = 8 * ((kb0 + kb) & 3);  // UE8M0: the byte of block kb0 + kb
+        if constexpr (UE8)
+            eb = (__builtin_amdgcn_readfirstlane(__float_as_int(sb)) >> sh) & 0xFF;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             tie(a0[i]);
             tie(a1[i]);
             tie(sa[i]);
             av[i] = v8i{a0[i].x, a0[i].y, a0[i].z, a0[i].w, a1[i].x, a1[i].y, a1[i].z, a1[i].w};
-            sc[i] = sa[i] * sb;
+            if constexpr (UE8)
+                ea[i] = (__float_as_int(sa[i]) >> sh) & 0xFF;
+            else
+                sc[i] = sa[i] * sb;
         }
         if (kb + 1 < nk) {  // the next block's reads overlap this block's MFMAs
             land(kb + 1);
@@ -190,9 +203,15 @@ __global__ __launch_bounds__(256) void dg_stream_kernel(GemmArgs p, int tiles_m,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bv, av[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            acc[i] += part * sc[i];
+            if constexpr (UE8) {
+                // first operand B (its block's exponent), second A (this lane's row's)
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av[i], acc[i], 0, 0,
+                                                                          0, eb, 0, ea[i]);
+            } else {
+                const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bv, av[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                acc[i] += part * sc[i];
+            }
         }
     }
 
@@ -262,8 +281,12 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t stream)
     const int64_t grid = stream_grid_size(a);
     if (grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(dg_stream_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, tiles_m,
-                       tiles_n);
+    if (a.sf_fmt == SF_UE8M0)
+        hipLaunchKernelGGL(dg_stream_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, a,
+                           tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL(dg_stream_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, a,
+                           tiles_m, tiles_n);
     if (a.splits > 1)
         hipLaunchKernelGGL(dg_stream_reduce_kernel, dim3((unsigned)(tiles_m * tiles_n * 4)),
                            dim3(256), 0, stream, a, tiles_n);

@@ -8,7 +8,6 @@ import sys
 import numpy as np
 import pytest
 
-import moe_grouped_gemm_fp8_amd as dg
 import oracle
 import workloads as W
 from gpu_util import (assert_parity, dense_rows_ref, fp32_scales, run_contiguous, run_dense,
@@ -53,12 +52,21 @@ def test_dense_ragged_every_tile_config(cfg, with_c, monkeypatch):
     assert_parity(run_dense(p), dense_ref(p), f"{cfg} c={with_c}")
 
 
-def test_streaming_tile_rejects_ue8m0(monkeypatch):
+@pytest.mark.parametrize("with_c", [False, True])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_streaming_split_k_with_ragged_tiles(splits, with_c, monkeypatch):
+    # 9 K blocks in 3 packed words: splits start inside a word (kb0 = 5, 3, 2, ...)
     monkeypatch.setenv("DG_FORCE_CONFIG", "stream64")
-    p = W.make_dense(64, 256, 512, seed=52, ue8m0=True)
-    with pytest.raises(dg.DGError) as e:
-        run_dense(p)
-    assert e.value.code == -2
+    monkeypatch.setenv("DG_FORCE_SPLITS", str(splits))
+    p = W.make_dense(100, 208, 1152, seed=52, with_c=with_c, ue8m0=True)
+    assert_parity(run_dense(p), dense_ref(p), f"stream64 splits={splits} c={with_c}")
+
+
+def test_dense_skinny_workload_full_and_deterministic():
+    p = W.make_config("dense_skinny", seed=0, ue8m0=True)      # 64 x 2112 x 7168, split-K
+    d1 = run_dense(p)
+    assert_parity(d1, dense_ref(p), "dense_skinny ue8m0")
+    assert np.array_equal(d1, run_dense(p)), "split-K reduction is not deterministic"
 
 
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 1152, 2048])
@@ -89,8 +97,7 @@ def test_dense_stress_scales():
     assert_parity(run_dense(p), dense_ref(p), "ue8m0 stress")
 
 
-def test_dense_small_shapes_take_pipelined_tiles():
-    # the FP32 call streams these with split-K; the UE8M0 call picks a pipelined tile
+def test_dense_small_shapes():
     for m, n, k in [(1, 128, 128), (16, 2112, 1024), (64, 256, 7168)]:
         p = W.make_dense(m, n, k, seed=56 + m, ue8m0=True)
         assert_parity(run_dense(p), dense_ref(p), f"{m}x{n}x{k}")
