@@ -163,3 +163,41 @@ def m_grouped_masked_ue8m0(a, sfa, b, sfb, masked_m) -> np.ndarray:
     kb = np.asarray(a).shape[2] // 128
     return m_grouped_masked(a, ue8m0_decode(sfa, 1, kb), b, ue8m0_decode(sfb, 2, kb),
                             masked_m)
+
+
+# ---------------------------------------------------------------------------------------------
+# K-grouped TN form (MoE weight gradient; pt.news.hada.io, "GEMM denso e grouped": grouping on
+# the K axis with M and N fixed; "Interface GEMM e restrições de layout": D = C + A @ B, with
+# the TN memory layout).  A is stored [K_total, M] and B [K_total, N] (both K-major in the
+# mathematical sense of "transposed" A and "not transposed" B), the groups are consecutive runs
+# of K of lengths ks[g] (multiples of 128), and both scale sets are one FP32 value per 128-deep
+# K block per column: sfa [K_total/128, M], sfb [K_total/128, N].  The plain definition:
+#   D[g, m, n] = C[g, m, n] + sum over the K blocks kb of group g of
+#                sfa[kb, m] * sfb[kb, n] * sum_{k in kb} dec(A[k, m]) * dec(B[k, n])
+# Each block sum is a matrix product of decoded values; every e4m3 value is an integer times
+# 2^-9 below 2^18 in magnitude, so the 128-term sums are exact in float64 in any order, and a
+# library product serves for them.  Then the scaled terms are added in float64, blocks in
+# ascending order, and C last.
+
+def k_grouped_tn(a, sfa, b, sfb, ks, c=None) -> np.ndarray:
+    """float64 D [G, M, N] of the K-grouped TN GEMM (``a`` uint8 [K_total, M], ``b`` uint8
+    [K_total, N], ``sfa`` [K_total/128, M], ``sfb`` [K_total/128, N], ``ks`` [G])."""
+    a, b = _c(a, np.uint8), _c(b, np.uint8)
+    sfa, sfb = _c(sfa, np.float32), _c(sfb, np.float32)
+    ks = np.asarray(ks, dtype=np.int64)
+    k_total, m = a.shape
+    n = b.shape[1]
+    if np.any(ks < 0) or np.any(ks % 128) or ks.sum() > k_total:
+        raise ValueError("oracle: group extents must be non-negative multiples of 128")
+    tab = e4m3_table()
+    d = np.zeros((len(ks), m, n), dtype=np.float64)
+    k0 = 0
+    for g, kg in enumerate(ks):
+        for kb in range(k0 // 128, (k0 + int(kg)) // 128):
+            rows = slice(kb * 128, (kb + 1) * 128)
+            part = tab[a[rows]].T @ tab[b[rows]]                     # exact block sums
+            d[g] += (sfa[kb].astype(np.float64)[:, None] * sfb[kb].astype(np.float64)[None, :]) * part
+        k0 += int(kg)
+    if c is not None:
+        d += _c(c, np.float32).astype(np.float64)
+    return d

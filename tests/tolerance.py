@@ -15,11 +15,13 @@ def rms(x: np.ndarray) -> float:
     return float(np.sqrt(np.mean(x * x))) if x.size else 0.0
 
 
-def tol_violations(d: np.ndarray, ref: np.ndarray) -> np.ndarray:
-    """Boolean mask of elements outside the tolerance (NaN anywhere counts as a violation)."""
+def tol_violations(d: np.ndarray, ref: np.ndarray, rel: float = REL,
+                   rms_frac: float = RMS) -> np.ndarray:
+    """Boolean mask of elements outside the tolerance (NaN anywhere counts as a violation).
+    ``rel`` and ``rms_frac`` replace the bf16-output rule's terms for the FP32-output form."""
     d = np.asarray(d, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    bound = REL * np.abs(ref) + RMS * rms(ref)
+    bound = rel * np.abs(ref) + rms_frac * rms(ref)
     err = np.abs(d - ref)
     return ~(err <= bound)
 

@@ -245,6 +245,85 @@ class Masked:
     k: int
 
 
+# ---------------------------------------------------------------------------------------------
+# K-grouped form (MoE weight gradient, pt.news.hada.io, "GEMM denso e grouped": grouping on the
+# K axis with M and N fixed).  Both operands are token-major ("T"/"N" of the TN layout): A is
+# stored [K_total, M] and B [K_total, N], K being the tokens, concatenated group after group,
+# each group's run padded with zero tokens to a multiple of 128.  Both are cast per 128 tokens
+# of one column (a 128x1 block along K), the granularity the two-level accumulation needs when
+# K is the token axis.
+
+
+def quantize_kblocks(x: np.ndarray, mult: Optional[np.ndarray] = None):
+    """128x1 cast along the leading (K) axis: x float32 [K, C] -> (bits uint8 [K, C],
+    scales float32 [K/128, C]); ``mult`` [K/128, C] multiplies each block first (stress)."""
+    k, cols = x.shape
+    assert k % BLOCK == 0
+    xs = x.reshape(k // BLOCK, BLOCK, cols)
+    if mult is not None:
+        xs = xs * mult[:, None, :].astype(np.float32)
+    scale = _scale_of(np.abs(xs).max(axis=1), False)
+    bits = _cast(xs, scale[:, None, :]).reshape(k, cols)
+    return bits, scale
+
+
+@dataclasses.dataclass
+class KGrouped:
+    a: np.ndarray            # uint8 [K_total, M]  (M contiguous)
+    sfa: np.ndarray          # float32 [K_total/128, M]
+    b: np.ndarray            # uint8 [K_total, N]  (N contiguous)
+    sfb: np.ndarray          # float32 [K_total/128, N]
+    ks: np.ndarray           # int32 [G]: the K extent of each group, multiples of 128 (0 allowed)
+    counts: np.ndarray       # real tokens per group (the rest of its extent is zero padding)
+    c: Optional[np.ndarray]  # float32 [G, M, N] or None
+    num_groups: int
+    m: int
+    n: int
+    k_total: int
+
+
+def make_k_grouped(num_groups: int, total_tokens: int, m: int, n: int, seed: int = 0,
+                   counts=None, with_c: bool = False, c_std: float = 0.1,
+                   stress: bool = False) -> KGrouped:
+    """K-grouped TN layout.  Draw order: the ``total_tokens`` token rows of A [T, M], those of
+    B [T, N], the routing p ~ Dirichlet(1) and counts ~ Multinomial(T, p) (unless ``counts`` is
+    given), C [G, M, N], then (stress) per-block multipliers 2^U{-8..8}.  Group g's tokens
+    follow group g-1's; its extent is its count rounded up to a multiple of 128, with zero
+    tokens (e4m3 0) in the padding."""
+    rng = np.random.default_rng(seed)
+    xa = rng.standard_normal((total_tokens, m), dtype=np.float32)
+    xb = rng.standard_normal((total_tokens, n), dtype=np.float32)
+    if counts is None:
+        p = rng.dirichlet(np.ones(num_groups))
+        counts = rng.multinomial(total_tokens, p)
+    counts = np.asarray(counts, dtype=np.int64)
+    assert counts.sum() == total_tokens
+    c = None
+    if with_c:
+        c = rng.standard_normal((num_groups, m, n), dtype=np.float32) * np.float32(c_std)
+    ks = (counts + BLOCK - 1) // BLOCK * BLOCK
+    k_total = int(ks.sum())
+    pa = np.zeros((k_total, m), dtype=np.float32)
+    pb = np.zeros((k_total, n), dtype=np.float32)
+    src = dst = 0
+    for g in range(num_groups):
+        cnt = int(counts[g])
+        pa[dst:dst + cnt] = xa[src:src + cnt]
+        pb[dst:dst + cnt] = xb[src:src + cnt]
+        src += cnt
+        dst += int(ks[g])
+    del xa, xb
+    ma = mb = None
+    if stress:
+        ma = _pow2_mult(rng, (k_total // BLOCK, m))
+        mb = _pow2_mult(rng, (k_total // BLOCK, n))
+    a, sfa = quantize_kblocks(pa, ma)
+    del pa
+    b, sfb = quantize_kblocks(pb, mb)
+    return KGrouped(a=a, sfa=sfa, b=b, sfb=sfb, ks=ks.astype(np.int32), counts=counts, c=c,
+                    num_groups=num_groups, m=m, n=n, k_total=k_total)
+
+
 def masked_counts(num_groups: int, m_max: int, seed: int, replay: Optional[int] = None) -> np.ndarray:
     """masked_m ~ U{0..m_max} per group (inclusive). Replay r draws from default_rng((seed, r))."""
     rng = np.random.default_rng(seed if replay is None else (seed, replay))
@@ -299,6 +378,8 @@ CONFIGS = {
     "dense_skinny": dict(kind="dense", m=64, n=2112, k=7168, with_c=False),
     "moe_contiguous": dict(kind="contiguous", num_groups=8, total_rows=32768, n=4096, k=7168),
     "moe_masked": dict(kind="masked", num_groups=16, m_max=256, n=7168, k=2048),
+    # weight gradient of moe_contiguous's experts: dW[g] (4096 x 7168) over each expert's tokens
+    "moe_wgrad": dict(kind="k_grouped", num_groups=8, total_tokens=32768, m=4096, n=7168),
 }
 
 
@@ -311,4 +392,6 @@ def make_config(name: str, seed: int = 0, **overrides):
         return make_dense(seed=seed, **cfg)
     if kind == "contiguous":
         return make_contiguous(seed=seed, **cfg)
+    if kind == "k_grouped":
+        return make_k_grouped(seed=seed, **cfg)
     return make_masked(seed=seed, **cfg)
