@@ -240,6 +240,32 @@ def make_masked_case(torch, dg, W, ue8m0=False):
     return c
 
 
+def make_kgrouped_case(torch, dg, W):
+    p = W.make_config("moe_wgrad", seed=0)
+    c = Case("moe_wgrad")
+    g, m, n = p.num_groups, p.m, p.n
+    t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
+             d=torch.empty(g, m, n, dtype=torch.float32, device="cuda"))
+    kbt = p.k_total // 128
+    tokens = int(p.counts.sum())
+    nbytes = p.k_total * (m + n) + 4 * kbt * (m + n) + 4 * g * m * n
+    c.sets = _copies(torch, t, nbytes)
+    per_graph = _steps_per_graph(len(c.sets))
+    ks = [int(x) for x in p.ks]
+
+    def call(s):
+        dg.k_grouped_fp8_gemm_tn_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d"], ks)
+
+    _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
+    c.config = dict(workload="moe_wgrad", groups=g, m=m, n=n, tokens=tokens,
+                    padded_k=p.k_total, d="fp32",
+                    launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
+    c.flops = lambda i: 2.0 * tokens * m * n
+    c.bytes = lambda i: float(nbytes)
+    return c
+
+
 def time_case(torch, case, steps, warmup):
     """Warm up, then time exactly `steps` steps as one region bracketed by HIP events on the
     launch stream (the step time and, for cases without a per-step device update, the kernel's
@@ -373,7 +399,7 @@ def main():
     ap.add_argument("--workload", default="dense_prefill",
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
                              "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
-                             "moe_contiguous_ue8m0", "moe_masked_ue8m0"])
+                             "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -407,6 +433,7 @@ def main():
         "dense_skinny_ue8m0": lambda: make_dense_case(torch, dg, W, "dense_skinny", True),
         "moe_contiguous_ue8m0": lambda: make_contiguous_case(torch, dg, W, True),
         "moe_masked_ue8m0": lambda: make_masked_case(torch, dg, W, True),
+        "moe_wgrad": lambda: make_kgrouped_case(torch, dg, W),
     }
     order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
     results = {}

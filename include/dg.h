@@ -130,6 +130,29 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int
                                           const int32_t *masked_m, int num_groups, int m_max,
                                           int n, int k, int expected_m, void *stream);
 
+/*
+ * K-grouped TN GEMM, the MoE weight gradient (pt.news.hada.io, "GEMM denso e grouped": an API
+ * grouped on the K axis for the backward pass of MoE weights, M and N fixed;
+ * "Interface GEMM e restrições de layout": D = C + A @ B, the TN memory layout).  For each
+ * group g and its run of K (consecutive K indices, ks[g] of them):
+ *   D[g, m, n] = C[g, m, n] + sum over the group's K blocks kb of
+ *                sfa[kb, m] * sfb[kb, n] * sum_{k in kb} A[k, m] * B[k, n]
+ *   a    e4m3 [k_total][m]   token-major (M contiguous), 16-byte aligned
+ *   sfa  FP32 [k_total/128][m]   one scale per 128-deep K block per column of A
+ *   b    e4m3 [k_total][n]   token-major (N contiguous)
+ *   sfb  FP32 [k_total/128][n]
+ *   c    FP32 [num_groups][m][n] or NULL (zeros); may be d itself (accumulate in place)
+ *   d    FP32 [num_groups][m][n], written whole (a group with ks[g] == 0 gets C, or zeros)
+ *   ks   HOST int32 [num_groups]: multiples of 128 (0 allowed) summing to k_total; they go
+ *        to the kernel as launch arguments, so the call is graph-capturable
+ * Preconditions: 1 <= num_groups <= 256; m, n multiples of 16; k_total a multiple of 128;
+ * k_total * max(m, n) < 2^31; A, B, C, D, sfa, sfb 16-byte aligned.  Errors as above.
+ */
+int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const void *b,
+                                        const float *sfb, const float *c, float *d,
+                                        const int32_t *ks, int num_groups, int m, int n,
+                                        int k_total, void *stream);
+
 /* Row alignment of each group segment in the contiguous layout: 128 (the M block size). */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

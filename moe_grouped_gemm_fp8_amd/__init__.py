@@ -16,12 +16,13 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 __all__ = [
     "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
-    "m_grouped_fp8_gemm_nt_masked_ue8m0",
+    "m_grouped_fp8_gemm_nt_masked_ue8m0", "k_grouped_fp8_gemm_tn_contiguous",
     "get_mk_alignment_for_contiguous_layout", "get_sf_aligned_m", "set_num_cus", "get_num_cus",
     "library_path",
 ]
@@ -65,6 +66,9 @@ def _load():
         fn = getattr(lib, name + "_ue8m0")
         fn.argtypes = getattr(lib, name).argtypes
         fn.restype = i32
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                         i32, i32, vp]
+    lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
     lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
     lib.dg_get_sf_aligned_m.argtypes = [i64]
     lib.dg_get_sf_aligned_m.restype = i64
@@ -217,6 +221,34 @@ def m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m: 
     """m_grouped_fp8_gemm_nt_masked with packed UE8M0 scales: sfa int32
     [G, ceil(K/512), ld>=M_max], sfb int32 [G, ceil(N/128), ceil(K/512)]."""
     return _masked(a, sfa, b, sfb, d, masked_m, expected_m, stream, True)
+
+
+def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, d, ks, c: Optional[torch.Tensor] = None,
+                                     stream=None):
+    """K-grouped TN GEMM (MoE weight gradient): a [K_total, M] e4m3, sfa [K_total/128, M] f32,
+    b [K_total, N] e4m3, sfb [K_total/128, N] f32, d [G, M, N] f32 (written), ks: G host ints
+    (multiples of 128 summing to K_total), c [G, M, N] f32, None, or d itself."""
+    pa = _dev(a, "a", _FP8_DTYPES, 2)
+    k_total, m = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 2)
+    _need(b.shape[0] == k_total, "a and b disagree on K_total")
+    n = b.shape[1]
+    _need(k_total % 128 == 0, "K_total must be a multiple of 128")
+    psfa = _dev(sfa, "sfa", torch.float32, 2)
+    _need(tuple(sfa.shape) == (k_total // 128, m), "sfa must be [K_total/128, M]")
+    psfb = _dev(sfb, "sfb", torch.float32, 2)
+    _need(tuple(sfb.shape) == (k_total // 128, n), "sfb must be [K_total/128, N]")
+    ks_host = np.ascontiguousarray(np.asarray(ks, dtype=np.int32).reshape(-1))
+    g = int(ks_host.shape[0])
+    pd = _dev(d, "d", torch.float32, 3)
+    _need(tuple(d.shape) == (g, m, n), "d must be [G, M, N]")
+    pc = None
+    if c is not None:
+        pc = _dev(c, "c", torch.float32, 3)
+        _need(tuple(c.shape) == (g, m, n), "c must be [G, M, N]")
+    _check(_load().dg_k_grouped_fp8_gemm_tn_contiguous(
+        pa, psfa, pb, psfb, pc, pd, ks_host.ctypes.data, g, m, n, k_total, _stream(stream)))
+    return d
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

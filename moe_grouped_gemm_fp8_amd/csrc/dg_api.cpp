@@ -422,6 +422,69 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int
                           n, k, expected_m, stream);
 }
 
+int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const void *b,
+                                        const float *sfb, const float *c, float *d,
+                                        const int32_t *ks, int num_groups, int m, int n,
+                                        int k_total, void *stream)
+{
+    if (!ks)
+        return fail(DG_ERR_INVALID_ARG, "null group extents");
+    if (num_groups < 1 || num_groups > dg::KG_MAX_GROUPS)
+        return fail(DG_ERR_UNSUPPORTED, "num_groups=%d outside [1, %d]", num_groups,
+                    dg::KG_MAX_GROUPS);
+    if (m <= 0 || n <= 0 || k_total < 0)
+        return fail(DG_ERR_INVALID_ARG, "sizes must be positive (m=%d n=%d k_total=%d)", m, n,
+                    k_total);
+    if (m % 16 != 0 || n % 16 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "m=%d and n=%d must be multiples of 16", m, n);
+    if (k_total % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "k_total=%d is not a multiple of 128", k_total);
+    if (!d || (k_total > 0 && (!a || !sfa || !b || !sfb)))
+        return fail(DG_ERR_INVALID_ARG, "null tensor pointer");
+    // byte offsets inside one operand are 32-bit
+    if ((int64_t)k_total * (m > n ? m : n) > 0x7fffffffLL)
+        return fail(DG_ERR_UNSUPPORTED, "k_total * max(m, n) exceeds 2^31 bytes");
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(c, 16))
+        return fail(DG_ERR_MISALIGNED, "A, B, C and D must be 16-byte aligned");
+    if (!aligned(sfa, 16) || !aligned(sfb, 16))
+        return fail(DG_ERR_MISALIGNED, "scale pointers must be 16-byte aligned");
+    // C may be D itself (accumulate in place), but must not overlap it otherwise
+    const int64_t d_bytes = (int64_t)num_groups * m * n * 4;
+    if (c && c != d) {
+        const char *cb = (const char *)c, *db = (const char *)d;
+        if (cb < db + d_bytes && db < cb + d_bytes)
+            return fail(DG_ERR_INVALID_ARG, "C overlaps D without being D");
+    }
+    dg::KGroupedArgs args;
+    memset(&args, 0, sizeof(args));
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.c = c;
+    args.d = d;
+    args.m = m;
+    args.n = n;
+    args.k_total = k_total;
+    args.num_groups = num_groups;
+    int64_t kb = 0;
+    for (int g = 0; g < num_groups; ++g) {
+        if (ks[g] < 0 || ks[g] % 128 != 0)
+            return fail(DG_ERR_UNSUPPORTED, "ks[%d]=%d is not a non-negative multiple of 128", g,
+                        ks[g]);
+        args.kb_start[g] = (int)kb;
+        kb += ks[g] / 128;
+    }
+    if (kb * 128 != k_total)
+        return fail(DG_ERR_INVALID_ARG, "the group extents sum to %lld, not k_total=%d",
+                    (long long)(kb * 128), k_total);
+    args.kb_start[num_groups] = (int)kb;
+    hipError_t e = dg::launch_kgrouped(args, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
 
 int64_t dg_get_sf_aligned_m(int64_t m) { return m <= 0 ? 0 : (m + 3) / 4 * 4; }

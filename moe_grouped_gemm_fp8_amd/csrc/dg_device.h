@@ -115,6 +115,30 @@ __device__ __forceinline__ float lds_read4_at(uint32_t base)
     return v;
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b8), as measured on the MI355X: within each
+// group of 16 lanes, lanes 2t and 2t+1 address the two 8-byte halves of a 16-byte "row" t
+// (t = 0..7), and lane j receives byte j of rows 0..7 in order: an 8 x 16 byte block turned
+// into 16 lanes x 8 bytes.  With one row per K index of an MN-major tile, lane j gets 8
+// consecutive K values of column j, the layout of an MFMA operand.
+typedef int v2i __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ v2i lds_read_tr8_at(uint32_t base)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    v2i v;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
+    return v;
+}
+
+template <int OFF>
+__device__ __forceinline__ v4f lds_read16f_at(uint32_t base)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    v4f v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
+    return v;
+}
+
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // All but the N most recent LDS reads have landed (LDS reads retire in order; outstanding
 // scalar loads only make the condition stricter).
@@ -143,6 +167,10 @@ __device__ __forceinline__ void lds_wait_le(int n)
 __device__ __forceinline__ void tie(v4i &v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ void tie(float &v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ void tie(v2i &v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ void tie(v4f &v) { asm volatile("" : "+v"(v)); }
 
 // Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: loop indices usable as constants.
 template <typename F, int... I>

@@ -148,3 +148,29 @@ def test_binding_rejects_host_tensors_before_the_library():
                              torch.zeros(256, 512, dtype=torch.uint8),
                              torch.zeros(2, 1, dtype=torch.int32),
                              torch.zeros(128, 256, dtype=torch.bfloat16))
+
+
+def kgrouped(lib, a=P, sfa=P, b=P, sfb=P, c=None, d=P, ks=(128, 256), m=128, n=256, k=384):
+    arr = (ctypes.c_int32 * len(ks))(*ks) if ks is not None else None
+    return lib.dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, c, d, arr, len(ks or ()), m,
+                                                   n, k, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), DG_ERR_INVALID_ARG),
+    (dict(ks=()), DG_ERR_UNSUPPORTED),
+    (dict(ks=(128,) * 257, k=128 * 257), DG_ERR_UNSUPPORTED),
+    (dict(m=120), DG_ERR_UNSUPPORTED),
+    (dict(n=0), DG_ERR_INVALID_ARG),
+    (dict(k=400), DG_ERR_UNSUPPORTED),
+    (dict(ks=(128, 100), k=228 + 28), DG_ERR_UNSUPPORTED),
+    (dict(ks=(128, 128)), DG_ERR_INVALID_ARG),
+    (dict(d=None), DG_ERR_INVALID_ARG),
+    (dict(a=P + 8), DG_ERR_MISALIGNED),
+    (dict(sfb=P + 4), DG_ERR_MISALIGNED),
+    (dict(c=P + 16), DG_ERR_INVALID_ARG),
+    (dict(m=65536, n=65536, k=32768, ks=(32768,)), DG_ERR_UNSUPPORTED),
+])
+def test_k_grouped_rejects_bad_arguments_on_host(lib, kw, code):
+    assert kgrouped(lib, **kw) == code
+    assert lib.dg_last_error().decode()
