@@ -8,8 +8,8 @@
 //
 // Design:
 //  * One workgroup per 128 x 128 tile of one group; eight waves (2 x 4), wave tile 64 x 32.
-//    Tiles go to the XCDs in contiguous ranges, rastered within a group, so the tiles in
-//    flight on one XCD share A and B panels in its L2.
+//    Tiles go round-robin to the XCDs, so each gets an equal share of every group whatever
+//    the groups' K extents, rastered within a group.
 //  * Per K block the tile needs 128 K rows of BM bytes of A and of BN bytes of B.  They are
 //    staged whole by direct-to-LDS buffer copies (1 KB per wave instruction), two blocks
 //    ahead, into three slots: block j+2 refills block j-1's slot, which every wave has left
@@ -84,12 +84,12 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
     const int wm = (wave / WN) * TM, wn = (wave % WN) * TN;
     const int M = p.m, N = p.n;
 
-    // ---- the tile: XCD x (workgroups x, x+8, ...) owns a contiguous range of tile ids
-    int t;
-    {
-        const int G = gridDim.x, q = G >> 3, r = G & 7, x = blockIdx.x & 7;
-        t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (blockIdx.x >> 3);
-    }
+    // ---- the tile: workgroup ids go round-robin over the 8 XCDs, so XCD x runs tiles x, x+8,
+    // ...: an eighth of every group.  (Contiguous ranges per XCD would keep more panel reuse in
+    // each L2, but groups differ in K, and a range would give one XCD the largest group's
+    // tiles.)  Within a group the raster keeps the tiles in flight on one XCD on the same
+    // rows of M.
+    const int t = blockIdx.x;
     const int per_g = tiles_m * tiles_n;
     const int g = t / per_g;
     int tm, tn;
