@@ -201,3 +201,21 @@ def k_grouped_tn(a, sfa, b, sfb, ks, c=None) -> np.ndarray:
     if c is not None:
         d += _c(c, np.float32).astype(np.float64)
     return d
+
+
+# ---------------------------------------------------------------------------------------------
+# The other dense memory layouts (pt.news.hada.io, "Interface GEMM e restrições de layout": the
+# NT, TN, NN and TT layouts of D = C + A @ B; "GEMM denso e grouped": fp8_gemm_{nt, nn, tn, tt}).
+# The first letter is A's storage, the second B's: "n" for A is [M, K] and "t" is [K, M]; "t"
+# for B is [N, K] (B given transposed, as in NT) and "n" is [K, N].  The scales keep the NT
+# layouts (sfa [K/128, ld] one per 1x128 segment of a row of A, sfb [ceil(N/128), K/128] one
+# per 128x128 block of B): only where the bytes sit changes, so the result is the NT
+# definition of the same mathematical A [M, K] and B^T [N, K].
+
+def fp8_gemm_layout(layout: str, a, sfa, b, sfb, c=None) -> np.ndarray:
+    """D = C + A @ B for ``layout`` in {"nt", "nn", "tn", "tt"} (storage as described above)."""
+    if layout not in ("nt", "nn", "tn", "tt"):
+        raise ValueError(f"oracle: unknown layout {layout!r}")
+    a_mk = np.asarray(a) if layout[0] == "n" else np.asarray(a).T
+    b_nk = np.asarray(b) if layout[1] == "t" else np.asarray(b).T
+    return fp8_gemm_nt(np.ascontiguousarray(a_mk), sfa, np.ascontiguousarray(b_nk), sfb, c)

@@ -305,3 +305,41 @@ def test_planted_faults_fail_grouped():
 
 def test_violation_mask_counts_nan():
     assert tol_violations(np.array([np.nan]), np.array([1.0])).all()
+
+
+# ---------------------------------------------------------------- other dense layouts
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+def test_layouts_with_unit_scales_equal_numpy_matmul(layout):
+    # with unit scales and no C, D = dec(A) @ dec(B) in the layout's own storage, computed by
+    # numpy's matmul on the stored arrays (their transposes taken as the layout says)
+    p = W.stored_layout(W.make_dense(48, 64, 256, seed=30), layout)
+    sfa = np.ones_like(p.sfa)
+    sfb = np.ones_like(p.sfb)
+    da, db = torch_decode(p.a), torch_decode(p.b)
+    a_math = da if layout[0] == "n" else da.T          # [M, K]
+    b_math = db.T if layout[1] == "t" else db          # [K, N]
+    want = a_math @ b_math
+    got = oracle.fp8_gemm_layout(layout, p.a, sfa, p.b, sfb)
+    assert np.allclose(got, want, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_layouts_match_rational_brute_force(layout):
+    q = W.make_dense(3, 16, 256, seed=31, with_c=True, stress=True)
+    p = W.stored_layout(q, layout)
+    got = oracle.fp8_gemm_layout(layout, p.a, p.sfa, p.b, p.sfb, p.c)
+    exact = _fraction_gemm(q.a, q.sfa, q.b, q.sfb, q.c)    # the NT storage of the same problem
+    for i in range(got.shape[0]):
+        for j in range(got.shape[1]):
+            e = exact[i, j]
+            assert abs(Fraction(float(got[i, j])) - e) <= abs(e) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 300)
+
+
+def test_layout_storage_is_transposed_bytes():
+    q = W.make_dense(32, 48, 256, seed=32)
+    p = W.stored_layout(q, "tn")
+    assert p.a.shape == (256, 32) and p.b.shape == (256, 48)
+    assert np.array_equal(p.a, q.a.T) and np.array_equal(p.b, q.b.T)
+    with pytest.raises(ValueError):
+        oracle.fp8_gemm_layout("xx", q.a, q.sfa, q.b, q.sfb)

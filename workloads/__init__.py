@@ -167,6 +167,15 @@ def make_dense(m: int, n: int, k: int, seed: int = 0, with_c: bool = False,
     return Dense(a=a, sfa=sfa, b=b, sfb=sb, c=c, m=m, n=n, k=k)
 
 
+def stored_layout(p: "Dense", layout: str) -> "Dense":
+    """The same problem with A and B stored as ``layout`` ("nt", "nn", "tn" or "tt"; first
+    letter A: "n" = [M, K], "t" = [K, M]; second letter B: "t" = [N, K], "n" = [K, N]).  The
+    scales keep their layouts."""
+    a = p.a if layout[0] == "n" else np.ascontiguousarray(p.a.T)
+    b = p.b if layout[1] == "t" else np.ascontiguousarray(p.b.T)
+    return dataclasses.replace(p, a=a, b=b)
+
+
 @dataclasses.dataclass
 class Contiguous:
     a: np.ndarray            # [M_total, K]
