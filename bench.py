@@ -145,16 +145,18 @@ def _scale_words(k, ue8m0):
     return (kb + 3) // 4 if ue8m0 else kb
 
 
-def make_dense_case(torch, dg, W, name, ue8m0=False):
+def make_dense_case(torch, dg, W, name, ue8m0=False, layout="nt"):
     p = W.make_config(name, seed=0, ue8m0=ue8m0)
-    c = Case(name + ("_ue8m0" if ue8m0 else ""))
+    if layout != "nt":
+        p = W.stored_layout(p, layout)
+    c = Case(name + ("_ue8m0" if ue8m0 else "") + ("" if layout == "nt" else "_" + layout))
     t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
              c=None if p.c is None else _dev(torch, p.c),
              d=torch.empty(p.m, p.n, dtype=torch.bfloat16, device="cuda"))
     kb, nb = _scale_words(p.k, ue8m0), (p.n + 127) // 128
     nbytes = (p.m * p.k + p.n * p.k + 4 * p.m * kb + 4 * nb * kb + 2 * p.m * p.n
               + (4 * p.m * p.n if p.c is not None else 0))
-    fn = dg.fp8_gemm_nt_ue8m0 if ue8m0 else dg.fp8_gemm_nt
+    fn = dg.fp8_gemm_nt_ue8m0 if ue8m0 else getattr(dg, "fp8_gemm_" + layout)
     c.sets = _copies(torch, t, nbytes)
     per_graph = _steps_per_graph(len(c.sets))
 
@@ -163,7 +165,7 @@ def make_dense_case(torch, dg, W, name, ue8m0=False):
 
     _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
     c.config = dict(workload=c.name, m=p.m, n=p.n, k=p.k, c="fp32" if p.c is not None else None,
-                    scales="ue8m0" if ue8m0 else "fp32",
+                    scales="ue8m0" if ue8m0 else "fp32", layout=layout,
                     d="bf16", launched_as=f"captured graph replay, {c.cycle} steps per graph",
                     rotating_copies=len(c.sets))
     c.flops = lambda i: 2.0 * p.m * p.n * p.k
@@ -399,7 +401,8 @@ def main():
     ap.add_argument("--workload", default="dense_prefill",
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
                              "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
-                             "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad"])
+                             "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad",
+                             "dense_prefill_nn", "dense_prefill_tn", "dense_prefill_tt"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -434,6 +437,9 @@ def main():
         "moe_contiguous_ue8m0": lambda: make_contiguous_case(torch, dg, W, True),
         "moe_masked_ue8m0": lambda: make_masked_case(torch, dg, W, True),
         "moe_wgrad": lambda: make_kgrouped_case(torch, dg, W),
+        "dense_prefill_nn": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="nn"),
+        "dense_prefill_tn": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tn"),
+        "dense_prefill_tt": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tt"),
     }
     order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
     results = {}

@@ -131,6 +131,24 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int
                                           int n, int k, int expected_m, void *stream);
 
 /*
+ * The other dense memory layouts of the same GEMM (pt.news.hada.io, "Interface GEMM e
+ * restrições de layout": NT, TN, NN and TT; "GEMM denso e grouped": fp8_gemm_{nt, nn, tn, tt}).
+ * The first letter is A's storage, the second B's:
+ *   A "n": e4m3 [m][k] (as in dg_fp8_gemm_nt)    A "t": e4m3 [k][m] (M contiguous)
+ *   B "t": e4m3 [n][k] (as in dg_fp8_gemm_nt)    B "n": e4m3 [k][n] (N contiguous)
+ * The mathematical operation, the scales (sfa MN-major [k/128][ld_sfa], 1x128 segments of A's
+ * rows; sfb [ceil(n/128)][k/128], 128x128 blocks of B), C, D and the error behaviour are those
+ * of dg_fp8_gemm_nt.  In addition: sfa 16-byte aligned, m % 16 == 0 when A is stored [k][m],
+ * and k * max(m, n) < 2^31.
+ */
+int dg_fp8_gemm_nn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
+int dg_fp8_gemm_tn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
+int dg_fp8_gemm_tt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
+
+/*
  * K-grouped TN GEMM, the MoE weight gradient (pt.news.hada.io, "GEMM denso e grouped": an API
  * grouped on the K axis for the backward pass of MoE weights, M and N fixed;
  * "Interface GEMM e restrições de layout": D = C + A @ B, the TN memory layout).  For each

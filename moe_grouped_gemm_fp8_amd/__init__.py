@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt",
     "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "m_grouped_fp8_gemm_nt_masked_ue8m0", "k_grouped_fp8_gemm_tn_contiguous",
     "get_mk_alignment_for_contiguous_layout", "get_sf_aligned_m", "set_num_cus", "get_num_cus",
@@ -61,6 +62,9 @@ def _load():
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_masked.restype = i32
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        getattr(lib, name).argtypes = lib.dg_fp8_gemm_nt.argtypes
+        getattr(lib, name).restype = i32
     for name in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous",
                  "dg_m_grouped_fp8_gemm_nt_masked"):
         fn = getattr(lib, name + "_ue8m0")
@@ -115,12 +119,12 @@ def _scale_spec(k: int, ue8m0: bool):
     return (torch.int32, (kb + 3) // 4, "ceil(K/512)") if ue8m0 else (torch.float32, kb, "K/128")
 
 
-def _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, ue8m0):
+def _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, ue8m0, layout="nt"):
     pa = _dev(a, "a", _FP8_DTYPES, 2)
-    m, k = a.shape
+    m, k = a.shape if layout[0] == "n" else (a.shape[1], a.shape[0])
     pb = _dev(b, "b", _FP8_DTYPES, 2)
-    n = b.shape[0]
-    _need(b.shape[1] == k, "a and b disagree on K")
+    n, kb_ = b.shape if layout[1] == "t" else (b.shape[1], b.shape[0])
+    _need(kb_ == k, "a and b disagree on K")
     _need(k % 128 == 0, "K must be a multiple of 128")
     sdt, ks, kname = _scale_spec(k, ue8m0)
     psfa = _dev(sfa, "sfa", sdt, 2)
@@ -134,7 +138,7 @@ def _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, ue8m0):
         pc = _dev(c, "c", torch.float32, 2)
         _need(tuple(c.shape) == (m, n), "c must be [M, N]")
     lib = _load()
-    fn = lib.dg_fp8_gemm_nt_ue8m0 if ue8m0 else lib.dg_fp8_gemm_nt
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if ue8m0 else getattr(lib, "dg_fp8_gemm_" + layout)
     _check(fn(pa, psfa, sfa.shape[1], pb, psfb, pc, pd, m, n, k, _stream(stream)))
     return d
 
@@ -143,6 +147,21 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None
     """D = C + A @ B.T.  a [M,K] e4m3, sfa [K/128, ld>=M] f32, b [N,K] e4m3,
     sfb [ceil(N/128), K/128] f32, d [M,N] bf16 (written), c [M,N] f32 or None."""
     return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False)
+
+
+def fp8_gemm_nn(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """D = C + A @ B with A [M, K] and B stored [K, N]; scales, C and D as in fp8_gemm_nt."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False, "nn")
+
+
+def fp8_gemm_tn(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """D = C + A @ B with A stored [K, M] and B stored [K, N]; as fp8_gemm_nt otherwise."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False, "tn")
+
+
+def fp8_gemm_tt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """D = C + A @ B.T with A stored [K, M] and B [N, K]; as fp8_gemm_nt otherwise."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False, "tt")
 
 
 def fp8_gemm_nt_ue8m0(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):

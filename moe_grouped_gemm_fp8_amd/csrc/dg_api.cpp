@@ -184,6 +184,46 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 
 
 
+// The dense NN, TN and TT layouts (operands stored MN-major on one or both sides).
+int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m, n, k);
+    if (rc != DG_OK)
+        return rc;
+    if (m == 0)
+        return ok();  // empty problem: nothing to write
+    const bool a_mn = layout == dg::LAYOUT_TN || layout == dg::LAYOUT_TT;
+    if (a_mn && m % 16 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "m=%d must be a multiple of 16 when A is stored [K, M]",
+                    m);
+    if ((int64_t)k * (m > n ? m : n) > 0x7fffffffLL)
+        return fail(DG_ERR_UNSUPPORTED, "k * max(m, n) exceeds 2^31 bytes");
+    if (!aligned(sfa, 16))
+        return fail(DG_ERR_MISALIGNED, "sfa must be 16-byte aligned");
+    if (c && !aligned(c, 16))
+        return fail(DG_ERR_MISALIGNED, "C must be 16-byte aligned");
+    if (c && (const void *)c == d)
+        return fail(DG_ERR_INVALID_ARG, "C and D must not alias");
+    dg::LayoutArgs args;
+    memset(&args, 0, sizeof(args));
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.ld_sfa = ld_sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.c = c;
+    args.d = d;
+    args.m = m;
+    args.n = n;
+    args.k = k;
+    args.num_groups = 1;
+    hipError_t e = dg::launch_layout(layout, args, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 // The three forms, for either scale format (UE8M0: the scale pointers hold int32 words).
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
             const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
@@ -393,6 +433,24 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_
                           k, expected_m, stream);
 }
 
+int dg_fp8_gemm_nn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    return gemm_layout(dg::LAYOUT_NN, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream);
+}
+
+int dg_fp8_gemm_tn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    return gemm_layout(dg::LAYOUT_TN, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream);
+}
+
+int dg_fp8_gemm_tt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                   const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+{
+    return gemm_layout(dg::LAYOUT_TT, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream);
+}
+
 // UE8M0 scales: int32 words of four biased exponents, 4-byte elements like the FP32 scales
 int dg_fp8_gemm_nt_ue8m0(const void *a, const int32_t *sfa, int64_t ld_sfa, const void *b,
                          const int32_t *sfb, const float *c, void *d, int m, int n, int k,
@@ -455,17 +513,18 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const v
         if (cb < db + d_bytes && db < cb + d_bytes)
             return fail(DG_ERR_INVALID_ARG, "C overlaps D without being D");
     }
-    dg::KGroupedArgs args;
+    dg::LayoutArgs args;
     memset(&args, 0, sizeof(args));
     args.a = (const uint8_t *)a;
     args.sfa = sfa;
+    args.ld_sfa = m;
     args.b = (const uint8_t *)b;
     args.sfb = sfb;
     args.c = c;
     args.d = d;
     args.m = m;
     args.n = n;
-    args.k_total = k_total;
+    args.k = k_total;
     args.num_groups = num_groups;
     int64_t kb = 0;
     for (int g = 0; g < num_groups; ++g) {
@@ -479,7 +538,7 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const v
         return fail(DG_ERR_INVALID_ARG, "the group extents sum to %lld, not k_total=%d",
                     (long long)(kb * 128), k_total);
     args.kb_start[num_groups] = (int)kb;
-    hipError_t e = dg::launch_kgrouped(args, (hipStream_t)stream);
+    hipError_t e = dg::launch_layout(dg::LAYOUT_KGROUPED_TN, args, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -61,26 +61,29 @@ struct GemmArgs {
     int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
 };
 
-// K-grouped TN form (MoE weight gradient): D[g] (FP32 [M, N]) = C[g] + the product over group
-// g's run of K.  A is stored [K_total, M] and B [K_total, N] (token-major), sfa [K_total/128, M]
-// and sfb [K_total/128, N] hold one FP32 scale per 128-deep K block per column, and group g
-// covers K blocks kb_start[g] .. kb_start[g+1]-1.  The group table travels in the kernel
-// arguments, so a launch needs no device copy of it (and can be captured in a graph).
+// The MN-major-operand kernel (dg_kgrouped.hip): the dense NN, TN and TT layouts (A stored
+// [M, K] or [K, M], B [N, K] or [K, N], the NT scale layouts, bf16 D, optional FP32 C) and the
+// K-grouped TN form (MoE weight gradient: A [K_total, M], B [K_total, N], one FP32 scale per
+// 128-deep K block per column for both, FP32 D[g] = C[g] + ..., group g covering K blocks
+// kb_start[g] .. kb_start[g+1]-1).  The group table travels in the kernel arguments, so a
+// launch needs no device copy of it (and can be captured in a graph).
+enum Layout : int { LAYOUT_NT = 0, LAYOUT_NN = 1, LAYOUT_TN = 2, LAYOUT_TT = 3, LAYOUT_KGROUPED_TN = 4 };
 constexpr int KG_MAX_GROUPS = 256;
-struct KGroupedArgs {
+struct LayoutArgs {
     const uint8_t *a;
     const float *sfa;
+    int64_t ld_sfa;  // K-grouped: m
     const uint8_t *b;
     const float *sfb;
-    const float *c;  // may be null, or equal to d (accumulate in place)
-    float *d;
-    int m, n, k_total, num_groups;
+    const float *c;  // may be null; K-grouped: may also equal d (accumulate in place)
+    void *d;         // bf16 (dense) or FP32 (K-grouped)
+    int m, n, k;     // K-grouped: k = K_total
+    int num_groups;  // dense: 1
     int kb_start[KG_MAX_GROUPS + 1];
 };
 
-// Workgroups of the K-grouped launch (one per tile of every group) and the launch itself.
-int64_t kgrouped_grid_size(const KGroupedArgs &args);
-hipError_t launch_kgrouped(const KGroupedArgs &args, hipStream_t stream);
+int64_t layout_grid_size(const LayoutArgs &args);
+hipError_t launch_layout(int layout, const LayoutArgs &args, hipStream_t stream);
 
 // Grid size in workgroups for a launch (host-side, no HIP call).
 int64_t grid_size(int mode, int cfg, const GemmArgs &args);

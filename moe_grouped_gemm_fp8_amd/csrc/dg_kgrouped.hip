@@ -1,28 +1,38 @@
-// K-grouped TN form of the fine-grained-scaled FP8 GEMM, the MoE weight gradient
-// (pt.news.hada.io, "GEMM denso e grouped": grouping on the K axis for the backward pass of
-// MoE weights, M and N fixed; "Interface GEMM e restrições de layout": D = C + A @ B, the TN
-// memory layout).  For each group g, over its run of K (the expert's tokens):
-//     D[g, m, n] = C[g, m, n] + sum over its K blocks kb of
-//                  sfa[kb, m] * sfb[kb, n] * sum_{k in kb} A[k, m] * B[k, n]
-// A is stored [K_total, M] and B [K_total, N] (both token-major), D and C are FP32 [G, M, N].
+// The FP8 GEMM for operands stored MN-major (pt.news.hada.io, "Interface GEMM e restrições
+// de layout": D = C + A @ B in the NT, TN, NN and TT memory layouts; "GEMM denso e grouped":
+// fp8_gemm_{nt, nn, tn, tt} and the K-grouped k_grouped_fp8_gemm_tn_contiguous for the
+// backward pass of MoE weights).  One kernel template covers
+//  * the dense NN, TN and TT layouts: A stored [M, K] ("n") or [K, M] ("t"), B stored [N, K]
+//    ("t") or [K, N] ("n"), the NT scale layouts (1x128 A segments, 128x128 B blocks), bf16 D
+//    and an optional FP32 C;
+//  * the K-grouped TN form (the MoE weight gradient): A [K_total, M] and B [K_total, N]
+//    token-major, group g a run of K, one FP32 scale per 128-deep K block per column for
+//    both operands, FP32 D[g] = C[g] + ..., C optional or D itself:
+//        D[g, m, n] = C[g, m, n] + sum over its K blocks kb of
+//                     sfa[kb, m] * sfb[kb, n] * sum_{k in kb} A[k, m] * B[k, n]
+// (the NT layout has its own, more deeply pipelined kernels).
 //
 // Design:
-//  * One workgroup per 128 x 128 tile of one group; eight waves (2 x 4), wave tile 64 x 32.
-//    Tiles go round-robin to the XCDs, so each gets an equal share of every group whatever
-//    the groups' K extents, rastered within a group.
-//  * Per K block the tile needs 128 K rows of BM bytes of A and of BN bytes of B.  They are
-//    staged whole by direct-to-LDS buffer copies (1 KB per wave instruction), two blocks
-//    ahead, into three slots: block j+2 refills block j-1's slot, which every wave has left
-//    once it is past block j-1's end barrier, so one barrier per block suffices.
-//  * The LDS rows are K indices.  An MFMA operand lane needs 32 consecutive K values of one
-//    column; ds_read_b64_tr_b8 delivers 8 of them per read (see dg_device.h), so a 16-column
-//    fragment is four transposing reads.  16-byte chunk c of row k sits at chunk c ^ s(k),
-//    with s chosen so that the 16 rows one half-wave reads land on distinct banks.
+//  * One workgroup per 128 x 128 tile (of one group); eight waves (2 x 4), wave tile 64 x 32.
+//    Dense tiles go to the XCDs in contiguous ranges (neighbours share A and B panels in an
+//    XCD's L2); K-grouped tiles go round-robin, so each XCD gets an equal share of every group
+//    whatever the groups' K extents (contiguous ranges gave one XCD the largest group).
+//  * Per K block a tile needs 128 x BM bytes of A and 128 x BN bytes of B.  They are staged
+//    whole by direct-to-LDS buffer copies (1 KB per wave instruction), two blocks ahead, into
+//    three slots: block j+2 refills block j-1's slot, which every wave has left once it is
+//    past block j-1's end barrier, so one barrier per block suffices.
+//  * A K-major operand's LDS rows are its rows (128 bytes of K each), read as two
+//    ds_read_b128 per MFMA operand lane, as in the NT kernels.  An MN-major operand's LDS
+//    rows are K indices; ds_read_b64_tr_b8 gives a lane 8 consecutive K values of one column
+//    (see dg_device.h), so an operand lane is four transposing reads.  Both use 16-byte chunk
+//    swizzles that keep the reads free of bank conflicts.
 //  * v_mfma_f32_16x16x128_f8f6f4 as in the NT kernels (D^T = B A^T: a lane holds 4
 //    consecutive N columns of one M row); each block's partial is promoted into the FP32
-//    accumulators with sa[m] * sb[n] (one A scale per lane, four B scales per lane).
-//  * Epilogue: + C (read before D is written, so C may be D itself), FP32 non-temporal
-//    stores of the valid rows and columns.  A group with no K blocks writes C (or zeros).
+//    accumulators with sa[m] * sb (one B scale per tile and block in the dense forms, four
+//    per lane in the K-grouped form).
+//  * Epilogue: + C, then bf16 (dense) or FP32 non-temporal (K-grouped; C read before D is
+//    written, so C may be D) stores of the valid rows and columns.  A group with no K blocks
+//    writes C, or zeros.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,18 +57,73 @@ __device__ __forceinline__ int kswz(int k)
         return (k & 7) | ((k >> 2) & 8);
 }
 
+// chunk swizzle of a K-major operand's LDS row r (8 chunks of 16 bytes): r3 | r1 << 1 | r2 << 2,
+// the one the NT kernels use
+__device__ __forceinline__ int hswz(int r) { return ((r >> 3) & 1) | (r & 2) | (((r >> 2) & 1) << 2); }
+
+// One MFMA operand lane's 32 bytes: four transposing reads (MN-major) or two 16-byte reads
+// (K-major).  Valid after lds_wait() and tie().
+template <bool MN>
+struct Frag;
+template <>
+struct Frag<true> {
+    v2i q[4];
+    __device__ __forceinline__ v8i op() const
+    {
+        return v8i{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
+    }
+    __device__ __forceinline__ void tie_all()
+    {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            tie(q[r]);
+    }
+};
+template <>
+struct Frag<false> {
+    v4i h[2];
+    __device__ __forceinline__ v8i op() const
+    {
+        return v8i{h[0].x, h[0].y, h[0].z, h[0].w, h[1].x, h[1].y, h[1].z, h[1].w};
+    }
+    __device__ __forceinline__ void tie_all()
+    {
+        tie(h[0]);
+        tie(h[1]);
+    }
+};
+
+// reads the operand lane of sub-tile S (16 rows or columns) from a slot: MN-major from the
+// lane's row base `lo` (read r adds K row offset 8 r), K-major from its two chunks `lo`, `hi`
+template <bool MN, int R, int S>
+__device__ __forceinline__ void read_frag(Frag<MN> &f, uint32_t lo, uint32_t hi)
+{
+    if constexpr (MN) {
+        f.q[0] = lds_read_tr8_at<0 * 8 * R>(lo);
+        f.q[1] = lds_read_tr8_at<1 * 8 * R>(lo);
+        f.q[2] = lds_read_tr8_at<2 * 8 * R>(lo);
+        f.q[3] = lds_read_tr8_at<3 * 8 * R>(lo);
+    } else {
+        f.h[0] = lds_read16_at<S * 16 * KBLK>(lo);
+        f.h[1] = lds_read16_at<S * 16 * KBLK>(hi);
+    }
+}
+
 }  // namespace
 
+// KG: the K-grouped form; else dense.  A_MN / B_MN: the operand is stored MN-major.
 // (the body is a device function: generic lambdas directly in a kernel template keep the host
 // pass from emitting its launch stub)
-template <int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m, int tiles_n)
+template <int BM, int BN, int WM, int WN, bool A_MN, bool B_MN, bool KG>
+__device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, int tiles_n)
 {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
     constexpr int CHA = BM / 16, CHB = BN / 16;
-    static_assert((CHA == 8 || CHA == 16) && (CHB == 8 || CHB == 16), "rows of 128 or 256 B");
+    static_assert(!A_MN || CHA == 8 || CHA == 16, "MN-major A rows of 128 or 256 bytes");
+    static_assert(!B_MN || CHB == 8 || CHB == 16, "MN-major B rows of 128 or 256 bytes");
+    static_assert(KG || BN == KBLK, "dense tiles span one 128-column B scale block");
     static_assert(SM % 2 == 0, "partials alternate between two register sets");
     constexpr int A_SLOT = KBLK * BM, B_SLOT = KBLK * BN;
     constexpr int S_SLOT = 1024;  // a block's BM (or BN) scales, 16 bytes per lane of one copy
@@ -71,7 +136,6 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
     constexpr int IA = A_SLOT / 1024, IB = B_SLOT / 1024;  // 1 KB copies per block
     static_assert(IA % NW == 0 && IB % NW == 0, "copies must split evenly over the waves");
     constexpr int CA = IA / NW, CB = IB / NW, MAXI = CA + CB;
-    constexpr int RA = 1024 / BM, RB = 1024 / BN;  // K rows per copy
     static_assert(2 * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
@@ -82,68 +146,111 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave / WN) * TM, wn = (wave % WN) * TN;
-    const int M = p.m, N = p.n;
+    const int M = p.m, N = p.n, K = p.k;
+    const int64_t ld = p.ld_sfa;
+    const int KBT = K / KBLK;  // K blocks of the whole K axis (all groups)
 
-    // ---- the tile: workgroup ids go round-robin over the 8 XCDs, so XCD x runs tiles x, x+8,
-    // ...: an eighth of every group.  (Contiguous ranges per XCD would keep more panel reuse in
-    // each L2, but groups differ in K, and a range would give one XCD the largest group's
-    // tiles.)  Within a group the raster keeps the tiles in flight on one XCD on the same
-    // rows of M.
-    const int t = blockIdx.x;
+    // ---- the tile.  Workgroup ids go round-robin over the 8 XCDs.  Dense: XCD x owns a
+    // contiguous range of tile ids; K-grouped: XCD x takes tiles x, x+8, ... (an eighth of every
+    // group).  Within a group the raster keeps neighbouring tiles on shared rows of M.
+    int t;
+    if constexpr (KG) {
+        t = blockIdx.x;
+    } else {
+        const int G = gridDim.x, q = G >> 3, r = G & 7, x = blockIdx.x & 7;
+        t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (blockIdx.x >> 3);
+    }
     const int per_g = tiles_m * tiles_n;
-    const int g = t / per_g;
+    const int g = KG ? t / per_g : 0;
     int tm, tn;
     raster(t - g * per_g, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kb_first = p.kb_start[g];
-    const int nkb = p.kb_start[g + 1] - kb_first;
-    const int KBT = p.k_total / KBLK;
+    const int kb_first = KG ? p.kb_start[g] : 0;
+    const int nkb = KG ? p.kb_start[g + 1] - kb_first : KBT;
 
-    // ---- copies.  Copy ci of a block (ci = wave + c * NW) holds K rows [R ci, R ci + R); lane
-    // l writes bytes [16 l, 16 l + 16) of it, i.e. row R ci + l / CH, physical chunk l % CH,
-    // which must hold logical chunk (l % CH) ^ s(row): the lane fetches that one.
+    // ---- copies.  Copy ci of a block is wave + c * NW; lane l writes bytes [16 l, 16 l + 16)
+    // of its 1 KB.  MN-major: LDS row = K index (R = 1024 / width rows per copy), row
+    // R ci + l / CH, physical chunk l % CH holding logical chunk (l % CH) ^ s(row).  K-major:
+    // LDS row = operand row (8 per copy), row 8 ci + l / 8, physical chunk l % 8 holding
+    // logical chunk (l % 8) ^ h(row).  The lane fetches the logical chunk.
+    auto lane_off = [&](auto MN, auto CH, int ci, int pitch) -> uint32_t {
+        if constexpr (decltype(MN)::value) {
+            constexpr int ch = decltype(CH)::value;
+            const int k = (1024 / (16 * ch)) * ci + lane / ch;
+            return (uint32_t)(k * pitch + 16 * ((lane % ch) ^ kswz<ch>(k)));
+        } else {
+            const int r = 8 * ci + (lane >> 3);
+            return (uint32_t)(r * pitch + 16 * ((lane & 7) ^ hswz(r)));
+        }
+    };
+    constexpr auto A_MNc = std::integral_constant<bool, A_MN>{};
+    constexpr auto B_MNc = std::integral_constant<bool, B_MN>{};
+    constexpr auto CHAc = std::integral_constant<int, CHA>{};
+    constexpr auto CHBc = std::integral_constant<int, CHB>{};
     uint32_t voa[CA], vob[CB];
 #pragma unroll
-    for (int c = 0; c < CA; ++c) {
-        const int k = RA * (wave + c * NW) + lane / CHA;
-        voa[c] = (uint32_t)(k * M + 16 * ((lane % CHA) ^ kswz<CHA>(k)));
-    }
+    for (int c = 0; c < CA; ++c)
+        voa[c] = lane_off(A_MNc, CHAc, wave + c * NW, A_MN ? M : K);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-        const int k = RB * (wave + c * NW) + lane / CHB;
-        vob[c] = (uint32_t)(k * N + 16 * ((lane % CHB) ^ kswz<CHB>(k)));
-    }
-    // block j of the group into slot s; blocks past the group's last read empty resources
-    // (zeros, no memory access), which keeps the count of copies per block constant
+    for (int c = 0; c < CB; ++c)
+        vob[c] = lane_off(B_MNc, CHBc, wave + c * NW, B_MN ? N : K);
+    // block j of the tile's K run into slot s; blocks past the last read empty resources
+    // (zeros, no memory access), which keeps the count of copies per block constant.  Every
+    // resource ends at the last valid byte of its operand (rows past M or N read zeros).
     auto issue_block = [&](int j, int s) {
         const bool in = j < nkb;
         const int kb = kb_first + (in ? j : 0);
         const int64_t ka = (int64_t)kb * KBLK;
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(p.a + ka * M + m0, in ? ((int64_t)p.k_total - ka) * M - m0 : 0);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(p.b + ka * N + n0, in ? ((int64_t)p.k_total - ka) * N - n0 : 0);
+        __amdgpu_buffer_rsrc_t ra, rb;
+        uint32_t soa = 0, sob = 0;
+        if constexpr (A_MN) {
+            ra = make_rsrc(p.a + ka * M + m0, in ? ((int64_t)K - ka) * M - m0 : 0);
+        } else {
+            ra = make_rsrc(p.a + (int64_t)m0 * K, in ? (int64_t)(M - m0) * K : 0);
+            soa = (uint32_t)ka;
+        }
+        if constexpr (B_MN) {
+            rb = make_rsrc(p.b + ka * N + n0, in ? ((int64_t)K - ka) * N - n0 : 0);
+        } else {
+            rb = make_rsrc(p.b + (int64_t)n0 * K, in ? (int64_t)(N - n0) * K : 0);
+            sob = (uint32_t)ka;
+        }
 #pragma unroll
         for (int c = 0; c < CA; ++c)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (DG_LDS void *)(ldsp + s * A_SLOT + (wave + c * NW) * 1024), 16, voa[c], 0,
+                ra, (DG_LDS void *)(ldsp + s * A_SLOT + (wave + c * NW) * 1024), 16, voa[c], soa,
                 0, 0);
 #pragma unroll
         for (int c = 0; c < CB; ++c)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (DG_LDS void *)(ldsp + B_BASE + s * B_SLOT + (wave + c * NW) * 1024), 16,
-                vob[c], 0, 0, 0);
+                vob[c], sob, 0, 0);
         if (wave == 0) {
+            // A scales: row kb of the MN-major [K/128][ld] array, the tile's BM columns.  B
+            // scales: K-grouped, row kb of [K/128][N]; dense, the tile's 128x128 block
+            // [n0/128][kb] (lane 0's word; the others read on along the row)
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-                p.sfa + (int64_t)kb * M + m0, in ? ((int64_t)(KBT - kb) * M - m0) * 4 : 0);
-            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
-                p.sfb + (int64_t)kb * N + n0, in ? ((int64_t)(KBT - kb) * N - n0) * 4 : 0);
+                p.sfa + (int64_t)kb * ld + m0, in ? ((int64_t)(KBT - kb) * ld - m0) * 4 : 0);
+            __amdgpu_buffer_rsrc_t rsb;
+            if constexpr (KG) {
+                rsb = make_rsrc(p.sfb + (int64_t)kb * N + n0,
+                                in ? ((int64_t)(KBT - kb) * N - n0) * 4 : 0);
+            } else {
+                const int nb = n0 / KBLK, NB = (N + KBLK - 1) / KBLK;
+                rsb = make_rsrc(p.sfb + (int64_t)nb * KBT + kb,
+                                in ? ((int64_t)(NB - nb) * KBT - kb) * 4 : 0);
+            }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsa, (DG_LDS void *)(ldsp + SA_BASE + s * S_SLOT), 16, (uint32_t)lane * 16u, 0, 0,
                 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsb, (DG_LDS void *)(ldsp + SB_BASE + s * S_SLOT), 16, (uint32_t)lane * 16u, 0, 0,
-                0);
+            if constexpr (KG)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsb, (DG_LDS void *)(ldsp + SB_BASE + s * S_SLOT), 16, (uint32_t)lane * 16u, 0,
+                    0, 0);
+            else  // (4-byte words: the block's scale need not be 16-byte aligned)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsb, (DG_LDS void *)(ldsp + SB_BASE + s * S_SLOT), 4, (uint32_t)lane * 4u, 0,
+                    0, 0);
         }
     };
     // the next block's copies have landed (only those of the block after it may be in flight)
@@ -154,63 +261,74 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
             wait_vm<MAXI>();
     };
 
-    // ---- fragments.  Lane (fr, fg) reads, for read r, row 32 fg + 8 r + fr / 2 at byte
-    // 8 (fr & 1) of the sub-tile's 16-byte chunk, and receives K rows 32 fg + 8 r .. + 7 of
-    // column fr: the four reads give the 32 K values of its MFMA operand lane.
+    // ---- fragment offsets.  MN-major: lane (fr, fg), read r, addresses K row
+    // 32 fg + 8 r + fr / 2 at byte 8 (fr & 1) of the sub-tile's chunk and receives K rows
+    // 32 fg + 8 r .. + 7 of column fr (r adds 8 r: K row bits 3, 4, which s does not use).
+    // K-major: row fr of the sub-tile, chunks 2 fg and 2 fg + 1.
     const int fr = lane & 15, fg = lane >> 4;
-    const int k_lane = 32 * fg + (fr >> 1);  // r adds 8 r: bits 3, 4, which s does not use
-    uint32_t fa_off[SM], fb_off[SN];
+    auto frag_off = [&](auto MN, auto CH, int w0, int width, bool second) -> uint32_t {
+        if constexpr (decltype(MN)::value) {
+            constexpr int ch = decltype(CH)::value;
+            const int k = 32 * fg + (fr >> 1);
+            return (uint32_t)(k * width + (((w0 >> 4) ^ kswz<ch>(k)) << 4) + 8 * (fr & 1));
+        } else {
+            const int r = w0 + fr;
+            return (uint32_t)(r * KBLK + (((2 * fg + (second ? 1 : 0)) ^ hswz(r)) << 4));
+        }
+    };
+    // MN-major: one base per sub-tile (the swizzle mixes the sub-tile index); K-major: one
+    // pair for all sub-tiles (the sub-tile adds 16 rows, which h does not see)
+    uint32_t fa_lo[A_MN ? SM : 1], fa_hi, fb_lo[B_MN ? SN : 1], fb_hi;
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
-        fa_off[i] = lds_base + (uint32_t)(k_lane * BM + ((((wm >> 4) + i) ^ kswz<CHA>(k_lane)) << 4) +
-                                          8 * (fr & 1));
+    for (int i = 0; i < (A_MN ? SM : 1); ++i)
+        fa_lo[i] = lds_base + frag_off(A_MNc, CHAc, wm + 16 * i, BM, false);
+    fa_hi = lds_base + frag_off(A_MNc, CHAc, wm, BM, true);
 #pragma unroll
-    for (int jj = 0; jj < SN; ++jj)
-        fb_off[jj] = lds_base + B_BASE +
-                     (uint32_t)(k_lane * BN + ((((wn >> 4) + jj) ^ kswz<CHB>(k_lane)) << 4) +
-                                8 * (fr & 1));
+    for (int jj = 0; jj < (B_MN ? SN : 1); ++jj)
+        fb_lo[jj] = lds_base + B_BASE + frag_off(B_MNc, CHBc, wn + 16 * jj, BN, false);
+    fb_hi = lds_base + B_BASE + frag_off(B_MNc, CHBc, wn, BN, true);
     const uint32_t sa_off = lds_base + SA_BASE + (uint32_t)(wm + fr) * 4;
-    const uint32_t sb_off = lds_base + SB_BASE + (uint32_t)(wn + 4 * fg) * 4;
+    const uint32_t sb_off = lds_base + SB_BASE + (KG ? (uint32_t)(wn + 4 * fg) * 4 : 0u);
 
-    v2i fa[2][SM][4], fb[2][SN][4];
+    Frag<A_MN> fa[2][SM];
+    Frag<B_MN> fb[2][SN];
     float fsa[2][SM];
-    v4f fsb[2][SN];
+    v4f fsb[2][KG ? SN : 1];  // K-grouped: the lane's four columns
+    float fsb1[2];            // dense: the tile's B scale
     auto read_frags = [&](auto BUF, int s) {
         constexpr int bf = decltype(BUF)::value;
         const uint32_t ao = (uint32_t)(s * A_SLOT), bo = (uint32_t)(s * B_SLOT);
         const uint32_t so = (uint32_t)(s * S_SLOT);
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            fa[bf][i][0] = lds_read_tr8_at<0 * 8 * BM>(fa_off[i] + ao);
-            fa[bf][i][1] = lds_read_tr8_at<1 * 8 * BM>(fa_off[i] + ao);
-            fa[bf][i][2] = lds_read_tr8_at<2 * 8 * BM>(fa_off[i] + ao);
-            fa[bf][i][3] = lds_read_tr8_at<3 * 8 * BM>(fa_off[i] + ao);
+            read_frag<A_MN, BM, i>(fa[bf][i], fa_lo[A_MN ? i : 0] + ao, fa_hi + ao);
             fsa[bf][i] = lds_read4_at<i * 64>(sa_off + so);
         });
         static_for<SN>([&](auto J) {
             constexpr int jj = decltype(J)::value;
-            fb[bf][jj][0] = lds_read_tr8_at<0 * 8 * BN>(fb_off[jj] + bo);
-            fb[bf][jj][1] = lds_read_tr8_at<1 * 8 * BN>(fb_off[jj] + bo);
-            fb[bf][jj][2] = lds_read_tr8_at<2 * 8 * BN>(fb_off[jj] + bo);
-            fb[bf][jj][3] = lds_read_tr8_at<3 * 8 * BN>(fb_off[jj] + bo);
-            fsb[bf][jj] = lds_read16f_at<jj * 64>(sb_off + so);
+            read_frag<B_MN, BN, jj>(fb[bf][jj], fb_lo[B_MN ? jj : 0] + bo, fb_hi + bo);
+            if constexpr (KG)
+                fsb[bf][jj] = lds_read16f_at<jj * 64>(sb_off + so);
         });
+        if constexpr (!KG)
+            fsb1[bf] = lds_read4_at<0>(sb_off + so);
     };
     auto tie_frags = [&](auto BUF) {
         constexpr int bf = decltype(BUF)::value;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                tie(fa[bf][i][r]);
+            fa[bf][i].tie_all();
             tie(fsa[bf][i]);
         }
 #pragma unroll
-        for (int jj = 0; jj < SN; ++jj) {
+        for (int jj = 0; jj < SN; ++jj)
+            fb[bf][jj].tie_all();
+        if constexpr (KG) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                tie(fb[bf][jj][r]);
-            tie(fsb[bf][jj]);
+            for (int jj = 0; jj < SN; ++jj)
+                tie(fsb[bf][jj]);
+        } else {
+            tie(fsb1[bf]);
         }
     };
 
@@ -224,14 +342,23 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
     v4f pend[2][SN];
     auto promote = [&](auto BUF, auto I) {
         constexpr int bf = decltype(BUF)::value, i = decltype(I)::value;
+        if constexpr (KG) {
 #pragma unroll
-        for (int jj = 0; jj < SN; ++jj) {
-            acc[i][jj] += pend[i % 2][jj] * (fsa[bf][i] * fsb[bf][jj]);
-            asm volatile("" : "+v"(acc[i][jj]));
+            for (int jj = 0; jj < SN; ++jj) {
+                acc[i][jj] += pend[i % 2][jj] * (fsa[bf][i] * fsb[bf][jj]);
+                asm volatile("" : "+v"(acc[i][jj]));
+            }
+        } else {
+            const float sc = fsa[bf][i] * fsb1[bf];
+#pragma unroll
+            for (int jj = 0; jj < SN; ++jj) {
+                acc[i][jj] += pend[i % 2][jj] * sc;
+                asm volatile("" : "+v"(acc[i][jj]));
+            }
         }
     };
 
-    // block j of the group: its fragments are in register set BUF (read, maybe in flight)
+    // block j of the tile's K run: its fragments are in register set BUF (maybe in flight)
     auto do_block = [&](auto BUF, int j) {
         constexpr int bf = decltype(BUF)::value;
         constexpr auto OTHER = std::integral_constant<int, 1 - bf>{};
@@ -240,16 +367,11 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
         tie_frags(BUF);
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            const v8i av = v8i{fa[bf][i][0].x, fa[bf][i][0].y, fa[bf][i][1].x, fa[bf][i][1].y,
-                               fa[bf][i][2].x, fa[bf][i][2].y, fa[bf][i][3].x, fa[bf][i][3].y};
+            const v8i av = fa[bf][i].op();
 #pragma unroll
-            for (int jj = 0; jj < SN; ++jj) {
-                const v8i bv = v8i{fb[bf][jj][0].x, fb[bf][jj][0].y, fb[bf][jj][1].x,
-                                   fb[bf][jj][1].y, fb[bf][jj][2].x, fb[bf][jj][2].y,
-                                   fb[bf][jj][3].x, fb[bf][jj][3].y};
+            for (int jj = 0; jj < SN; ++jj)
                 pend[i % 2][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            }
+                    fb[bf][jj].op(), av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
             if constexpr (i > 0)
                 promote(BUF, std::integral_constant<int, i - 1>{});
         });
@@ -275,12 +397,11 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
         if (j + 1 < nkb)
             do_block(B1, j + 1);
     }
-    // every copy (also those past the group's blocks) has landed before the workgroup ends
+    // every copy (also those past the last block) has landed before the workgroup ends
     wait_vm<0>();
     lds_wait();
 
-    // ---- epilogue: + C, FP32 stores of the valid rows and columns
-    const int64_t gbase = (int64_t)g * M * N;
+    // ---- epilogue: + C, stores of the valid rows and columns
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
         const int m = m0 + wm + 16 * i + fr;
@@ -288,41 +409,66 @@ __device__ __forceinline__ void kgrouped_tile(const KGroupedArgs &p, int tiles_m
         for (int jj = 0; jj < SN; ++jj) {
             const int n = n0 + wn + 16 * jj + 4 * fg;
             if (m < M && n < N) {
-                const int64_t o = gbase + (int64_t)m * N + n;
+                const int64_t o = (int64_t)g * M * N + (int64_t)m * N + n;
                 v4f v = acc[i][jj];
                 if (p.c)
                     v += *reinterpret_cast<const v4f *>(p.c + o);
-                __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(p.d + o));
+                if constexpr (KG)
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4f *>((float *)p.d + o));
+                else
+                    store_bf16x4((uint16_t *)p.d + o, v);
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void dg_kgrouped_kernel(KGroupedArgs p, int tiles_m,
-                                                                    int tiles_n)
+template <int BM, int BN, int WM, int WN, bool A_MN, bool B_MN, bool KG>
+__global__ __launch_bounds__(64 * WM * WN) void dg_layout_kernel(LayoutArgs p, int tiles_m,
+                                                                  int tiles_n)
 {
-    kgrouped_tile<BM, BN, WM, WN>(p, tiles_m, tiles_n);
+    layout_tile<BM, BN, WM, WN, A_MN, B_MN, KG>(p, tiles_m, tiles_n);
 }
 
 namespace {
-constexpr int KG_BM = 128, KG_BN = 128, KG_WM = 2, KG_WN = 4;
+constexpr int LY_BM = 128, LY_BN = 128, LY_WM = 2, LY_WN = 4;
 }
 
-int64_t kgrouped_grid_size(const KGroupedArgs &a)
+int64_t layout_grid_size(const LayoutArgs &a)
 {
-    const int64_t tiles_m = (a.m + KG_BM - 1) / KG_BM, tiles_n = (a.n + KG_BN - 1) / KG_BN;
+    const int64_t tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
     return tiles_m * tiles_n * a.num_groups;
 }
 
-hipError_t launch_kgrouped(const KGroupedArgs &a, hipStream_t stream)
+hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 {
-    const int tiles_m = (a.m + KG_BM - 1) / KG_BM, tiles_n = (a.n + KG_BN - 1) / KG_BN;
-    const int64_t grid = kgrouped_grid_size(a);
+    const int tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
+    const int64_t grid = layout_grid_size(a);
     if (grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dg_kgrouped_kernel<KG_BM, KG_BN, KG_WM, KG_WN>), dim3((unsigned)grid),
-                       dim3(64 * KG_WM * KG_WN), 0, stream, a, tiles_m, tiles_n);
+    const dim3 g((unsigned)grid), b(64 * LY_WM * LY_WN);
+#define DG_LAUNCH_LAYOUT(AMN, BMN, KGR)                                                         \
+    hipLaunchKernelGGL((dg_layout_kernel<LY_BM, LY_BN, LY_WM, LY_WN, AMN, BMN, KGR>), g, b, 0,   \
+                       stream, a, tiles_m, tiles_n)
+    switch (layout) {
+    case LAYOUT_KGROUPED_TN:
+        DG_LAUNCH_LAYOUT(true, true, true);
+        break;
+    case LAYOUT_NN:
+        DG_LAUNCH_LAYOUT(false, true, false);
+        break;
+    case LAYOUT_TN:
+        DG_LAUNCH_LAYOUT(true, true, false);
+        break;
+    case LAYOUT_TT:
+        DG_LAUNCH_LAYOUT(true, false, false);
+        break;
+    case LAYOUT_NT:
+        DG_LAUNCH_LAYOUT(false, false, false);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef DG_LAUNCH_LAYOUT
     return hipGetLastError();
 }
 

@@ -1,0 +1,84 @@
+"""Parity of the dense NN, TN and TT layouts (operands stored MN-major on one or both sides) on
+the GPU with the CPU oracle, on the same seeded inputs: ragged M and N tiles, K-block counts
+around the pipeline depth, extreme scales, N with a partial last B scale block, the full-size
+prefill shape on sampled rows, and the host checks particular to the layouts."""
+import sys
+
+import numpy as np
+import pytest
+
+import moe_grouped_gemm_fp8_amd as dg
+import oracle
+import workloads as W
+from gpu_util import assert_parity, dev, sentinel_like, bits
+import torch
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["nn", "tn", "tt"]
+
+
+def _say(msg):
+    print(f"[layouts] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    _say(f"start {request.node.name}")
+    yield
+
+
+def run(layout, p):
+    d = sentinel_like((p.m, p.n))
+    getattr(dg, "fp8_gemm_" + layout)(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d,
+                                      None if p.c is None else dev(p.c))
+    torch.cuda.synchronize()
+    return bits(d)
+
+
+def ref(layout, p):
+    return oracle.fp8_gemm_layout(layout, p.a, p.sfa, p.b, p.sfb, p.c)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("with_c", [False, True])
+def test_ragged_tiles(layout, with_c):
+    p = W.stored_layout(W.make_dense(208, 336, 640, seed=91, with_c=with_c), layout)
+    assert_parity(run(layout, p), ref(layout, p), f"{layout} c={with_c}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("k", [128, 256, 384, 1152])
+def test_k_blocks(layout, k):
+    p = W.stored_layout(W.make_dense(128, 256, k, seed=92, with_c=True, c_std=2.0), layout)
+    assert_parity(run(layout, p), ref(layout, p), f"{layout} k={k}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_stress_scales_and_partial_b_block(layout):
+    p = W.stored_layout(W.make_dense(64, 2112, 1024, seed=93, stress=True), layout)
+    assert_parity(run(layout, p), ref(layout, p), f"{layout} stress")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_prefill_shape_sampled_rows(layout):
+    q = W.make_config("dense_prefill", seed=0)                   # 4096 x 7168 x 2048 with C
+    p = W.stored_layout(q, layout)
+    got = run(layout, p)
+    assert not np.any(got == W.BF16_SENTINEL), "some outputs were never written"
+    rng = np.random.default_rng(130)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(q.m - 4, q.m),
+                                     rng.choice(q.m, 24, replace=False)]))
+    want = oracle.fp8_gemm_nt(q.a[rows], W.mn_major(q.sfa[:, rows].T), q.b, q.sfb, q.c[rows])
+    assert_parity(got[rows], want, f"{layout} prefill")
+
+
+def test_host_checks_of_the_layouts():
+    p = W.stored_layout(W.make_dense(200, 256, 256, seed=94), "tn")
+    d = sentinel_like((200, 256))
+    with pytest.raises(dg.DGError) as e:
+        dg.fp8_gemm_tn(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d)
+    assert e.value.code == -2                                     # m % 16 with A stored [K, M]
+    q = W.stored_layout(W.make_dense(200, 256, 256, seed=94), "nn")
+    assert_parity(run("nn", q), ref("nn", q), "nn m=200")          # fine with A stored [M, K]
