@@ -82,7 +82,7 @@ struct LayoutArgs {
     int kb_start[KG_MAX_GROUPS + 1];
 };
 
-int64_t layout_grid_size(const LayoutArgs &args);
+int64_t layout_grid_size(int layout, const LayoutArgs &args);
 hipError_t launch_layout(int layout, const LayoutArgs &args, hipStream_t stream);
 
 // Grid size in workgroups for a launch (host-side, no HIP call).

@@ -14,9 +14,10 @@
 //
 // Design:
 //  * One workgroup per 128 x 128 tile (of one group); eight waves (2 x 4), wave tile 64 x 32.
-//    Dense tiles go to the XCDs in contiguous ranges (neighbours share A and B panels in an
-//    XCD's L2); K-grouped tiles go round-robin, so each XCD gets an equal share of every group
-//    whatever the groups' K extents (contiguous ranges gave one XCD the largest group).
+//    Dense tiles go to the XCDs in 8 raster-order chunks (neighbours share A and B panels in
+//    an XCD's L2); K-grouped tiles go round-robin, so each XCD gets an equal share of every
+//    group whatever the groups' K extents (one range over all groups gave one XCD the largest
+//    group's tiles).
 //  * Per K block a tile needs 128 x BM bytes of A and 128 x BN bytes of B.  They are staged
 //    whole by direct-to-LDS buffer copies (1 KB per wave instruction), two blocks ahead, into
 //    three slots: block j+2 refills block j-1's slot, which every wave has left once it is
@@ -150,20 +151,31 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     const int64_t ld = p.ld_sfa;
     const int KBT = K / KBLK;  // K blocks of the whole K axis (all groups)
 
-    // ---- the tile.  Workgroup ids go round-robin over the 8 XCDs.  Dense: XCD x owns a
-    // contiguous range of tile ids; K-grouped: XCD x takes tiles x, x+8, ... (an eighth of every
-    // group).  Within a group the raster keeps neighbouring tiles on shared rows of M.
-    int t;
-    if constexpr (KG) {
-        t = blockIdx.x;
-    } else {
-        const int G = gridDim.x, q = G >> 3, r = G & 7, x = blockIdx.x & 7;
-        t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (blockIdx.x >> 3);
-    }
+    // ---- the tile.  Workgroup ids go round-robin over the 8 XCDs: XCD x runs ids x, x+8, ...
+    // Dense: the tiles, in raster order, are cut into 8 consecutive chunks, and XCD x runs
+    // chunk x, so the tiles in flight on one XCD are raster neighbours (4 rows of M by 8
+    // columns of N) that share A and B panels in its L2; ids past the chunk (when 8 does not
+    // divide the tile count) end at once.  K-grouped: tile id = workgroup id, so every XCD runs
+    // an eighth of every group whatever the groups' K extents.  (Cutting each group into such
+    // chunks fetched 2.7 GB from memory per routed wgrad call instead of 7.6 GB but ran 4%
+    // slower: this kernel is bound inside the CU.)
     const int per_g = tiles_m * tiles_n;
-    const int g = KG ? t / per_g : 0;
+    int g, t;
+    if constexpr (KG) {
+        g = blockIdx.x / per_g;
+        t = blockIdx.x - g * per_g;
+    } else {
+        const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+        const int lo = (x * per_g) >> 3, len = (((x + 1) * per_g) >> 3) - lo;
+        if (len == 0)
+            return;
+        if (i >= len)
+            return;
+        g = 0;
+        t = lo + i;
+    }
     int tm, tn;
-    raster(t - g * per_g, tiles_m, tiles_n, tm, tn);
+    raster(t, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kb_first = KG ? p.kb_start[g] : 0;
     const int nkb = KG ? p.kb_start[g + 1] - kb_first : KBT;
@@ -433,16 +445,21 @@ namespace {
 constexpr int LY_BM = 128, LY_BN = 128, LY_WM = 2, LY_WN = 4;
 }
 
-int64_t layout_grid_size(const LayoutArgs &a)
+int64_t layout_grid_size(int layout, const LayoutArgs &a)
 {
     const int64_t tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
-    return tiles_m * tiles_n * a.num_groups;
+    const int64_t per_g = tiles_m * tiles_n;
+    if (layout == LAYOUT_KGROUPED_TN)
+        return per_g * a.num_groups;  // one workgroup per tile of every group
+    if (per_g > (int64_t)1 << 27)
+        return -1;  // chunk bounds are computed in 32 bits
+    return 8 * ((per_g + 7) / 8);     // 8 XCDs x the longest chunk
 }
 
 hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 {
     const int tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
-    const int64_t grid = layout_grid_size(a);
+    const int64_t grid = layout_grid_size(layout, a);
     if (grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const dim3 g((unsigned)grid), b(64 * LY_WM * LY_WN);
