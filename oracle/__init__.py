@@ -219,3 +219,59 @@ def fp8_gemm_layout(layout: str, a, sfa, b, sfb, c=None) -> np.ndarray:
     a_mk = np.asarray(a) if layout[0] == "n" else np.asarray(a).T
     b_nk = np.asarray(b) if layout[1] == "t" else np.asarray(b).T
     return fp8_gemm_nt(np.ascontiguousarray(a_mk), sfa, np.ascontiguousarray(b_nk), sfb, c)
+
+
+# ---------------------------------------------------------------------------------------------
+# The activation step between an expert's two GEMMs (the work the pages leave to the caller:
+# pt.news.hada.io, "Interface GEMM e restrições de layout", casting to FP8 is the user's job;
+# the feifmx.com release article's fine-grained scaling fixes the 1x128 granularity of the
+# next GEMM's A).  Input: the first GEMM's bf16 output X [M, 2I], gate X[:, :I] and up
+# X[:, I:].  SwiGLU: h = silu(gate) * up = gate * up / (1 + exp(-gate)).  Quantisation of h
+# for the second GEMM: per 1x128 segment of a row, scale = max(amax, 1e-4) / 448 and
+# code = the e4m3 value nearest to h / scale (ties to the even code), never past +-448; the
+# scales go out MN-major, [I/128, ld] with ld = ceil(M/4)*4, the layout of the NT GEMM's sfa.
+
+def bf16_decode(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exact."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def swiglu(x_bits) -> np.ndarray:
+    """float64 h [M, I] of a bf16 [M, 2I] input (gate first, then up)."""
+    x = bf16_decode(x_bits)
+    i = x.shape[1] // 2
+    g, u = x[:, :i], x[:, i:]
+    return g * u / (1.0 + np.exp(-g))
+
+
+def e4m3_nearest(y) -> np.ndarray:
+    """uint8 e4m3 codes nearest to float64 y (|y| <= 448), ties to the even code.  The format
+    is sign-magnitude: the magnitude code is the one among 0x00 .. 0x7E (the finite
+    non-negative values of the decode table) nearest to |y|, and a negative y (or -0) sets
+    the sign bit."""
+    tab = e4m3_table()
+    mags = np.arange(0x7F)                                   # 0 .. 448
+    vals = tab[mags]
+    y = np.asarray(y, dtype=np.float64)
+    d = np.abs(np.abs(y)[..., None] - vals)
+    cand = d == d.min(axis=-1, keepdims=True)
+    even = cand & ((mags & 1) == 0)
+    pick = np.where(even.any(axis=-1, keepdims=True), even, cand)
+    code = mags[np.argmax(pick, axis=-1)]
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def swiglu_quant(x_bits, ld: Optional[int] = None):
+    """(h float64 [M, I], scales float64 [I/128, ld], codes uint8 [M, I]) by the definition."""
+    h = swiglu(x_bits)
+    m, i = h.shape
+    if i % 128:
+        raise ValueError("oracle: I must be a multiple of 128")
+    ld = (m + 3) // 4 * 4 if ld is None else ld
+    seg = h.reshape(m, i // 128, 128)
+    scale = np.maximum(np.abs(seg).max(axis=2), 1e-4) / 448.0    # [M, I/128]
+    y = np.clip(seg / scale[:, :, None], -448.0, 448.0).reshape(m, i)
+    sf = np.zeros((i // 128, ld), dtype=np.float64)
+    sf[:, :m] = scale.T
+    return h, sf, e4m3_nearest(y)

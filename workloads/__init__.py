@@ -333,6 +333,34 @@ def make_k_grouped(num_groups: int, total_tokens: int, m: int, n: int, seed: int
                     num_groups=num_groups, m=m, n=n, k_total=k_total)
 
 
+# ---------------------------------------------------------------------------------------------
+# Input of the activation step between an expert's two GEMMs: the first GEMM's bf16 output
+# X [M, 2I] (gate columns first, then up).
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (no NaN in the input)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def make_swiglu_input(m: int, i: int, seed: int = 0, outliers: bool = True) -> np.ndarray:
+    """bf16 bits [M, 2I]: N(0, 2) activations; with ``outliers``, one row segment in 64 scaled
+    by 2^U{-6..6} (so segments' amax spans a wide range) and a few all-zero segments."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, 2 * i), dtype=np.float32) * np.float32(2.0)
+    if outliers:
+        segs = x.reshape(m, 2 * i // 128, 128)
+        pick = rng.random(segs.shape[:2]) < 1 / 64
+        mult = np.exp2(rng.integers(-6, 7, size=segs.shape[:2])).astype(np.float32)
+        segs *= np.where(pick, mult, np.float32(1.0))[:, :, None]
+        zero = rng.random(segs.shape[:2]) < 1 / 256
+        segs *= np.where(zero, np.float32(0.0), np.float32(1.0))[:, :, None]
+        x = segs.reshape(m, 2 * i)
+    return f32_to_bf16_bits(x)
+
+
 def masked_counts(num_groups: int, m_max: int, seed: int, replay: Optional[int] = None) -> np.ndarray:
     """masked_m ~ U{0..m_max} per group (inclusive). Replay r draws from default_rng((seed, r))."""
     rng = np.random.default_rng(seed if replay is None else (seed, replay))
@@ -389,6 +417,8 @@ CONFIGS = {
     "moe_masked": dict(kind="masked", num_groups=16, m_max=256, n=7168, k=2048),
     # weight gradient of moe_contiguous's experts: dW[g] (4096 x 7168) over each expert's tokens
     "moe_wgrad": dict(kind="k_grouped", num_groups=8, total_tokens=32768, m=4096, n=7168),
+    # SwiGLU + 1x128 FP8 cast of moe_contiguous's 32768 routed rows, expert width I = 2048
+    "moe_swiglu_quant": dict(kind="swiglu", m=32768, i=2048),
 }
 
 
@@ -403,4 +433,6 @@ def make_config(name: str, seed: int = 0, **overrides):
         return make_contiguous(seed=seed, **cfg)
     if kind == "k_grouped":
         return make_k_grouped(seed=seed, **cfg)
+    if kind == "swiglu":
+        return make_swiglu_input(seed=seed, **cfg)
     return make_masked(seed=seed, **cfg)
