@@ -269,6 +269,30 @@ def make_kgrouped_case(torch, dg, W):
     return c
 
 
+def make_quant_case(torch, dg, W):
+    x = W.make_config("moe_swiglu_quant", seed=0)
+    m, i = x.shape[0], x.shape[1] // 2
+    c = Case("moe_swiglu_quant")
+    ld = (m + 3) // 4 * 4
+    t = dict(x=_dev(torch, x.view(np.int16)),
+             q=torch.empty(m, i, dtype=torch.uint8, device="cuda"),
+             sf=torch.empty(i // 128, ld, dtype=torch.float32, device="cuda"))
+    nbytes = 4 * m * i + m * i + 4 * m * (i // 128)
+    c.sets = _copies(torch, t, nbytes)
+    per_graph = _steps_per_graph(len(c.sets))
+
+    def call(s):
+        dg.swiglu_fp8_quant(s["x"], s["q"], s["sf"])
+
+    _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
+    c.config = dict(workload="moe_swiglu_quant", m=m, i=i, x="bf16 [M, 2I]", q="e4m3 [M, I]",
+                    launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
+    c.flops = lambda i_: 0.0
+    c.bytes = lambda i_: float(nbytes)
+    return c
+
+
 def time_case(torch, case, steps, warmup):
     """Warm up, then time exactly `steps` steps as one region bracketed by HIP events on the
     launch stream (the step time and, for cases without a per-step device update, the kernel's
@@ -403,7 +427,8 @@ def main():
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
                              "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
                              "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad",
-                             "dense_prefill_nn", "dense_prefill_tn", "dense_prefill_tt"])
+                             "dense_prefill_nn", "dense_prefill_tn", "dense_prefill_tt",
+                             "moe_swiglu_quant"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -441,6 +466,7 @@ def main():
         "dense_prefill_nn": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="nn"),
         "dense_prefill_tn": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tn"),
         "dense_prefill_tt": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tt"),
+        "moe_swiglu_quant": lambda: make_quant_case(torch, dg, W),
     }
     order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
     results = {}
@@ -451,7 +477,7 @@ def main():
         # the short workloads take many steps (their spread matters); the long ones fewer
         steps = args.steps if name == args.workload else (
             200 if name in ("dense_small", "dense_skinny", "moe_masked", "dense_skinny_ue8m0",
-                            "moe_masked_ue8m0")
+                            "moe_masked_ue8m0", "moe_swiglu_quant")
             else max(20, args.steps // 2))
         log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
         res = time_case(torch, case, steps, args.warmup)
@@ -477,7 +503,8 @@ def main():
                     frac=achieved / PEAK_FP8_TFLOPS, traffic=traffic,
                     kernel_avg_us=summ["avg_kernel_us"], hbm_gbs_algorithmic=summ["hbm_gbs"],
                     hbm_frac_algorithmic=summ["hbm_gbs"] / PEAK_HBM_GBS)
-    if dom in ("dense_skinny", "moe_masked", "dense_skinny_ue8m0", "moe_masked_ue8m0"):
+    if dom in ("dense_skinny", "moe_masked", "dense_skinny_ue8m0", "moe_masked_ue8m0",
+               "moe_swiglu_quant"):
         roofline.update(bound="hbm", achieved=summ["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=summ["hbm_gbs"] / PEAK_HBM_GBS)
     out = {

@@ -171,6 +171,20 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const v
                                         const int32_t *ks, int num_groups, int m, int n,
                                         int k_total, void *stream);
 
+/*
+ * The activation step between an expert's two GEMMs, fused (pt.news.hada.io, "Interface GEMM
+ * e restrições de layout": casting to FP8 is left to the caller).  x: bf16 [m][2i], gate
+ * columns first, then up (the first GEMM's D).  Writes
+ *   q    e4m3 [m][i]      q = e4m3(h / scale), nearest even, within +-448, where
+ *                         h = gate * up / (1 + exp(-gate))
+ *   sfa  FP32 [i/128][ld_sfa]   scale = max(amax of the 1x128 segment of h, 1e-4) / 448, at
+ *                         sfa[seg * ld_sfa + row] (MN-major: the NT GEMM's A scales for q)
+ * i % 128 == 0; ld_sfa >= m; x 16-byte, q 8-byte, sfa 4-byte aligned; m == 0 is a no-op.
+ * sfa's columns past m are not written.
+ */
+int dg_swiglu_fp8_quant(const void *x, void *q, float *sfa, int64_t ld_sfa, int m, int i,
+                        void *stream);
+
 /* Row alignment of each group segment in the contiguous layout: 128 (the M block size). */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
-    "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt",
+    "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "swiglu_fp8_quant",
     "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "m_grouped_fp8_gemm_nt_masked_ue8m0", "k_grouped_fp8_gemm_tn_contiguous",
     "get_mk_alignment_for_contiguous_layout", "get_sf_aligned_m", "set_num_cus", "get_num_cus",
@@ -73,6 +73,8 @@ def _load():
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                          i32, i32, vp]
     lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = i32
+    lib.dg_swiglu_fp8_quant.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    lib.dg_swiglu_fp8_quant.restype = i32
     lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
     lib.dg_get_sf_aligned_m.argtypes = [i64]
     lib.dg_get_sf_aligned_m.restype = i64
@@ -268,6 +270,21 @@ def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, d, ks, c: Optional[torch.Te
     _check(_load().dg_k_grouped_fp8_gemm_tn_contiguous(
         pa, psfa, pb, psfb, pc, pd, ks_host.ctypes.data, g, m, n, k_total, _stream(stream)))
     return d
+
+
+def swiglu_fp8_quant(x, q, sfa, stream=None):
+    """SwiGLU of x (bf16 [M, 2I], gate then up) cast per 1x128 segment to e4m3: q [M, I] (uint8
+    or float8_e4m3fn) and sfa float32 [I/128, ld >= M] (MN-major), both written."""
+    px = _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m, i2 = x.shape
+    _need(i2 % 256 == 0, "x must be [M, 2I] with I a multiple of 128")
+    i = i2 // 2
+    pq = _dev(q, "q", _FP8_DTYPES, 2)
+    _need(tuple(q.shape) == (m, i), "q must be [M, I]")
+    psf = _dev(sfa, "sfa", torch.float32, 2)
+    _need(sfa.shape[0] == i // 128 and sfa.shape[1] >= m, "sfa must be [I/128, ld >= M]")
+    _check(_load().dg_swiglu_fp8_quant(px, pq, psf, sfa.shape[1], m, i, _stream(stream)))
+    return q, sfa
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

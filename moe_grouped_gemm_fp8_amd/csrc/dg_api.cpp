@@ -544,6 +544,27 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const v
     return ok();
 }
 
+int dg_swiglu_fp8_quant(const void *x, void *q, float *sfa, int64_t ld_sfa, int m, int i,
+                        void *stream)
+{
+    if (m < 0 || i <= 0)
+        return fail(DG_ERR_INVALID_ARG, "sizes must be positive (m=%d i=%d)", m, i);
+    if (i % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "i=%d is not a multiple of 128", i);
+    if (m == 0)
+        return ok();
+    if (!x || !q || !sfa)
+        return fail(DG_ERR_INVALID_ARG, "null tensor pointer");
+    if (ld_sfa < m)
+        return fail(DG_ERR_INVALID_ARG, "ld_sfa=%lld is smaller than m=%d", (long long)ld_sfa, m);
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(sfa, 4))
+        return fail(DG_ERR_MISALIGNED, "X must be 16-byte, q 8-byte and sfa 4-byte aligned");
+    hipError_t e = dg::launch_swiglu_quant(x, q, sfa, ld_sfa, m, i, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
 
 int64_t dg_get_sf_aligned_m(int64_t m) { return m <= 0 ? 0 : (m + 3) / 4 * 4; }

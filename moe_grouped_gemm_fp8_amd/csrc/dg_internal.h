@@ -85,6 +85,11 @@ struct LayoutArgs {
 int64_t layout_grid_size(int layout, const LayoutArgs &args);
 hipError_t launch_layout(int layout, const LayoutArgs &args, hipStream_t stream);
 
+// The activation step (dg_quant.hip): SwiGLU of bf16 X [m, 2i] and its 1x128 FP8 cast into
+// q [m, i] with scales sfa [i/128][ld] (MN-major).
+hipError_t launch_swiglu_quant(const void *x, void *q, float *sfa, int64_t ld, int m, int i,
+                               hipStream_t stream);
+
 // Grid size in workgroups for a launch (host-side, no HIP call).
 int64_t grid_size(int mode, int cfg, const GemmArgs &args);
 

@@ -1,0 +1,102 @@
+// The activation step between an expert's two GEMMs, fused: SwiGLU of the first GEMM's bf16
+// output and the 1x128 FP8 cast that the second GEMM's A needs (pt.news.hada.io, "Interface
+// GEMM e restrições de layout": casting to FP8 is left to the caller; the feifmx.com release
+// article's fine-grained scaling fixes the 1x128 granularity).  For X [M, 2I] (gate columns
+// first, then up):
+//     h = gate * up / (1 + exp(-gate));   per 1x128 segment of a row of h:
+//     scale = max(amax, 1e-4) / 448,  q = e4m3(h / scale) (nearest even, within +-448)
+// with the scales written MN-major, sfa[seg * ld + row], the layout of the NT GEMM's sfa.
+//
+// The step is bound by memory (4 bytes read per byte written), so it is laid out for
+// coalescing: one wave per 512 consecutive columns of a row, each lane 8 columns (16-byte
+// loads of gate and up, an 8-byte store of codes), so a 16-lane quarter of the wave holds
+// one segment; its amax is a 4-step butterfly across those lanes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float silu_times(float g, float u) { return g * u / (1.f + __expf(-g)); }
+
+// two FP32 values (already within +-448) to e4m3 (round to nearest even), packed into bytes
+// 2 sel .. 2 sel + 1 of `old`
+template <bool SEL>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
+{
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, SEL);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void dg_swiglu_quant_kernel(const uint16_t *__restrict__ x,
+                                                               uint8_t *__restrict__ q,
+                                                               float *__restrict__ sfa,
+                                                               int64_t ld, int m, int i,
+                                                               int tasks_per_row)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = task / tasks_per_row;
+    if (row >= m)
+        return;
+    const int col = (int)(task - row * tasks_per_row) * 512 + lane * 8;
+    const bool live = col < i;  // the row's last task may hold fewer than 4 segments
+    float h[8];
+    float amax = 0.f;
+    if (live) {
+        const uint16_t *xr = x + row * 2 * (int64_t)i;
+        const uint4 gw = *reinterpret_cast<const uint4 *>(xr + col);
+        const uint4 uw = *reinterpret_cast<const uint4 *>(xr + i + col);
+        const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[2 * e] = silu_times(bf16_lo(gs[e]), bf16_lo(us[e]));
+            h[2 * e + 1] = silu_times(bf16_hi(gs[e]), bf16_hi(us[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            amax = fmaxf(amax, fabsf(h[e]));
+    }
+    // the segment's 16 lanes (lanes 16 s .. 16 s + 15 share one segment)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (!live)
+        return;
+    const float scale = fmaxf(amax, 1e-4f) / 448.f;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        y[e] = fminf(fmaxf(h[e] / scale, -448.f), 448.f);
+    int lo = 0, hi = 0;
+    lo = cvt_pk_e4m3<false>(y[0], y[1], lo);
+    lo = cvt_pk_e4m3<true>(y[2], y[3], lo);
+    hi = cvt_pk_e4m3<false>(y[4], y[5], hi);
+    hi = cvt_pk_e4m3<true>(y[6], y[7], hi);
+    *reinterpret_cast<uint2 *>(q + row * (int64_t)i + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    if ((lane & 15) == 0)
+        sfa[(int64_t)(col / 128) * ld + row] = scale;
+}
+
+hipError_t launch_swiglu_quant(const void *x, void *q, float *sfa, int64_t ld, int m, int i,
+                               hipStream_t stream)
+{
+    const int tasks_per_row = (i + 511) / 512;
+    const int64_t waves = (int64_t)m * tasks_per_row;
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks <= 0 || blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(dg_swiglu_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t *)x, (uint8_t *)q, sfa, ld, m, i, tasks_per_row);
+    return hipGetLastError();
+}
+
+}  // namespace dg
