@@ -184,7 +184,57 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 
 
 
-// The dense NN, TN and TT layouts (operands stored MN-major on one or both sides).
+int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
+
+// Transposed-operand workspace of the dense NN/TN/TT calls: one per device, allocated (or
+// grown) on a call made while the stream is not being captured, then reused.  Calls that
+// overlap on one device (different streams) share it and must not run concurrently.
+int get_layout_workspace(hipStream_t stream, size_t need, void **out)
+{
+    static std::mutex mu;
+    static void *bufs[64] = {nullptr};
+    static size_t sizes[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(DG_ERR_HIP, "no HIP device available");
+    std::lock_guard<std::mutex> lk(mu);
+    if (sizes[dev] >= need) {
+        *out = bufs[dev];
+        return DG_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        *out = nullptr;  // the caller uses the kernel that reads MN-major operands directly
+        return DG_OK;
+    }
+    if (bufs[dev]) {
+        // earlier calls may still read the old buffer
+        if (hipDeviceSynchronize() != hipSuccess || hipFree(bufs[dev]) != hipSuccess)
+            return fail(DG_ERR_HIP, "cannot release the layout workspace");
+        bufs[dev] = nullptr;
+        sizes[dev] = 0;
+    }
+    const size_t bytes = (need + ((size_t)32 << 20) - 1) / ((size_t)32 << 20) * ((size_t)32 << 20);
+    if (hipMalloc(&bufs[dev], bytes) != hipSuccess) {
+        bufs[dev] = nullptr;
+        return fail(DG_ERR_HIP, "layout workspace allocation failed");
+    }
+    sizes[dev] = bytes;
+    *out = bufs[dev];
+    return DG_OK;
+}
+
+bool layout_native_forced()
+{
+    const char *s = getenv("DG_LAYOUT_NATIVE");
+    return s && *s && *s != '0';
+}
+
+// The dense NN, TN and TT layouts (operands stored MN-major on one or both sides).  By default
+// each MN-major operand is transposed into a workspace (a byte transpose moves it once through
+// HBM) and the NT path runs; under graph capture before the workspace exists, or with
+// DG_LAYOUT_NATIVE=1, the layout kernel reads the MN-major operands directly.
 int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
                 const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
 {
@@ -205,6 +255,30 @@ int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, con
         return fail(DG_ERR_MISALIGNED, "C must be 16-byte aligned");
     if (c && (const void *)c == d)
         return fail(DG_ERR_INVALID_ARG, "C and D must not alias");
+    const bool b_mn = layout == dg::LAYOUT_NN || layout == dg::LAYOUT_TN;
+    hipStream_t s = (hipStream_t)stream;
+    if (!layout_native_forced()) {
+        const size_t a_bytes = a_mn ? ((size_t)m * k + 255) / 256 * 256 : 0;
+        const size_t b_bytes = b_mn ? (size_t)n * k : 0;
+        void *ws = nullptr;
+        if ((rc = get_layout_workspace(s, a_bytes + b_bytes, &ws)) != DG_OK)
+            return rc;
+        if (ws) {
+            const void *a_nt = a, *b_nt = b;
+            hipError_t e = hipSuccess;
+            if (a_mn) {  // A stored [k][m] -> [m][k]
+                e = dg::launch_transpose_u8(a, ws, k, m, s);
+                a_nt = ws;
+            }
+            if (e == hipSuccess && b_mn) {  // B stored [k][n] -> [n][k]
+                b_nt = (const uint8_t *)ws + a_bytes;
+                e = dg::launch_transpose_u8(b, (uint8_t *)ws + a_bytes, k, n, s);
+            }
+            if (e != hipSuccess)
+                return fail(DG_ERR_HIP, "transpose launch failed: %s", hipGetErrorString(e));
+            return gemm_nt(dg::SF_FP32, a_nt, sfa, ld_sfa, b_nt, sfb, c, d, m, n, k, stream);
+        }
+    }
     dg::LayoutArgs args;
     memset(&args, 0, sizeof(args));
     args.a = (const uint8_t *)a;
@@ -218,7 +292,7 @@ int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, con
     args.n = n;
     args.k = k;
     args.num_groups = 1;
-    hipError_t e = dg::launch_layout(layout, args, (hipStream_t)stream);
+    hipError_t e = dg::launch_layout(layout, args, s);
     if (e != hipSuccess)
         return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

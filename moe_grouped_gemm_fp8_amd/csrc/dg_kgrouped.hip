@@ -489,4 +489,57 @@ hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ---- byte transpose y[c][r] = x[r][c] (x: rows x cols, pitch cols; y: cols x rows, pitch
+// rows) of e4m3 operands, for the dense NN/TN/TT calls: their MN-major operands become
+// K-major, which the NT kernels take.  rows % 64 == 0 and cols % 16 == 0.  A workgroup moves
+// one 64 x 64 byte tile: 16-byte loads into a padded LDS tile (80-byte rows), then
+// ds_read_b64_tr_b8, whose 16-lane groups turn an 8 x 16 byte block into 16 lanes of 8
+// consecutive row bytes; wave w writes output rows 16 w .. 16 w + 15, 32 consecutive bytes
+// of each per instruction.
+__global__ __launch_bounds__(256) void dg_transpose_u8_kernel(const uint8_t *__restrict__ x,
+                                                               uint8_t *__restrict__ y, int rows,
+                                                               int cols, int tiles_c)
+{
+    constexpr int PITCH = 80;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
+    const int tid = threadIdx.x;
+    const int r0 = (blockIdx.x / tiles_c) * 64, c0 = (blockIdx.x % tiles_c) * 64;
+    {
+        const int r = tid >> 2, c = (tid & 3) * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c0 + c < cols)
+            v = *reinterpret_cast<const uint4 *>(x + (int64_t)(r0 + r) * cols + c0 + c);
+        *reinterpret_cast<uint4 *>(tile + r * PITCH + c) = v;
+    }
+    __syncthreads();
+    const uint32_t base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)tile;
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int inst = 0; inst < 2; ++inst) {
+        const int b = g + 4 * inst;  // K rows 8 b .. 8 b + 7 of the tile
+        const uint32_t addr =
+            base + (uint32_t)((8 * b + (j >> 1)) * PITCH + 16 * w + 8 * (j & 1));
+        v2i v = lds_read_tr8_at<0>(addr);
+        lds_wait();
+        tie(v);
+        const int c = c0 + 16 * w + j;  // output row
+        if (c < cols)
+            *reinterpret_cast<uint2 *>(y + (int64_t)c * rows + r0 + 8 * b) =
+                make_uint2((uint32_t)v.x, (uint32_t)v.y);
+    }
+}
+
+hipError_t launch_transpose_u8(const void *x, void *y, int rows, int cols, hipStream_t stream)
+{
+    if (rows % 64 != 0 || cols % 16 != 0)
+        return hipErrorInvalidValue;
+    const int tiles_c = (cols + 63) / 64;
+    const int64_t grid = (int64_t)(rows / 64) * tiles_c;
+    if (grid <= 0 || grid > 0x7fffffff)
+        return grid == 0 ? hipSuccess : hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(dg_transpose_u8_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint8_t *)x, (uint8_t *)y, rows, cols, tiles_c);
+    return hipGetLastError();
+}
+
 }  // namespace dg

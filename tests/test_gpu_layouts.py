@@ -41,18 +41,53 @@ def ref(layout, p):
     return oracle.fp8_gemm_layout(layout, p.a, p.sfa, p.b, p.sfb, p.c)
 
 
+# "transposed": MN-major operands transposed into the workspace, then the NT kernels (the
+# default); "native": the layout kernel reads them directly (the path under graph capture
+# before the workspace exists)
+PATHS = ["transposed", "native"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("with_c", [False, True])
-def test_ragged_tiles(layout, with_c):
+def test_ragged_tiles(layout, with_c, path, monkeypatch):
+    monkeypatch.setenv("DG_LAYOUT_NATIVE", "1" if path == "native" else "0")
     p = W.stored_layout(W.make_dense(208, 336, 640, seed=91, with_c=with_c), layout)
-    assert_parity(run(layout, p), ref(layout, p), f"{layout} c={with_c}")
+    assert_parity(run(layout, p), ref(layout, p), f"{layout} c={with_c} {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("k", [128, 256, 384, 1152])
+def test_k_blocks(layout, k, path, monkeypatch):
+    monkeypatch.setenv("DG_LAYOUT_NATIVE", "1" if path == "native" else "0")
+    p = W.stored_layout(W.make_dense(128, 256, k, seed=92, with_c=True, c_std=2.0), layout)
+    assert_parity(run(layout, p), ref(layout, p), f"{layout} k={k} {path}")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("k", [128, 256, 384, 1152])
-def test_k_blocks(layout, k):
-    p = W.stored_layout(W.make_dense(128, 256, k, seed=92, with_c=True, c_std=2.0), layout)
-    assert_parity(run(layout, p), ref(layout, p), f"{layout} k={k}")
+def test_graph_replays_of_the_transposed_path(layout):
+    p = W.stored_layout(W.make_dense(256, 512, 512, seed=95, with_c=True), layout)
+    a, sfa, b, sfb, c = dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), dev(p.c)
+    fn = getattr(dg, "fp8_gemm_" + layout)
+    d = sentinel_like((p.m, p.n))
+    fn(a, sfa, b, sfb, d, c)                                         # workspace in place
+    torch.cuda.synchronize()
+    eager = bits(d)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            fn(a, sfa, b, sfb, d, c)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(3):
+        d.view(torch.int16).fill_(W.BF16_SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), eager), f"replay {r}"
+    assert_parity(eager, ref(layout, p), f"{layout} graph")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
