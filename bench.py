@@ -4,8 +4,9 @@
 One step = one call of the library's hot path on one batch of seeded synthetic input that
 is already resident in device memory.  The headline workload is the dense prefill GEMM
 M=4096 N=7168 K=2048 with an FP32 C (D = C + A @ B.T, bf16 D); the other workloads (small
-dense, skinny dense, contiguous MoE, masked MoE replayed from a captured graph) are timed
-too and reported under "workloads".  Inputs rotate over several device-resident copies whose
+dense, skinny dense, contiguous MoE, masked MoE replayed from a captured graph, their UE8M0
+forms, the K-grouped MoE weight gradient, the dense NN/TN/TT layouts and the fused SwiGLU
+FP8 cast) are timed too and reported under "workloads".  Inputs rotate over several device-resident copies whose
 total exceeds the 256 MB Infinity Cache, so every launch reads its operands from HBM.
 
 Prints ONE JSON line on stdout; progress goes to stderr.

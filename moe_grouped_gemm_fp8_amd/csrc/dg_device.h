@@ -50,28 +50,6 @@ __device__ __forceinline__ void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Same, for a wave-uniform count known only at run time (anything above 31 waits for all).
-__device__ __forceinline__ void wait_vm_dyn(int n)
-{
-    switch (n) {
-#define DG_WAIT_CASE(k) \
-    case k:             \
-        wait_vm<k>();   \
-        break;
-        DG_WAIT_CASE(1) DG_WAIT_CASE(2) DG_WAIT_CASE(3) DG_WAIT_CASE(4) DG_WAIT_CASE(5)
-        DG_WAIT_CASE(6) DG_WAIT_CASE(7) DG_WAIT_CASE(8) DG_WAIT_CASE(9) DG_WAIT_CASE(10)
-        DG_WAIT_CASE(11) DG_WAIT_CASE(12) DG_WAIT_CASE(13) DG_WAIT_CASE(14) DG_WAIT_CASE(15)
-        DG_WAIT_CASE(16) DG_WAIT_CASE(17) DG_WAIT_CASE(18) DG_WAIT_CASE(19) DG_WAIT_CASE(20)
-        DG_WAIT_CASE(21) DG_WAIT_CASE(22) DG_WAIT_CASE(23) DG_WAIT_CASE(24) DG_WAIT_CASE(25)
-        DG_WAIT_CASE(26) DG_WAIT_CASE(27) DG_WAIT_CASE(28) DG_WAIT_CASE(29) DG_WAIT_CASE(30)
-        DG_WAIT_CASE(31)
-#undef DG_WAIT_CASE
-    default:
-        wait_vm<0>();
-        break;
-    }
-}
-
 __device__ __forceinline__ void bare_barrier()
 {
     asm volatile("" ::: "memory");
@@ -146,23 +124,6 @@ template <int N>
 __device__ __forceinline__ void lds_wait_n()
 {
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
-// lds_wait_n for a count that is a constant only after loop unrolling
-__device__ __forceinline__ void lds_wait_le(int n)
-{
-    switch (n) {
-#define DG_LGKM_CASE(k)    \
-    case k:                \
-        lds_wait_n<k>();   \
-        break;
-        DG_LGKM_CASE(1) DG_LGKM_CASE(2) DG_LGKM_CASE(3) DG_LGKM_CASE(4) DG_LGKM_CASE(5)
-        DG_LGKM_CASE(6) DG_LGKM_CASE(7) DG_LGKM_CASE(8) DG_LGKM_CASE(9) DG_LGKM_CASE(10)
-        DG_LGKM_CASE(11) DG_LGKM_CASE(12) DG_LGKM_CASE(13) DG_LGKM_CASE(14) DG_LGKM_CASE(15)
-#undef DG_LGKM_CASE
-    default:
-        lds_wait_n<0>();
-        break;
-    }
 }
 __device__ __forceinline__ void tie(v4i &v) { asm volatile("" : "+v"(v)); }
 

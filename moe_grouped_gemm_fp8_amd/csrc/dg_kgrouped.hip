@@ -10,7 +10,9 @@
 //    both operands, FP32 D[g] = C[g] + ..., C optional or D itself:
 //        D[g, m, n] = C[g, m, n] + sum over its K blocks kb of
 //                     sfa[kb, m] * sfb[kb, n] * sum_{k in kb} A[k, m] * B[k, n]
-// (the NT layout has its own, more deeply pipelined kernels).
+// (the NT layout has its own, more deeply pipelined kernels; the dense NN/TN/TT calls run
+// those by default after dg_transpose_u8_kernel below has made their MN-major operands
+// K-major, and use this template under graph capture before their workspace exists).
 //
 // Design:
 //  * One workgroup per 128 x 128 tile (of one group); eight waves (2 x 4), wave tile 64 x 32.
