@@ -140,9 +140,10 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int
  * rows; sfb [ceil(n/128)][k/128], 128x128 blocks of B), C, D and the error behaviour are those
  * of dg_fp8_gemm_nt.  In addition: sfa 16-byte aligned, m % 16 == 0 when A is stored [k][m],
  * and k * max(m, n) < 2^31.  MN-major operands are transposed into a per-device workspace
- * (allocated or grown by a call made outside graph capture; calls overlapping on one device
- * share it and must not run concurrently); a captured call finding it too small reads them
- * directly instead.
+ * (allocated or grown by a call made outside graph capture, at least doubling; a replaced
+ * workspace is kept until the process ends, since captured graphs may still use it; calls
+ * overlapping on one device share it and must not run concurrently); a captured call finding
+ * it too small reads the operands directly instead.
  */
 int dg_fp8_gemm_nn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
                    const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);

@@ -187,9 +187,11 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
             const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
 
-// Transposed-operand workspace of the dense NN/TN/TT calls: one per device, allocated (or
-// grown) on a call made while the stream is not being captured, then reused.  Calls that
-// overlap on one device (different streams) share it and must not run concurrently.
+// Transposed-operand workspace of the dense NN/TN/TT calls: one per device, allocated on a
+// call made while the stream is not being captured, then reused.  When a call needs more, a
+// larger one (at least twice the size) replaces it, and the old one is never freed: graphs
+// captured earlier keep its address and may be replayed.  Calls that overlap on one device
+// (different streams) share it and must not run concurrently.
 int get_layout_workspace(hipStream_t stream, size_t need, void **out)
 {
     static std::mutex mu;
@@ -208,20 +210,14 @@ int get_layout_workspace(hipStream_t stream, size_t need, void **out)
         *out = nullptr;  // the caller uses the kernel that reads MN-major operands directly
         return DG_OK;
     }
-    if (bufs[dev]) {
-        // earlier calls may still read the old buffer
-        if (hipDeviceSynchronize() != hipSuccess || hipFree(bufs[dev]) != hipSuccess)
-            return fail(DG_ERR_HIP, "cannot release the layout workspace");
-        bufs[dev] = nullptr;
-        sizes[dev] = 0;
-    }
-    const size_t bytes = (need + ((size_t)32 << 20) - 1) / ((size_t)32 << 20) * ((size_t)32 << 20);
-    if (hipMalloc(&bufs[dev], bytes) != hipSuccess) {
-        bufs[dev] = nullptr;
+    size_t bytes = sizes[dev] * 2 > need ? sizes[dev] * 2 : need;
+    bytes = (bytes + ((size_t)32 << 20) - 1) / ((size_t)32 << 20) * ((size_t)32 << 20);
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess)
         return fail(DG_ERR_HIP, "layout workspace allocation failed");
-    }
+    bufs[dev] = p;  // the previous buffer stays allocated (see above)
     sizes[dev] = bytes;
-    *out = bufs[dev];
+    *out = p;
     return DG_OK;
 }
 

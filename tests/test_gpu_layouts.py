@@ -117,3 +117,33 @@ def test_host_checks_of_the_layouts():
     assert e.value.code == -2                                     # m % 16 with A stored [K, M]
     q = W.stored_layout(W.make_dense(200, 256, 256, seed=94), "nn")
     assert_parity(run("nn", q), ref("nn", q), "nn m=200")          # fine with A stored [M, K]
+
+
+def test_graph_captured_before_the_workspace_grows_still_replays():
+    # a graph records the workspace's address; a later, larger call replaces the workspace
+    # with a bigger one, and the old graph must still find its buffer
+    small = W.stored_layout(W.make_dense(128, 256, 256, seed=96, with_c=True), "tn")
+    a, sfa, b, sfb, c = (dev(x) for x in (small.a, small.sfa, small.b, small.sfb, small.c))
+    d = sentinel_like((small.m, small.n))
+    dg.fp8_gemm_tn(a, sfa, b, sfb, d, c)
+    torch.cuda.synchronize()
+    eager = bits(d)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            dg.fp8_gemm_tn(a, sfa, b, sfb, d, c)
+    torch.cuda.current_stream().wait_stream(side)
+    # 8192 x 2048 bytes of A and of B to transpose (33.6 MB): more than any earlier call in
+    # the suite needs (at most 23 MB, in 32 MB units), so the workspace is replaced
+    big = W.stored_layout(W.make_dense(8192, 8192, 2048, seed=97), "tn")
+    db = sentinel_like((big.m, big.n))
+    dg.fp8_gemm_tn(dev(big.a), dev(big.sfa), dev(big.b), dev(big.sfb), db)
+    torch.cuda.synchronize()
+    d.view(torch.int16).fill_(W.BF16_SENTINEL)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d), eager)
+    assert_parity(eager, ref("tn", small), "tn graph before growth")
