@@ -8,6 +8,8 @@ import sys
 import numpy as np
 import pytest
 
+import moe_grouped_gemm_fp8_amd as dg
+
 import oracle
 import workloads as W
 from gpu_util import (assert_parity, dense_rows_ref, fp32_scales, run_contiguous, run_dense,
@@ -188,3 +190,32 @@ def test_masked_workload_sampled_rows():
         ref = oracle.fp8_gemm_nt(p.a[g, rows], W.mn_major(sfa[g][:, rows].T), p.b[g], sfb[g])
         assert_parity(got[g, rows], ref, f"moe_masked ue8m0 group {g}")
         assert not np.any(got[g, :valid] == W.BF16_SENTINEL)
+
+
+def test_masked_graph_replays_follow_device_masked_m():
+    import torch
+    from gpu_util import bits, dev, sentinel_like
+    g_, m_max, n, k = 6, 256, 448, 640
+    p = W.make_masked(g_, m_max, n, k, seed=73, ue8m0=True)
+    a, sfa, b, sfb = dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb)
+    mm_dev = dev(p.masked_m)
+    d = sentinel_like((g_, m_max, n))
+    call = lambda: dg.m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, d, mm_dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(4):
+        mm = W.masked_counts(g_, m_max, seed=73, replay=r)
+        d.view(torch.int16).fill_(W.BF16_SENTINEL)
+        mm_dev.copy_(torch.from_numpy(mm))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.m_grouped_masked_ue8m0(p.a, p.sfa, p.b, p.sfb, mm)
+        assert_parity(bits(d), ref, f"ue8m0 graph replay {r}")

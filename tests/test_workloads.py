@@ -53,3 +53,29 @@ def test_masked_counts_inclusive_range_and_replays():
     assert not np.array_equal(r1, r2)
     draws = W.masked_counts(20000, 256, seed=3)
     assert draws.min() == 0 and draws.max() == 256
+
+
+def test_new_generators_are_deterministic():
+    a = W.make_k_grouped(3, 300, 32, 48, seed=5, counts=[100, 0, 200], with_c=True)
+    b = W.make_k_grouped(3, 300, 32, 48, seed=5, counts=[100, 0, 200], with_c=True)
+    for f in ("a", "sfa", "b", "sfb", "ks", "c"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    x1 = W.make_swiglu_input(8, 256, seed=6)
+    x2 = W.make_swiglu_input(8, 256, seed=6)
+    assert x1.dtype == np.uint16 and x1.shape == (8, 512) and np.array_equal(x1, x2)
+    u = W.make_dense(64, 128, 512, seed=7, ue8m0=True)
+    assert u.sfa.dtype == np.int32 and u.sfa.shape == (1, 64) and u.sfb.shape == (1, 1)
+
+
+def test_f32_to_bf16_bits_rounds_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e38], np.float32)
+    got = W.f32_to_bf16_bits(x)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: to the even mantissa (1.0)
+    assert got.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x7F62]
+
+
+def test_stored_layout_keeps_the_scales():
+    q = W.make_dense(32, 64, 256, seed=8)
+    for lay in ("nn", "tn", "tt"):
+        p = W.stored_layout(q, lay)
+        assert p.sfa is q.sfa and p.sfb is q.sfb
