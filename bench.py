@@ -42,7 +42,7 @@ def kernel_source_hash() -> str:
     """Hash of the library's code with comments and whitespace removed, so that a counter
     record stays valid across edits that cannot change the kernels."""
     h = hashlib.sha256()
-    for f in ("dg_gemm.hip", "dg_stream.hip", "dg_kgrouped.hip", "dg_quant.hip", "dg_api.cpp",
+    for f in ("dg_gemm.hip", "dg_stream.hip", "dg_layout.hip", "dg_quant.hip", "dg_api.cpp",
               "dg_device.h",
               "dg_internal.h"):
         with open(os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", f)) as fh:

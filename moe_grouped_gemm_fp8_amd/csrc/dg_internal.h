@@ -61,7 +61,7 @@ struct GemmArgs {
     int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
 };
 
-// The MN-major-operand kernel (dg_kgrouped.hip): the dense NN, TN and TT layouts (A stored
+// The MN-major-operand kernel (dg_layout.hip): the dense NN, TN and TT layouts (A stored
 // [M, K] or [K, M], B [N, K] or [K, N], the NT scale layouts, bf16 D, optional FP32 C) and the
 // K-grouped TN form (MoE weight gradient: A [K_total, M], B [K_total, N], one FP32 scale per
 // 128-deep K block per column for both, FP32 D[g] = C[g] + ..., group g covering K blocks
