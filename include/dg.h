@@ -76,8 +76,8 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
  *   m_indices  device int32 [m_total]: the group of each row; -1 marks a padding row
  * Row r is computed with B[m_indices[r]] and written to D; rows whose index is outside
  * [0, num_groups) are neither read into any result nor written (D keeps its old contents).
- * Each aligned 128-row block must hold rows of at most one group (padding aside); a block
- * mixing two groups computes only the rows of the largest group index in it.
+ * Each aligned 128-row block must hold rows of at most one group (padding aside); rows of a
+ * block that mixes two groups may be left unwritten.
  */
 int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,
                                         const void *b, const float *sfb, void *d,

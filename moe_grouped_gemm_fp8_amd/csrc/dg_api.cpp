@@ -402,9 +402,31 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
     int cus = 0;
     if ((rc = device_cus(&cus)) != DG_OK)
         return rc;
+    // A tile takes one group's B.  Tiles of up to 128 rows hold one group (the alignment);
+    // a 256-row tile, one workgroup per tile, runs twice where it holds two groups, about
+    // half of the (num_groups - 1) group boundaries for padded expert blocks.
     int cfg = forced_config();
-    if (cfg < 0 || cfg == dg::CFG_STREAM64 || 128 % dg::kTiles[cfg].bm != 0)
-        cfg = (n % 256 == 0) ? dg::CFG_128x256w8 : dg::CFG_128x128;
+    if (cfg >= 0 && (cfg == dg::CFG_STREAM64 ||
+                     (128 % dg::kTiles[cfg].bm != 0 &&
+                      (dg::kTiles[cfg].bm != 256 || dg::kTiles[cfg].persistent))))
+        cfg = -1;
+    if (cfg < 0) {
+        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
+        double best = 0;
+        for (int cnd : cands) {
+            const dg::TileInfo &t = dg::kTiles[cnd];
+            if (cnd == dg::CFG_128x256w8 && n % 256 != 0)
+                continue;
+            int64_t rows = (m_total + t.bm - 1) / t.bm;
+            if (t.bm > 128)
+                rows += (num_groups - 1) / 2;
+            const double cost = tile_cost(t.bm, t.bn, rows * ((n + t.bn - 1) / t.bn), cus);
+            if (cfg < 0 || cost < best) {
+                best = cost;
+                cfg = cnd;
+            }
+        }
+    }
     dg::GemmArgs args{};
     args.a = (const uint8_t *)a;
     args.sfa = sfa;
@@ -420,6 +442,15 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
     args.splits = 1;
     args.max_wgs = persistent_wgs(cus);
     args.sf_fmt = sf_fmt;
+    if (dg::kTiles[cfg].bm > 128) {
+        // second groups of straddling 256-row tiles on workgroups of their own: as many
+        // tile-rows as group boundaries (groups laid out in order), for up to 256 tile-rows
+        const int tiles_m = (m_total + 255) / 256;
+        args.straddle_rows = tiles_m <= 256 ? (num_groups - 1 < tiles_m ? num_groups - 1 : tiles_m) : 0;
+        const char *e = getenv("DG_STRADDLE_ROWS");  // tests: fewer served slots
+        if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
+            args.straddle_rows = atoi(e);
+    }
     print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
 }

@@ -157,6 +157,14 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int &tm,
     tn = rem / gsz;
 }
 
+// (tm, tn) -> tile id, the inverse of raster()
+__device__ __forceinline__ int raster_index(int tm, int tn, int tiles_m, int tiles_n)
+{
+    const int first = tm / GROUP_M * GROUP_M;
+    const int gsz = min(tiles_m - first, GROUP_M);
+    return first * tiles_n + tn * gsz + (tm - first);
+}
+
 // 128-bit buffer resource for raw (unstrided) loads of `bytes` bytes from `base`: any lane
 // whose offset falls outside the range reads zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)

@@ -36,6 +36,10 @@
 //    together on one XCD share A rows and B columns in that XCD's L2.  Most tile shapes run
 //    persistent workgroups (one per CU) that walk their XCD's range; the next tile's first K
 //    blocks are copied while the current tile finishes, hiding the per-tile prologue.
+//  * Contiguous form: a tile takes the group of its rows from the per-row group indices.  The
+//    groups are aligned to 128 rows, so a 256-row tile (one workgroup per tile) can hold the
+//    rows of two groups; it then runs twice, once with each group's B, and each pass stores
+//    only the rows of its own group.
 //  * Shapes too small to fill the CUs with these tiles go to the split-K streaming kernel
 //    (dg_stream.hip) instead.
 #include <hip/hip_runtime.h>
@@ -151,6 +155,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
+    // contiguous tiles that may straddle two groups (their last rows may also lie past M)
+    constexpr bool TWO_GROUPS = MODE == MODE_CONTIG && BM > 128;
+    static_assert(!TWO_GROUPS || (BM == 256 && !PERSIST), "straddling tiles: 256 rows, one per workgroup");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -180,15 +187,70 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // workgroups stride through it together, so the tiles in flight on one XCD are neighbours
     // in the raster and share A rows and B columns in that XCD's L2.  With one workgroup per
     // tile this is the plain XCD-contiguous remap.
+    //
+    // Contiguous 256-row tiles can hold the rows of two groups (the groups are aligned to 128
+    // rows); such a tile needs a second pass with the other group's B.  Run inside the tile's
+    // own workgroup it would double that workgroup's time, and in the last wave of workgroups
+    // it would lengthen the whole launch by a tile.  So the "listed" straddles get workgroups
+    // of their own, ahead of the tiles: tile-row t is listed when the first rows of its two
+    // 128-row blocks hold two different valid groups (one per group boundary for groups laid
+    // out in order).  Listed straddles are numbered in tile-row order; the first E workgroups
+    // serve the first straddle_rows of them, one per N tile, and a tile's own workgroup runs
+    // the second pass itself only for a straddle not served so (a straddle the first rows do
+    // not show, or one past straddle_rows).  Both sides decide from the same loads.
     const int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
+    const int E = TWO_GROUPS ? ((p.straddle_rows * tiles_n + 7) & ~7) : 0;
+    const int bid = (int)blockIdx.x - E;  // < 0: a workgroup serving a listed straddle
     int tile_id, tile_end, tile_step;
-    {
-        const int G = gridDim.x, q = G >> 3, r = G & 7, x = blockIdx.x & 7;
+    // listed straddles among tile-rows 64 c + lane (c < 4; the host lists them only while
+    // tiles_m <= 256), and the groups of tile-row t's two block-leading rows
+    auto leaders = [&](int t, int &la, int &lb) {
+        const int r0 = t * BM;
+        la = p.grp[r0];
+        lb = r0 + 128 < M ? p.grp[r0 + 128] : -1;
+        la = (la >= 0 && la < p.num_groups) ? la : -1;
+        lb = (lb >= 0 && lb < p.num_groups) ? lb : -1;
+    };
+    uint64_t listed[4];
+    auto scan_listed = [&]() {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int t = 64 * c + lane;
+            int la = -1, lb = -1;
+            if (t < tiles_m)
+                leaders(t, la, lb);
+            listed[c] = __ballot(la >= 0 && lb >= 0 && la != lb);
+        }
+    };
+    if (TWO_GROUPS && bid < 0) {
+        const int b = (int)blockIdx.x / tiles_n, tn = (int)blockIdx.x - b * tiles_n;
+        if (b >= p.straddle_rows)
+            return;  // (E is rounded up to whole XCD rounds)
+        scan_listed();
+        int t = -1, left = b;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint64_t mk = listed[c];
+            const int cnt = __builtin_popcountll(mk);
+            if (t < 0 && left < cnt) {
+                for (int i = 0; i < left; ++i)
+                    mk &= mk - 1;
+                t = 64 * c + __builtin_ctzll(mk);
+            }
+            left -= t < 0 ? cnt : 0;
+        }
+        if (t < 0)
+            return;  // fewer listed straddles than served slots
+        tile_id = raster_index(t, tn, tiles_m, tiles_n);
+        tile_end = tile_id + 1;
+        tile_step = 1;
+    } else {
+        const int G = gridDim.x - E, q = G >> 3, r = G & 7, x = bid & 7;
         const int px = q + (x < r ? 1 : 0);
         const int wx = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
         // 32-bit products: the host launches fewer workgroups than tiles only while
         // total * G < 2^31
-        tile_id = (int)((uint32_t)(total * wx) / (uint32_t)G) + (blockIdx.x >> 3);
+        tile_id = (int)((uint32_t)(total * wx) / (uint32_t)G) + (bid >> 3);
         tile_end = (int)((uint32_t)(total * (wx + px)) / (uint32_t)G);
         tile_step = px;
     }
@@ -197,8 +259,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
 
     // Tile bookkeeping, wave-uniform: coordinates, group, the rows that are computed, and
     // whether it has none (a contiguous block of padding rows, a masked tile past masked_m).
+    // Contiguous tiles taller than the 128-row group alignment can hold the rows of two
+    // groups: g is the larger, g2 the other one (or -1), computed by a second pass.
     struct Tile {
-        int m0, n0, g, row_limit;
+        int m0, n0, g, g2, row_limit;
         bool empty;
     };
     // raw per-tile data that comes from device memory: masked_m of the tile's group, or the
@@ -230,6 +294,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         u.m0 = tm * BM;
         u.n0 = tn * BN;
         u.g = g;
+        u.g2 = -1;
         u.row_limit = M;
         u.empty = false;
         return u;
@@ -238,12 +303,17 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if constexpr (MODE == MODE_MASKED) {
             raw_cnt = p.grp[u.g];
         } else if constexpr (MODE == MODE_CONTIG) {
+            // (rows past M: only a tile taller than the 128-row alignment reaches them)
 #pragma unroll
-            for (int r = 0; r < BM / 64; ++r)
-                raw_max[r] = p.grp[u.m0 + lane + 64 * r];
+            for (int r = 0; r < BM / 64; ++r) {
+                const int row = u.m0 + lane + 64 * r;
+                raw_max[r] = (!TWO_GROUPS || row < M) ? p.grp[row] : -1;
+            }
 #pragma unroll
-            for (int i = 0; i < SM; ++i)
-                raw_row[i] = p.grp[u.m0 + wm + 16 * i + fr];
+            for (int i = 0; i < SM; ++i) {
+                const int row = u.m0 + wm + 16 * i + fr;
+                raw_row[i] = (!TWO_GROUPS || row < M) ? p.grp[row] : -1;
+            }
         }
     };
     int rowg_next[SM];  // contiguous: the epilogue rows' groups of the tile being prepared
@@ -260,6 +330,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 best = max(best, (v >= 0 && v < p.num_groups) ? v : -1);
             }
             u.g = __builtin_amdgcn_readfirstlane(wave_max(best));
+            if constexpr (TWO_GROUPS) {
+                int second = -1;
+#pragma unroll
+                for (int r = 0; r < BM / 64; ++r) {
+                    const int v = raw_max[r];
+                    second = max(second, (v >= 0 && v < u.g) ? v : -1);
+                }
+                u.g2 = __builtin_amdgcn_readfirstlane(wave_max(second));
+            }
             u.empty = u.g < 0;
 #pragma unroll
             for (int i = 0; i < SM; ++i)
@@ -505,6 +584,37 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     Tile cur = place(tile_id);
     load_meta(cur);
     cur = finish_meta(cur);
+    if constexpr (TWO_GROUPS) {
+        // a straddle is served ahead of the tiles when it is listed, among the first
+        // straddle_rows listed ones, and its groups are those of its block-leading rows
+        if (bid < 0 || cur.g2 >= 0) {
+            const int t = cur.m0 / BM;
+            int la, lb;
+            leaders(t, la, lb);
+            la = __builtin_amdgcn_readfirstlane(la);
+            lb = __builtin_amdgcn_readfirstlane(lb);
+            const bool match = cur.g2 >= 0 && la >= 0 && lb >= 0 && max(la, lb) == cur.g &&
+                               min(la, lb) == cur.g2;
+            if (bid < 0) {
+                if (match)
+                    cur.g = cur.g2;  // this workgroup: the second group only
+                else
+                    cur.empty = true;  // the tile's own workgroup runs it
+                cur.g2 = -1;
+            } else if (match && p.straddle_rows > 0) {
+                scan_listed();
+                int rank = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int below = t - 64 * c;
+                    const uint64_t m = below >= 64 ? ~0ull : (below <= 0 ? 0ull : (1ull << below) - 1);
+                    rank += __builtin_popcountll(listed[c] & m);
+                }
+                if (rank < p.straddle_rows)
+                    cur.g2 = -1;  // served ahead
+            }
+        }
+    }
     int rowg[SM];
 #pragma unroll
     for (int i = 0; i < SM; ++i)
@@ -935,14 +1045,20 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             constexpr int CPR = BN / 8;  // 16-byte pieces per output row
             static_assert((BM * CPR) % NT == 0, "output pieces split evenly over the threads");
             constexpr int PPT = BM * CPR / NT;  // pieces per thread
+            // addresses from an opaque copy of the thread id: where a workgroup runs a tile
+            // twice they are then formed here, not held in registers through the K loop
+            int et = tid;
+            asm volatile("" : "+v"(et));
+            const int el = et & 63, ew = et >> 6;
+            const int ewm = (ew / WN) * TM, ewn = (ew % WN) * TN;
             wait_vm<0>();
             bare_barrier();  // every wave is past its last fragment read and copy
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
                 for (int j = 0; j < SN; ++j)
-                    lds_write8(lds_base + (uint32_t)((wm + 16 * i + fr) * OS +
-                                                     (wn + 16 * j + 4 * fg) * 2),
+                    lds_write8(lds_base + (uint32_t)((ewm + 16 * i + (el & 15)) * OS +
+                                                     (ewn + 16 * j + 4 * (el >> 4)) * 2),
                                pack_bf16x2(acc[i][j].x, acc[i][j].y),
                                pack_bf16x2(acc[i][j].z, acc[i][j].w));
             lds_wait();
@@ -950,20 +1066,22 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             v4i piece[PPT];
 #pragma unroll
             for (int t = 0; t < PPT; ++t) {
-                const int q = tid + t * NT;
+                const int q = et + t * NT;
                 piece[t] = lds_read16(lds_base + (uint32_t)((q / CPR) * OS + (q % CPR) * 16));
             }
             int prow[PPT];
             if constexpr (MODE == MODE_CONTIG) {
 #pragma unroll
-                for (int t = 0; t < PPT; ++t)
-                    prow[t] = p.grp[cur.m0 + (tid + t * NT) / CPR];
+                for (int t = 0; t < PPT; ++t) {
+                    const int row = cur.m0 + (et + t * NT) / CPR;
+                    prow[t] = (!TWO_GROUPS || row < M) ? p.grp[row] : -1;
+                }
             }
             lds_wait();
             if (!cur.empty) {
 #pragma unroll
                 for (int t = 0; t < PPT; ++t) {
-                    const int q = tid + t * NT;
+                    const int q = et + t * NT;
                     const int row = cur.m0 + q / CPR;
                     const int col = cur.n0 + (q % CPR) * 8;
                     bool ok = row < cur.row_limit && col < N;
@@ -973,6 +1091,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                         __builtin_nontemporal_store(
                             piece[t], reinterpret_cast<v4i *>(D + (int64_t)row * N + col));
                 }
+            }
+        }
+        if constexpr (TWO_GROUPS) {
+            // a tile holding the rows of two groups runs again for the other group (its
+            // epilogue writes only the rows of the group it ran for); its prologue copies
+            // into the LDS that every wave has read its output pieces from
+            if (cur.g2 >= 0) {
+                cur.g = cur.g2;
+                cur.g2 = -1;
+                bare_barrier();
+                first = true;
+                continue;
             }
         }
         if (!has_next)
@@ -1000,14 +1130,11 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
 
 // ------------------------------------------------------------------------------ host side
 
-static void tiles_for(int mode, int cfg, const GemmArgs &a, int &tiles_m, int &tiles_n)
+static void tiles_for(int cfg, const GemmArgs &a, int &tiles_m, int &tiles_n)
 {
     const TileInfo &ti = kTiles[cfg];
     tiles_n = (a.n + ti.bn - 1) / ti.bn;
-    if (mode == MODE_CONTIG)
-        tiles_m = a.m / ti.bm;
-    else
-        tiles_m = (a.m + ti.bm - 1) / ti.bm;
+    tiles_m = (a.m + ti.bm - 1) / ti.bm;
 }
 
 // Workgroups for `total` tiles: one per tile, or for a persistent tile configuration at most
@@ -1021,16 +1148,26 @@ static int64_t workgroups(int64_t total, bool persistent, const GemmArgs &a)
     return total;
 }
 
+// Workgroups ahead of the tiles that serve listed straddling tile-rows (contiguous form,
+// 256-row tiles, one workgroup per tile), rounded up to whole rounds of the 8 XCDs
+static int64_t straddle_wgs(int mode, int bm, bool persistent, const GemmArgs &a, int tiles_n)
+{
+    if (mode != MODE_CONTIG || bm <= 128 || persistent || a.straddle_rows <= 0)
+        return 0;
+    return ((int64_t)a.straddle_rows * tiles_n + 7) / 8 * 8;
+}
+
 int64_t grid_size(int mode, int cfg, const GemmArgs &a)
 {
     if (cfg == CFG_STREAM64)
         return mode == MODE_DENSE ? stream_grid_size(a) : -1;
     int tiles_m, tiles_n;
-    tiles_for(mode, cfg, a, tiles_m, tiles_n);
+    tiles_for(cfg, a, tiles_m, tiles_n);
     int64_t g = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         g *= a.num_groups;
-    return workgroups(g, kTiles[cfg].persistent, a);
+    return workgroups(g, kTiles[cfg].persistent, a) +
+           straddle_wgs(mode, kTiles[cfg].bm, kTiles[cfg].persistent, a, tiles_n);
 }
 
 template <int BM, int BN, int WM, int WN, int DEPTH, bool PERSIST, int SF>
@@ -1045,7 +1182,7 @@ static void launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_
                            stream, a, tiles_m, tiles_n);
         break;
     case MODE_CONTIG:
-        if constexpr (SF != SF_UE8M0_PARTIAL)
+        if constexpr (SF != SF_UE8M0_PARTIAL && !(BM > 128 && PERSIST))
             hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST, SF>), g,
                                b, 0, stream, a, tiles_m, tiles_n);
         break;
@@ -1063,13 +1200,16 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     int tiles_m, tiles_n;
     const int cfg_threads = 64 * WM * WN;
     tiles_n = (a.n + BN - 1) / BN;
-    tiles_m = mode == MODE_CONTIG ? a.m / BM : (a.m + BM - 1) / BM;
+    // (contiguous: m is a multiple of 128; a 256-row tile past it reads no group indices there)
+    tiles_m = (a.m + BM - 1) / BM;
+    if (mode == MODE_CONTIG && BM > 128 && PERSIST)
+        return hipErrorInvalidConfiguration;  // straddling tiles need one workgroup per tile
     int64_t total = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         total *= a.num_groups;
     if (total <= 0 || total > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    const int64_t grid = workgroups(total, PERSIST, a);
+    const int64_t grid = workgroups(total, PERSIST, a) + straddle_wgs(mode, BM, PERSIST, a, tiles_n);
     dim3 g((unsigned)grid), b(cfg_threads);
     // UE8M0: MFMAs accumulate directly unless C is added inside the K loop or masked rows
     // skip MFMAs

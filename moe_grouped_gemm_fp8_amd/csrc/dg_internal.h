@@ -59,6 +59,8 @@ struct GemmArgs {
     int max_wgs;          // persistent tiles: workgroups to launch at most (the CU count);
                           // <= 0 launches one workgroup per tile
     int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
+    int straddle_rows;    // contiguous, 256-row tiles: listed straddling tile-rows whose second
+                          // group runs on workgroups ahead of the tiles (0: none)
 };
 
 // The MN-major-operand kernel (dg_layout.hip): the dense NN, TN and TT layouts (A stored

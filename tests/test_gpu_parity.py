@@ -202,6 +202,68 @@ def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     assert_parity(run_contiguous(p), ref, f"contiguous {cfg}")
 
 
+# 256-row tiles, one workgroup each: the groups are aligned to 128 rows only, so such a tile
+# can hold two groups (run once with each group's B) or end 128 rows past m_total.
+# counts -> 128-row blocks: [0,130,41,300,129] -> 1 1 | 2 3 | 3 3 | 4 4 (one straddle);
+# [41,0,300,1,130] -> 0 2 | 2 2 | 3 4 | 4 - (two straddles, the last tile half past m_total)
+# A straddle's second group runs on a workgroup of its own, ahead of the tiles, for up to
+# num_groups - 1 straddles (DG_STRADDLE_ROWS lowers that: 0 runs every second pass inside the
+# tile's own workgroup, 1 splits the two straddles of the second layout between both paths).
+@pytest.mark.parametrize("cfg,served", [("256x224w8", None), ("256x128w8", None),
+                                        (None, None), ("256x224w8", "0"), ("256x224w8", "1")])
+@pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
+def test_contiguous_256_row_tiles_across_group_boundaries(cfg, served, counts, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
+    # stress: a distinct power-of-two magnitude per group, so a row computed with another
+    # group's B is off by 2x or more
+    p = W.make_contiguous(5, sum(counts), 448, 640, seed=34, counts=counts, stress=True,
+                          pad_nan=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"contiguous 256-row {cfg} {counts}")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
+@pytest.mark.parametrize("cfg", ["256x224w8", "256x128w8"])
+def test_contiguous_256_row_tile_with_an_all_padding_half(cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_contiguous(3, 600, 256, 384, seed=35, counts=[200, 250, 150], pad_nan=True)
+    # blocks 0 0 | 1 1 | 2 2: blank block 2 (group 1's second half) and block 5
+    p.m_indices[256:384] = -1
+    p.m_indices[640:768] = -1
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"contiguous padding half {cfg}")
+    assert np.all(got[p.m_indices < 0] == W.BF16_SENTINEL), "padding rows were written"
+
+
+@pytest.mark.parametrize("served", [None, "0"])
+def test_contiguous_256_row_tiles_unordered_groups(served, monkeypatch):
+    # 128-row blocks 0 1 | 1 0 | 0 1: three straddles for two groups (one served slot), and
+    # 1 (-1..0) | 1 1: a straddle whose second block starts with padding rows, so the block-
+    # leading rows do not show it (its own workgroup runs both groups)
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x224w8")
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
+    p = W.make_contiguous(2, 768, 448, 384, seed=36, counts=[384, 384], stress=True)
+    p.m_indices[:] = np.repeat(np.array([0, 1, 1, 0, 0, 1], np.int32), 128)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"unordered served={served}")
+    assert not np.any(got == W.BF16_SENTINEL), "valid rows left unwritten"
+    q = W.make_contiguous(2, 512, 448, 384, seed=37, counts=[256, 256], stress=True)
+    q.m_indices[:] = np.repeat(np.array([1, 0, 1, 1], np.int32), 128)
+    q.m_indices[128:192] = -1
+    ref = oracle.m_grouped_contiguous(q.a, q.sfa, q.b, q.sfb, q.m_indices)
+    got = run_contiguous(q)
+    assert_parity(got, ref, f"hidden straddle served={served}")
+    assert np.all(got[q.m_indices < 0] == W.BF16_SENTINEL), "padding rows were written"
+    assert not np.any(got[q.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
 def test_contiguous_stress_routing():
     p = W.make_contiguous(4, 700, 384, 256, seed=32, stress=True)
     ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)

@@ -132,7 +132,8 @@ def test_dense_prefill_workload_sampled_rows():
 
 # ------------------------------------------------------------------------------ contiguous
 
-@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w8d4", "128x256w8"])
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w8d4", "128x256w8",
+                                 "256x224w8", "256x128w8"])
 def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -140,6 +141,18 @@ def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
                           pad_nan=True, ue8m0=True)
     ref = oracle.m_grouped_contiguous_ue8m0(p.a, p.sfa, p.b, p.sfb, p.m_indices)
     assert_parity(run_contiguous(p), ref, f"contiguous ue8m0 {cfg}")
+
+
+@pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
+def test_contiguous_256_row_tiles_across_group_boundaries(counts, monkeypatch):
+    # 128-row blocks 1 1 | 2 3 | 3 3 | 4 4, and 0 2 | 2 2 | 3 4 | 4 - (last tile past m_total)
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x224w8")
+    p = W.make_contiguous(5, sum(counts), 448, 640, seed=62, counts=counts, stress=True,
+                          pad_nan=True, ue8m0=True)
+    ref = oracle.m_grouped_contiguous_ue8m0(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"contiguous ue8m0 256-row {counts}")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
 def test_contiguous_workload_sampled_rows():
