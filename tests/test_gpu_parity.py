@@ -212,14 +212,15 @@ def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
 @pytest.mark.parametrize("cfg,served", [("256x224w8", None), ("256x128w8", None),
                                         (None, None), ("256x224w8", "0"), ("256x224w8", "1")])
 @pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
-def test_contiguous_256_row_tiles_across_group_boundaries(cfg, served, counts, monkeypatch):
+@pytest.mark.parametrize("n", [448, 400])
+def test_contiguous_256_row_tiles_across_group_boundaries(cfg, served, counts, n, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     if served is not None:
         monkeypatch.setenv("DG_STRADDLE_ROWS", served)
     # stress: a distinct power-of-two magnitude per group, so a row computed with another
-    # group's B is off by 2x or more
-    p = W.make_contiguous(5, sum(counts), 448, 640, seed=34, counts=counts, stress=True,
+    # group's B is off by 2x or more (n = 400: a ragged last N tile)
+    p = W.make_contiguous(5, sum(counts), n, 640, seed=34, counts=counts, stress=True,
                           pad_nan=True)
     ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
     got = run_contiguous(p)
@@ -277,7 +278,11 @@ def test_contiguous_all_padding_writes_nothing():
     assert np.all(got == W.BF16_SENTINEL)
 
 
-def test_contiguous_workload_sampled_rows():
+@pytest.mark.parametrize("served", [None, "0"])
+def test_contiguous_workload_sampled_rows(served, monkeypatch):
+    # served=0: every straddling tile runs its second group inside its own workgroup
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
     p = W.make_config("moe_contiguous", seed=0)                # 8 experts, 32768 rows, 4096 x 7168
     got = run_contiguous(p)
     pad = p.m_indices < 0
