@@ -260,16 +260,12 @@ int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, con
         if ((rc = get_layout_workspace(s, a_bytes + b_bytes, &ws)) != DG_OK)
             return rc;
         if (ws) {
-            const void *a_nt = a, *b_nt = b;
-            hipError_t e = hipSuccess;
-            if (a_mn) {  // A stored [k][m] -> [m][k]
-                e = dg::launch_transpose_u8(a, ws, k, m, s);
-                a_nt = ws;
-            }
-            if (e == hipSuccess && b_mn) {  // B stored [k][n] -> [n][k]
-                b_nt = (const uint8_t *)ws + a_bytes;
-                e = dg::launch_transpose_u8(b, (uint8_t *)ws + a_bytes, k, n, s);
-            }
+            // A stored [k][m] -> [m][k] and B stored [k][n] -> [n][k], in one launch
+            const void *a_nt = a_mn ? ws : a;
+            const void *b_nt = b_mn ? (const void *)((const uint8_t *)ws + a_bytes) : b;
+            const hipError_t e = dg::launch_transpose_u8(
+                a_mn ? a : nullptr, ws, k, m, b_mn ? b : nullptr, (uint8_t *)ws + a_bytes, k, n,
+                s);
             if (e != hipSuccess)
                 return fail(DG_ERR_HIP, "transpose launch failed: %s", hipGetErrorString(e));
             return gemm_nt(dg::SF_FP32, a_nt, sfa, ld_sfa, b_nt, sfb, c, d, m, n, k, stream);

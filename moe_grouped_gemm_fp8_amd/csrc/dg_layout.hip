@@ -498,14 +498,26 @@ hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 // ds_read_b64_tr_b8, whose 16-lane groups turn an 8 x 16 byte block into 16 lanes of 8
 // consecutive row bytes; wave w writes output rows 16 w .. 16 w + 15, 32 consecutive bytes
 // of each per instruction.
-__global__ __launch_bounds__(256) void dg_transpose_u8_kernel(const uint8_t *__restrict__ x,
-                                                               uint8_t *__restrict__ y, int rows,
-                                                               int cols, int tiles_c)
+// One launch moves up to two operands (A and B of the TN layout): workgroups [0, p0.tiles)
+// transpose p0, the rest p1.
+struct U8Transpose {
+    const uint8_t *x;
+    uint8_t *y;
+    int rows, cols, tiles_c, tiles;
+};
+
+__global__ __launch_bounds__(256) void dg_transpose_u8_kernel(U8Transpose p0, U8Transpose p1)
 {
     constexpr int PITCH = 80;
     __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
+    const bool second = (int)blockIdx.x >= p0.tiles;
+    const int bid = (int)blockIdx.x - (second ? p0.tiles : 0);
+    const uint8_t *__restrict__ x = second ? p1.x : p0.x;
+    uint8_t *__restrict__ y = second ? p1.y : p0.y;
+    const int rows = second ? p1.rows : p0.rows, cols = second ? p1.cols : p0.cols;
+    const int tiles_c = second ? p1.tiles_c : p0.tiles_c;
     const int tid = threadIdx.x;
-    const int r0 = (blockIdx.x / tiles_c) * 64, c0 = (blockIdx.x % tiles_c) * 64;
+    const int r0 = (bid / tiles_c) * 64, c0 = (bid % tiles_c) * 64;
     {
         const int r = tid >> 2, c = (tid & 3) * 16;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -531,16 +543,30 @@ __global__ __launch_bounds__(256) void dg_transpose_u8_kernel(const uint8_t *__r
     }
 }
 
-hipError_t launch_transpose_u8(const void *x, void *y, int rows, int cols, hipStream_t stream)
+hipError_t launch_transpose_u8(const void *x0, void *y0, int rows0, int cols0, const void *x1,
+                               void *y1, int rows1, int cols1, hipStream_t stream)
 {
-    if (rows % 64 != 0 || cols % 16 != 0)
-        return hipErrorInvalidValue;
-    const int tiles_c = (cols + 63) / 64;
-    const int64_t grid = (int64_t)(rows / 64) * tiles_c;
-    if (grid <= 0 || grid > 0x7fffffff)
-        return grid == 0 ? hipSuccess : hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(dg_transpose_u8_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint8_t *)x, (uint8_t *)y, rows, cols, tiles_c);
+    U8Transpose p[2] = {{(const uint8_t *)x0, (uint8_t *)y0, rows0, cols0, 1, 0},
+                        {(const uint8_t *)x1, (uint8_t *)y1, rows1, cols1, 1, 0}};
+    int64_t grid = 0;
+    for (U8Transpose &t : p) {
+        if (!t.x || t.rows <= 0 || t.cols <= 0)
+            continue;  // no job
+        if (t.rows % 64 != 0 || t.cols % 16 != 0)
+            return hipErrorInvalidValue;
+        t.tiles_c = (t.cols + 63) / 64;
+        const int64_t tiles = (int64_t)(t.rows / 64) * t.tiles_c;
+        if (tiles > 0x3fffffff)
+            return hipErrorInvalidConfiguration;
+        t.tiles = (int)tiles;
+        grid += tiles;
+    }
+    if (grid == 0)
+        return hipSuccess;
+    if (p[0].tiles == 0)
+        std::swap(p[0], p[1]);
+    hipLaunchKernelGGL(dg_transpose_u8_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p[0],
+                       p[1]);
     return hipGetLastError();
 }
 
