@@ -50,6 +50,7 @@
 
 #include "dg_device.h"
 #include "dg_internal.h"
+#include "dg_tiles.h"
 
 namespace dg {
 
@@ -245,14 +246,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         tile_end = tile_id + 1;
         tile_step = 1;
     } else {
-        const int G = gridDim.x - E, q = G >> 3, r = G & 7, x = bid & 7;
-        const int px = q + (x < r ? 1 : 0);
-        const int wx = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-        // 32-bit products: the host launches fewer workgroups than tiles only while
-        // total * G < 2^31
-        tile_id = (int)((uint32_t)(total * wx) / (uint32_t)G) + (bid >> 3);
-        tile_end = (int)((uint32_t)(total * (wx + px)) / (uint32_t)G);
-        tile_step = px;
+        const TileRange tr = xcd_tile_range(total, (int)gridDim.x, E, (int)blockIdx.x);
+        tile_id = tr.first;
+        tile_end = tr.end;
+        tile_step = tr.step;
     }
     if (tile_id >= tile_end)
         return;
@@ -1138,12 +1135,10 @@ static void tiles_for(int cfg, const GemmArgs &a, int &tiles_m, int &tiles_n)
 }
 
 // Workgroups for `total` tiles: one per tile, or for a persistent tile configuration at most
-// one per CU (each then loops over its share), as long as the kernel's 32-bit tile-range
-// arithmetic (total * workgroups < 2^31) holds.
+// one per CU (each then loops over its share; xcd_tile_range forms the shares in 64 bits)
 static int64_t workgroups(int64_t total, bool persistent, const GemmArgs &a)
 {
-    if (persistent && a.max_wgs > 0 && total > a.max_wgs &&
-        total * (int64_t)a.max_wgs < ((int64_t)1 << 31))
+    if (persistent && a.max_wgs > 0 && total > a.max_wgs)
         return a.max_wgs;
     return total;
 }

@@ -168,7 +168,8 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         t = blockIdx.x - g * per_g;
     } else {
         const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
-        const int lo = (x * per_g) >> 3, len = (((x + 1) * per_g) >> 3) - lo;
+        const int lo = (int)(((int64_t)x * per_g) >> 3);
+        const int len = (int)((((int64_t)x + 1) * per_g) >> 3) - lo;
         if (len == 0)
             return;
         if (i >= len)

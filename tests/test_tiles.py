@@ -1,0 +1,43 @@
+"""The XCD-aware tile mapping (``dg_tiles.h``, used by the GEMM kernels) checked on the host:
+every tile id is assigned to exactly one workgroup, for persistent grids (fewer workgroups
+than tiles), one workgroup per tile (up to 75008 tiles, where 32-bit products of the tile
+count and the grid would wrap), and with straddle-serving workgroups ahead of the tiles.
+CPU only: the header is plain C++ and is compiled here with g++."""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc")
+SRC = os.path.join(ROOT, "tests", "native", "tile_cover.cpp")
+
+
+@pytest.fixture(scope="module")
+def tile_cover(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("tiles") / "tile_cover")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-Wall", "-Werror", "-I", CSRC, SRC, "-o", exe],
+                   check=True)
+    return exe
+
+
+def _run(exe, cases):
+    args = [str(v) for case in cases for v in case]
+    out = subprocess.run([exe, *args], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.count("ok ") == len(cases)
+
+
+@pytest.mark.parametrize("lead", [0, 8, 24])
+def test_one_workgroup_per_tile(tile_cover, lead):
+    # G == total: 46341 is the first count whose total * G passes 2^31, 65536 the first whose
+    # product passes 2^32, 75008 the 256x224 tile count of a 65536 x 65536 output
+    _run(tile_cover, [(g, g, lead) for g in list(range(1, 10)) + [46341, 65536, 75008]])
+
+
+@pytest.mark.parametrize("lead", [0, 16])
+def test_persistent_workgroups(tile_cover, lead):
+    cases = [(t, g, lead) for g in range(1, 10) for t in (g, g + 1, 1000, 46341, 65536, 75008)]
+    cases += [(t, g, lead) for g in (255, 256, 46341, 65536)
+              for t in (g, g + 7, 3 * g + 5, 1 << 21)]
+    _run(tile_cover, cases)
