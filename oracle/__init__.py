@@ -247,18 +247,19 @@ def swiglu(x_bits) -> np.ndarray:
 
 def e4m3_nearest(y) -> np.ndarray:
     """uint8 e4m3 codes nearest to float64 y (|y| <= 448), ties to the even code.  The format
-    is sign-magnitude: the magnitude code is the one among 0x00 .. 0x7E (the finite
-    non-negative values of the decode table) nearest to |y|, and a negative y (or -0) sets
+    is sign-magnitude and its non-negative finite codes 0x00 .. 0x7E increase with their
+    value, so the magnitude code is the lower or the upper end of the interval of the decode
+    table that holds |y|: the nearer one, or on a tie the even one.  A negative y (or -0) sets
     the sign bit."""
     tab = e4m3_table()
-    mags = np.arange(0x7F)                                   # 0 .. 448
-    vals = tab[mags]
+    vals = tab[:0x7F]                                        # 0 .. 448, increasing
     y = np.asarray(y, dtype=np.float64)
-    d = np.abs(np.abs(y)[..., None] - vals)
-    cand = d == d.min(axis=-1, keepdims=True)
-    even = cand & ((mags & 1) == 0)
-    pick = np.where(even.any(axis=-1, keepdims=True), even, cand)
-    code = mags[np.argmax(pick, axis=-1)]
+    a = np.abs(y)
+    lo = np.clip(np.searchsorted(vals, a, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
     return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 

@@ -1,7 +1,8 @@
 """Parity of the K-grouped TN GEMM (MoE weight gradient) on the GPU with the CPU oracle, on the
 same seeded inputs: ragged M and N tails, groups of every extent from zero blocks up, C added,
 accumulated in place and absent, a single group, the full group table, and the full-size
-workload on sampled rows.  D is FP32, compared under the FP32-output rule (per-group rms)."""
+workload compared in full.  D is FP32, compared under the same rule as the bf16 outputs:
+|d - d_ref| <= 1e-2 |d_ref| + 1e-3 rms(D_ref), rms over all of D."""
 import sys
 
 import numpy as np
@@ -12,7 +13,7 @@ import moe_grouped_gemm_fp8_amd as dg
 import oracle
 import workloads as W
 from gpu_util import DEV, dev
-from tolerance import kgrouped_violations
+from tolerance import tol_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +45,7 @@ def run(p, c_mode="given"):
 
 def check(got, ref, what):
     assert not np.isnan(got).any(), f"{what}: elements left unwritten"
-    bad = kgrouped_violations(got, ref)
+    bad = tol_violations(got, ref)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside the tolerance, "
@@ -98,11 +99,25 @@ def test_host_rejects_bad_extents():
         assert e.value.code == code, ks
 
 
-def test_wgrad_workload_sampled_rows():
+def _k_grouped_ref_by_column_chunks(p, chunk=256):
+    """The oracle on every column of A, in chunks of columns run on a thread pool: each output
+    row m depends on column m of A and its scales only, so the chunks give exactly the whole
+    result (numpy's products and element-wise passes run outside the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((p.num_groups, p.m, p.n), dtype=np.float64)
+
+    def one(m0):
+        cols = slice(m0, min(p.m, m0 + chunk))
+        out[:, cols] = oracle.k_grouped_tn(np.ascontiguousarray(p.a[:, cols]),
+                                           np.ascontiguousarray(p.sfa[:, cols]), p.b, p.sfb, p.ks)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(one, range(0, p.m, chunk)))
+    return out
+
+
+def test_wgrad_workload_full():
     p = W.make_config("moe_wgrad", seed=0)                     # 8 experts, 4096 x 7168
     got = run(p, "none")
     assert not np.isnan(got).any(), "some outputs were never written"
-    rng = np.random.default_rng(120)
-    rows = np.unique(np.concatenate([[0, 1, p.m - 1], rng.choice(p.m, 5, replace=False)]))
-    ref = oracle.k_grouped_tn(p.a[:, rows], p.sfa[:, rows], p.b, p.sfb, p.ks)
-    check(got[:, rows], ref, "moe_wgrad")
+    check(got, _k_grouped_ref_by_column_chunks(p), "moe_wgrad")

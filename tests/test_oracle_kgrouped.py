@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from tolerance import kgrouped_violations
+from tolerance import tol_violations
 
 
 def _decode(bits):
@@ -121,17 +121,17 @@ def test_planted_faults_fail_the_tolerance():
         args = dict(a=p.a, sfa=p.sfa, b=p.b, sfb=p.sfb, ks=p.ks, c=p.c)
         args.update(kw)
         bad = oracle.k_grouped_tn(**args)
-        assert kgrouped_violations(bad.astype(np.float32), ref).any(), name
+        assert tol_violations(bad.astype(np.float32), ref).any(), name
     q = W.make_k_grouped(2, 300, 32, 32, seed=9, counts=[140, 160], with_c=True, c_std=30.0)
     refc = oracle.k_grouped_tn(q.a, q.sfa, q.b, q.sfb, q.ks, q.c)
     bad = oracle.k_grouped_tn(q.a, q.sfa, q.b, q.sfb, q.ks)
-    assert kgrouped_violations(bad.astype(np.float32), refc).any(), "c_dropped"
+    assert tol_violations(bad.astype(np.float32), refc).any(), "c_dropped"
 
 
 def test_tolerance_accepts_fp32_rounding_of_the_exact_result():
     p = W.make_k_grouped(3, 700, 64, 64, seed=10, counts=[300, 150, 250], with_c=True)
     ref = oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c)
-    assert not kgrouped_violations(ref.astype(np.float32), ref).any()
+    assert not tol_violations(ref.astype(np.float32), ref).any()
 
 
 def test_rejects_bad_group_extents():

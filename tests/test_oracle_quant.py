@@ -56,7 +56,15 @@ def test_cast_invariants_and_scale_layout():
     seg = h.reshape(37, 4, 128)
     amax = np.abs(seg).max(axis=2)
     scale = sf[:, :37].T
-    assert np.array_equal(scale, np.maximum(amax, 1e-4) / 448.0)
+    # the scale maps each segment's largest magnitude onto the format's largest finite value,
+    # read off the decode table (0x7E): before any clip, max |h| / scale equals it within one
+    # float64 ulp, and no element of the segment exceeds it (a denominator of 447 or 449
+    # fails both ways)
+    top = oracle.e4m3_table()[0x7E]
+    big = amax >= 1e-4
+    ratio = amax[big] / scale[big]
+    assert np.all(np.abs(ratio - top) <= np.spacing(top)), ratio[np.abs(ratio - top) > np.spacing(top)][:4]
+    assert np.all(np.abs(seg / scale[:, :, None]) <= top + np.spacing(top))
     # the largest element of every non-zero segment is cast to +-448
     qs = q.reshape(37, 4, 128)
     for r in range(37):
@@ -75,5 +83,21 @@ def test_zero_segments_give_the_floor_scale_and_zero_codes():
     g = np.zeros((2, 256), np.float32)
     u = np.random.default_rng(4).standard_normal((2, 256)).astype(np.float32)
     h, sf, q = oracle.swiglu_quant(_bits(g, u))
-    assert np.all(sf[:, :2] == 1e-4 / 448.0)
+    # a zero segment takes the floor: its scale maps 1e-4 onto the largest e4m3 value
+    top = oracle.e4m3_table()[0x7E]
+    assert np.all(np.abs(1e-4 / sf[:, :2] - top) <= np.spacing(top))
     assert np.all((q == 0) | (q == 0x80))
+
+
+def test_scale_of_a_known_segment():
+    # gate 20 makes silu(gate) = 20 / (1 + e^-20); with up = 2 at one column and 1 elsewhere the
+    # segment's largest magnitude is 40 / (1 + e^-20), so the scale is that over 448, and the
+    # codes are 448 at that column and the nearest e4m3 of 448 / 2 = 224 elsewhere
+    gate = np.full((1, 128), 20.0, np.float32)
+    up = np.ones((1, 128), np.float32)
+    up[0, 5] = 2.0
+    h, sf, q = oracle.swiglu_quant(_bits(gate, up))
+    amax = 40.0 / (1.0 + np.exp(-20.0))
+    assert abs(sf[0, 0] * 448.0 / amax - 1.0) <= 2.0 ** -52
+    tab = oracle.e4m3_table()
+    assert tab[q[0, 5]] == 448.0 and np.all(tab[np.delete(q[0], 5)] == 224.0)

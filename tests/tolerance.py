@@ -18,30 +18,13 @@ def rms(x: np.ndarray) -> float:
 def tol_violations(d: np.ndarray, ref: np.ndarray, rel: float = REL,
                    rms_frac: float = RMS) -> np.ndarray:
     """Boolean mask of elements outside the tolerance (NaN anywhere counts as a violation).
-    ``rel`` and ``rms_frac`` replace the bf16-output rule's terms for the FP32-output form."""
+    The same rule holds for the bf16 outputs and for the FP32 output of the K-grouped form;
+    for the latter every element of D[G, M, N] is computed, so the rms is over all of it."""
     d = np.asarray(d, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     bound = rel * np.abs(ref) + rms_frac * rms(ref)
     err = np.abs(d - ref)
     return ~(err <= bound)
-
-
-# FP32-output rule of the K-grouped form (D[g] = C[g] + ..., no bf16 rounding): the relative
-# term drops to 1e-3; the cancellation term stays 1e-3 of the rms, taken per group, since a
-# group's rounding scales with its own magnitude (empty groups are exact and would only deflate
-# a rms over all groups).
-KG_REL = 1e-3
-KG_RMS = 1e-3
-
-
-def kgrouped_violations(d: np.ndarray, ref: np.ndarray) -> np.ndarray:
-    """Violation mask of [G, ...] results with one rms per group (leading axis)."""
-    d = np.asarray(d, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    axes = tuple(range(1, ref.ndim))
-    g_rms = np.sqrt(np.mean(ref * ref, axis=axes, keepdims=True)) if ref.size else ref
-    bound = KG_REL * np.abs(ref) + KG_RMS * g_rms
-    return ~(np.abs(d - ref) <= bound)
 
 
 def within_tol(d, ref) -> bool:
