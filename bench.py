@@ -2,11 +2,13 @@
 """Throughput of the fine-grained-scaled FP8 GEMM library on one MI355X.
 
 One step = one call of the library's hot path on one batch of seeded synthetic input that
-is already resident in device memory.  The headline workload is the dense prefill GEMM
-M=4096 N=7168 K=2048 with an FP32 C (D = C + A @ B.T, bf16 D); the other workloads (small
-dense, skinny dense, contiguous MoE, masked MoE replayed from a captured graph, their UE8M0
-forms, the K-grouped MoE weight gradient, the dense NN/TN/TT layouts and the fused SwiGLU
-FP8 cast) are timed too and reported under "workloads".  Inputs rotate over several device-resident copies whose
+is already resident in device memory.  The headline workload is the largest one, the
+contiguous M-grouped MoE GEMM (8 experts sharing N=4096, K=7168, 32768 routed token rows
+padded per expert to multiples of 128, bf16 D); the other workloads (the dense prefill GEMM
+M=4096 N=7168 K=2048 with an FP32 C, small and skinny dense, masked MoE replayed from a
+captured graph, the UE8M0 forms, the K-grouped MoE weight gradient, the dense NN/TN/TT layouts
+and the fused SwiGLU FP8 cast) are timed too and reported under "workloads", each with its own
+roofline block.  Inputs rotate over several device-resident copies whose
 total exceeds the 256 MB Infinity Cache, so every launch reads its operands from HBM.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -110,7 +112,7 @@ def _capture(torch, sets, call, per_graph=1):
 
     def cap(chunk):
         gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
+        with torch.cuda.graph(gr, stream=side):        # the stream whose workspaces exist
             for s in chunk:
                 call(s)
         return gr
@@ -204,6 +206,7 @@ def make_contiguous_case(torch, dg, W, ue8m0=False):
                     rotating_copies=len(c.sets))
     c.flops = lambda i: 2.0 * valid * p.n * p.k
     c.bytes = lambda i: float(nbytes)
+    c.problem = p
     return c
 
 
@@ -356,50 +359,121 @@ def time_case(torch, case, steps, warmup):
                 steps=steps, flops=flops, bytes=nbytes)
 
 
-def summarize(res):
+# workloads bound by HBM (their roofline is bytes); the others by the FP8 MFMA rate
+HBM_BOUND = ("dense_skinny", "moe_masked", "dense_skinny_ue8m0", "moe_masked_ue8m0",
+             "moe_swiglu_quant", "dense_small")
+
+
+def summarize(name, res):
     per = res["per_launch_s"]
     avg = float(res["avg_s"])
     tflops = float(res["flops"].mean() / avg / 1e12)
     gbs = float(res["bytes"].mean() / avg / 1e9)
+    if name in HBM_BOUND:
+        roof = dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=gbs / PEAK_HBM_GBS)
+    else:
+        roof = dict(bound="mfma", achieved=tflops, peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=tflops / PEAK_FP8_TFLOPS)
+    roof["traffic"] = measured_traffic(name)
+    roof["algorithmic_bytes"] = float(res["bytes"].mean())
     return dict(avg_kernel_us=avg * 1e6, timing=res["timing"],
                 per_launch_event_us=float(per.mean() * 1e6),
                 p50_us=float(np.percentile(per, 50) * 1e6),
                 p10_us=float(np.percentile(per, 10) * 1e6),
                 p90_us=float(np.percentile(per, 90) * 1e6), tflops=tflops, hbm_gbs=gbs,
-                frac_fp8_peak=tflops / PEAK_FP8_TFLOPS, frac_hbm_peak=gbs / PEAK_HBM_GBS)
+                frac_fp8_peak=tflops / PEAK_FP8_TFLOPS, frac_hbm_peak=gbs / PEAK_HBM_GBS,
+                roofline=roof)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rows(W, p, rows):
+    """One oracle call on the first `rows` rows of the workload's A (all of N and K); returns
+    the valid-row FLOPs it computed."""
+    import oracle
+    sfa, sfb = p.sfa, p.sfb
+    if sfa.dtype == np.int32:                         # packed UE8M0: the oracle decodes them
+        sfa = oracle.ue8m0_decode(sfa, 0, p.k // 128)
+        sfb = oracle.ue8m0_decode(sfb, sfb.ndim - 1, p.k // 128)
+    sub_sfa = W.mn_major(sfa[:, :rows].T)
+    if hasattr(p, "m_indices"):                       # contiguous MoE
+        idx = p.m_indices[:rows]
+        oracle.m_grouped_contiguous(p.a[:rows], sub_sfa, p.b, sfb, idx)
+        return 2.0 * float((idx >= 0).sum()) * p.n * p.k
+    oracle.fp8_gemm_nt(p.a[:rows], sub_sfa, p.b, sfb, None if p.c is None else p.c[:rows])
+    return 2.0 * rows * p.n * p.k
+
+
+# the oracle on the two small dense workloads (whole problems), on one thread, in a child process
+# (so the parent's thread pool is left as it is)
+_ONE_THREAD = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle, workloads as W
+oracle.set_num_threads(1)
+out = {}
+for name in ("dense_small", "dense_skinny"):
+    p = W.make_config(name, seed=0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 2.0:
+            break
+    out[name] = dict(tflops=2.0 * p.m * p.n * p.k * reps / dt / 1e12, reps=reps,
+                     seconds=round(dt, 2), threads=oracle.num_threads())
+print(json.dumps(out))
+"""
 
 
 def cpu_baseline(W, case, target_s):
     """The CPU oracle on a bounded sample of the workload: the first rows of A (all of N and K),
-    grown until one call takes a good part of `target_s`, then repeated to about `target_s`."""
+    grown until one call takes a good part of `target_s`, then repeated to about `target_s`;
+    plus the two small dense workloads in full on one thread."""
+    import subprocess
+
     import oracle
     p = case.problem
-    sfa, sfb = p.sfa, p.sfb
-    if sfa.dtype == np.int32:                         # packed UE8M0: the oracle decodes them
-        sfa = oracle.ue8m0_decode(sfa, 0, p.k // 128)
-        sfb = oracle.ue8m0_decode(sfb, 1, p.k // 128)
+    m_rows = p.m_total if hasattr(p, "m_total") else p.m
     log("timing the CPU oracle on a row sample of the workload")
     rows = 2
     while True:
         t0 = time.perf_counter()
-        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(sfa[:, :rows].T), p.b, sfb,
-                           None if p.c is None else p.c[:rows])
+        _oracle_rows(W, p, rows)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or rows >= p.m:
+        if dt >= target_s / 4 or rows >= m_rows:
             break
-        rows = int(min(p.m, max(rows * 2, rows * target_s / 4 / max(dt, 1e-3))))
-    reps, total = 1, dt
-    while total < target_s:
-        t0 = time.perf_counter()
-        oracle.fp8_gemm_nt(p.a[:rows], W.mn_major(sfa[:, :rows].T), p.b, sfb,
-                           None if p.c is None else p.c[:rows])
-        total += time.perf_counter() - t0
+        rows = int(min(m_rows, max(rows * 2, rows * target_s / 4 / max(dt, 1e-3))))
+    flops = 0.0
+    t_all = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t_all < target_s:
+        flops += _oracle_rows(W, p, rows)
         reps += 1
-    flops = 2.0 * rows * p.n * p.k * reps
-    return dict(value=flops / total / 1e12, unit="TFLOPS", cores=oracle.num_threads(),
-                kind="oracle",
-                sample=f"{reps} x {rows} of {p.m} rows of the {case.name} workload (all N={p.n}, "
-                       f"K={p.k}), {total:.1f} s of float64 work")
+    total = time.perf_counter() - t_all
+    out = dict(value=flops / total / 1e12, unit="TFLOPS", cores=oracle.num_threads(),
+               kind="oracle", cpu_model=_cpu_model(),
+               sample=f"{reps} x the first {rows} of {m_rows} rows of the {case.name} workload "
+                      f"(all N={p.n}, K={p.k}), {total:.1f} s of float64 work")
+    log("timing the CPU oracle on one thread (dense_small, dense_skinny)")
+    r = subprocess.run([sys.executable, "-c", _ONE_THREAD, ROOT], capture_output=True,
+                       text=True, timeout=120)
+    if r.returncode == 0 and r.stdout.strip():
+        out["one_thread"] = json.loads(r.stdout.strip().splitlines()[-1])
+    else:
+        out["one_thread"] = dict(error=(r.stderr or "")[-300:])
+    return out
 
 
 def calibration_copy(torch):
@@ -425,7 +499,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dense_prefill",
+    ap.add_argument("--workload", default="moe_contiguous",
                     choices=["dense_small", "dense_prefill", "dense_skinny", "moe_contiguous",
                              "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
                              "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad",
@@ -483,7 +557,7 @@ def main():
             else max(20, args.steps // 2))
         log(f"timing {name}: {args.warmup} warm-up + {steps} steps")
         res = time_case(torch, case, steps, args.warmup)
-        summ = summarize(res)
+        summ = summarize(name, res)
         summ["config"] = case.config
         results[name] = summ
         log(f"{name}: {summ['avg_kernel_us']:.1f} us/launch, {summ['tflops']:.1f} TFLOPS, "
@@ -499,16 +573,9 @@ def main():
     total_flops = float(res["flops"].sum())
     value = total_flops / res["total_s"] / 1e12
     dom = case.name
-    traffic = measured_traffic(dom)
-    achieved = summ["tflops"]
-    roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_FP8_TFLOPS, traffic=traffic,
-                    kernel_avg_us=summ["avg_kernel_us"], hbm_gbs_algorithmic=summ["hbm_gbs"],
+    roofline = dict(summ["roofline"], kernel_avg_us=summ["avg_kernel_us"],
+                    hbm_gbs_algorithmic=summ["hbm_gbs"],
                     hbm_frac_algorithmic=summ["hbm_gbs"] / PEAK_HBM_GBS)
-    if dom in ("dense_skinny", "moe_masked", "dense_skinny_ue8m0", "moe_masked_ue8m0",
-               "moe_swiglu_quant"):
-        roofline.update(bound="hbm", achieved=summ["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
-                        frac=summ["hbm_gbs"] / PEAK_HBM_GBS)
     out = {
         "metric": METRIC,
         "value": value,

@@ -24,7 +24,7 @@
  *    (thread-local).  A launch failure reported by the HIP runtime returns DG_ERR_HIP.
  *  - Preconditions: K > 0 and K % 128 == 0; N > 0 and N % 16 == 0; row counts >= 0 (zero
  *    rows is a no-op that returns DG_OK without touching the device); ld_sfa % 4 == 0 and
- *    ld_sfa >= the number of A rows; A, B, D and C 16-byte aligned; sfa, sfb 4-byte aligned.
+ *    ld_sfa >= the number of A rows; A, B, D, C and sfa 16-byte aligned; sfb 4-byte aligned.
  *  - Values in device memory cannot be checked without a synchronization, so their
  *    behaviour is defined instead (see each call).
  */
@@ -55,10 +55,12 @@ typedef enum {
  *   c      FP32 [m, n] or NULL (then C = 0); must not overlap d
  *   d      bf16 [m, n], written in full
  * Skinny shapes may split K across workgroups; the partial sums then go through a
- * library-owned workspace (allocated once per device on first use, outside stream capture)
- * and are reduced in a fixed order, so results are deterministic.  Concurrent calls on
- * different streams of one device that both split K share that workspace and must not
- * overlap in time.
+ * library-owned workspace and are reduced in a fixed order, so results are deterministic.
+ * There is one workspace per (device, stream): it is allocated by the first such call made on
+ * that stream outside graph capture, grown (never freed) when a call needs more, and a graph
+ * keeps using the workspace of the stream it was captured on.  So calls on different streams
+ * may run concurrently; calls on one stream are ordered by the stream.  A call captured on a
+ * stream that has no workspace yet runs a slower tile configuration that needs none.
  */
 int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
                    const float *sfb, const float *c, void *d, int m, int n, int k,
@@ -95,7 +97,10 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
  *   d         bf16 [num_groups, m_max, n]
  *   masked_m  device int32 [num_groups]: valid rows of each group, read on the device at run
  *             time (clamped to [0, m_max]); rows at or beyond it are not written
- *   expected_m  host hint of the typical valid-row count for the tile choice (<= 0: m_max/2)
+ *   expected_m  host hint of the typical valid-row count (<= 0: m_max/2), printed with the
+ *             tile choice under DG_PRINT_CONFIGS.  On gfx950 the measured fastest tile does
+ *             not depend on it (256-row tiles whenever m_max > 128, at every expected count
+ *             from 8 to 128 rows), so the choice is made from m_max, n and k alone.
  * The call performs no allocation, no host synchronization and no host read of device
  * memory, so it can be captured in a hipGraph and replayed after masked_m is rewritten.
  */
@@ -138,12 +143,12 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void *a, const int32_t *sfa, int
  *   B "t": e4m3 [n][k] (as in dg_fp8_gemm_nt)    B "n": e4m3 [k][n] (N contiguous)
  * The mathematical operation, the scales (sfa MN-major [k/128][ld_sfa], 1x128 segments of A's
  * rows; sfb [ceil(n/128)][k/128], 128x128 blocks of B), C, D and the error behaviour are those
- * of dg_fp8_gemm_nt.  In addition: sfa 16-byte aligned, m % 16 == 0 when A is stored [k][m],
- * and k * max(m, n) < 2^31.  MN-major operands are transposed into a per-device workspace
- * (allocated or grown by a call made outside graph capture, at least doubling; a replaced
- * workspace is kept until the process ends, since captured graphs may still use it; calls
- * overlapping on one device share it and must not run concurrently); a captured call finding
- * it too small reads the operands directly instead.
+ * of dg_fp8_gemm_nt.  In addition: m % 16 == 0 when A is stored [k][m], and
+ * k * max(m, n) < 2^31.  MN-major operands are transposed into a library-owned workspace, one
+ * per (device, stream), allocated or grown (at least doubling) by a call made outside graph
+ * capture; a replaced workspace is kept until the process ends, since captured graphs may
+ * still use it.  A captured call whose stream has no large enough workspace reads the
+ * MN-major operands directly instead (a slower kernel that needs none).
  */
 int dg_fp8_gemm_nn(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
                    const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
@@ -189,21 +194,31 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void *a, const float *sfa, const v
 int dg_swiglu_fp8_quant(const void *x, void *q, float *sfa, int64_t ld_sfa, int m, int i,
                         void *stream);
 
-/* Row alignment of each group segment in the contiguous layout: 128 (the M block size). */
+/* Row alignment of each group segment in the contiguous layout: 128 (the M block size).
+ * pt.news.hada.io, "Utilitários e variáveis de ambiente" (get_mk_alignment_for_contiguous_layout)
+ * and "GEMM denso e grouped" (each expert segment aligned to the GEMM M block).  No error. */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 
-/* Smallest valid ld_sfa for m rows: m rounded up to a multiple of 4 (16-byte columns). */
+/* Smallest valid ld_sfa for m rows: m rounded up to a multiple of 4, so that each K-block
+ * column of the MN-major A scales starts on a 16-byte boundary; 0 for m <= 0.
+ * pt.news.hada.io, "Utilitários e variáveis de ambiente" (get_tma_aligned_size: the alignment
+ * the transposed LHS scale layout needs) and "Interface GEMM e restrições de layout" (LHS
+ * scale transposed and aligned).  No error. */
 int64_t dg_get_sf_aligned_m(int64_t m);
 
 /* Cap (n > 0) or reset (n <= 0) the number of compute units the tile heuristic plans for;
- * returns the previous cap (0 = none).  Mirrors the pages' set_num_sms / get_num_sms. */
+ * returns the previous cap (0 = none).  pt.news.hada.io, "Utilitários e variáveis de
+ * ambiente" (set_num_sms: the number of SMs the kernels use).  Process-wide, not per device;
+ * no error. */
 int dg_set_num_cus(int n);
 
-/* Compute units the heuristic plans for on the current device (the cap if set), or a
- * negative dg_status if no device is available. */
+/* Compute units the heuristic plans for on the current device (the cap if set), or
+ * DG_ERR_HIP if no device is available.  pt.news.hada.io, "Utilitários e variáveis de
+ * ambiente" (get_num_sms). */
 int dg_get_num_cus(void);
 
-/* Message for the most recent non-OK return on this thread ("" if none). */
+/* Message for the most recent non-OK return on this thread ("" after an OK return).  The pages
+ * define no error convention for a C interface; this one and dg_status are the library's own. */
 const char *dg_last_error(void);
 
 #ifdef __cplusplus

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 #include <set>
 #include <string>
@@ -58,8 +59,11 @@ int check_common(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
         return fail(DG_ERR_MISALIGNED, "ld_sfa=%lld is not a multiple of 4", (long long)ld_sfa);
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16))
         return fail(DG_ERR_MISALIGNED, "A, B and D must be 16-byte aligned");
-    if (!aligned(sfa, 4) || !aligned(sfb, 4))
-        return fail(DG_ERR_MISALIGNED, "scale pointers must be 4-byte aligned");
+    // the A scales are copied 16 bytes (four rows) at a time from sfa + row
+    if (!aligned(sfa, 16))
+        return fail(DG_ERR_MISALIGNED, "sfa must be 16-byte aligned");
+    if (!aligned(sfb, 4))
+        return fail(DG_ERR_MISALIGNED, "sfb must be 4-byte aligned");
     return DG_OK;
 }
 
@@ -85,35 +89,42 @@ int device_cus(int *out)
     return DG_OK;
 }
 
-// Split-K workspace of the streaming kernel: one per device, allocated on the first call that
-// needs it while the stream is not being captured, then reused.  Calls that overlap on one
-// device (different streams) share it and must not run concurrently.
-struct Workspace {
-    float *partials = nullptr;
-    size_t partial_floats = 0;
-};
-constexpr size_t kWsFloats = size_t(16) << 20;  // 64 MiB of FP32 partial tiles
+// Library-owned device workspaces (the split-K partial tiles of the streaming kernel, the
+// transposed operands of the dense NN/TN/TT layouts): one per (device, stream, purpose), so that
+// calls on different streams never share one.  A workspace is allocated on the first call that
+// needs it on its stream while that stream is not being captured, and replaced by a larger one
+// (at least twice the size) when a call needs more; a replaced one is never freed, since graphs
+// captured earlier keep its address and may still be replayed.  A captured call that finds no
+// large enough workspace for its stream gets none (*out = nullptr) and takes a path without it.
+// A graph keeps using the workspace of the stream it was captured on, wherever it is replayed.
+enum WsKind { WS_SPLITK = 0, WS_LAYOUT = 1 };
 
-int get_workspace(hipStream_t stream, Workspace **out)
+int stream_workspace(int kind, hipStream_t stream, size_t need, void **out)
 {
     static std::mutex mu;
-    static Workspace ws[64];
+    static std::map<std::tuple<int, uintptr_t, int>, std::pair<void *, size_t>> table;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess)
         return fail(DG_ERR_HIP, "no HIP device available");
     std::lock_guard<std::mutex> lk(mu);
-    Workspace &w = ws[dev];
-    if (!w.partials) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-            *out = nullptr;  // caller falls back to a configuration without split-K
-            return DG_OK;
-        }
-        if (hipMalloc(&w.partials, kWsFloats * sizeof(float)) != hipSuccess)
-            return fail(DG_ERR_HIP, "split-K workspace allocation failed");
-        w.partial_floats = kWsFloats;
+    std::pair<void *, size_t> &e = table[std::make_tuple(dev, (uintptr_t)stream, kind)];
+    if (e.first && e.second >= need) {
+        *out = e.first;
+        return DG_OK;
     }
-    *out = &w;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        *out = nullptr;
+        return DG_OK;
+    }
+    constexpr size_t kUnit = (size_t)4 << 20;
+    size_t bytes = e.second * 2 > need ? e.second * 2 : need;
+    bytes = (bytes + kUnit - 1) / kUnit * kUnit;
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess)
+        return fail(DG_ERR_HIP, "workspace allocation of %zu bytes failed", bytes);
+    e = std::make_pair(p, bytes);  // the previous buffer stays allocated (see above)
+    *out = p;
     return DG_OK;
 }
 
@@ -148,18 +159,23 @@ int forced_splits()
     return (s && *s) ? atoi(s) : 0;
 }
 
-void print_config(const char *what, int m, int n, int k, int g, int cfg, int splits)
+void print_config(const char *what, int m, int n, int k, int g, int cfg, int splits,
+                  int expected_m = -1)
 {
     static std::mutex mu;
-    static std::set<std::tuple<std::string, int, int, int, int>> seen;
+    static std::set<std::tuple<std::string, int, int, int, int, int>> seen;
     const char *env = getenv("DG_PRINT_CONFIGS");
     if (!env || !*env || *env == '0')
         return;
     std::lock_guard<std::mutex> lk(mu);
-    if (!seen.insert(std::make_tuple(std::string(what), m, n, k, g)).second)
+    if (!seen.insert(std::make_tuple(std::string(what), m, n, k, g, expected_m)).second)
         return;
-    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %s (%dx%d), splits=%d\n", what, m,
-            n, k, g, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn, splits);
+    char hint[32] = "";
+    if (expected_m >= 0)
+        snprintf(hint, sizeof(hint), " expected_m=%d", expected_m);
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d%s -> tile %s (%dx%d), splits=%d\n", what,
+            m, n, k, g, hint, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn,
+            splits);
 }
 
 // Estimated cost of a tile choice: waves of workgroups over the CUs times the work of one
@@ -186,40 +202,6 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
             const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
-
-// Transposed-operand workspace of the dense NN/TN/TT calls: one per device, allocated on a
-// call made while the stream is not being captured, then reused.  When a call needs more, a
-// larger one (at least twice the size) replaces it, and the old one is never freed: graphs
-// captured earlier keep its address and may be replayed.  Calls that overlap on one device
-// (different streams) share it and must not run concurrently.
-int get_layout_workspace(hipStream_t stream, size_t need, void **out)
-{
-    static std::mutex mu;
-    static void *bufs[64] = {nullptr};
-    static size_t sizes[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return fail(DG_ERR_HIP, "no HIP device available");
-    std::lock_guard<std::mutex> lk(mu);
-    if (sizes[dev] >= need) {
-        *out = bufs[dev];
-        return DG_OK;
-    }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-        *out = nullptr;  // the caller uses the kernel that reads MN-major operands directly
-        return DG_OK;
-    }
-    size_t bytes = sizes[dev] * 2 > need ? sizes[dev] * 2 : need;
-    bytes = (bytes + ((size_t)32 << 20) - 1) / ((size_t)32 << 20) * ((size_t)32 << 20);
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess)
-        return fail(DG_ERR_HIP, "layout workspace allocation failed");
-    bufs[dev] = p;  // the previous buffer stays allocated (see above)
-    sizes[dev] = bytes;
-    *out = p;
-    return DG_OK;
-}
 
 bool layout_native_forced()
 {
@@ -257,7 +239,7 @@ int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, con
         const size_t a_bytes = a_mn ? ((size_t)m * k + 255) / 256 * 256 : 0;
         const size_t b_bytes = b_mn ? (size_t)n * k : 0;
         void *ws = nullptr;
-        if ((rc = get_layout_workspace(s, a_bytes + b_bytes, &ws)) != DG_OK)
+        if ((rc = stream_workspace(WS_LAYOUT, s, a_bytes + b_bytes, &ws)) != DG_OK)
             return rc;
         if (ws) {
             // A stored [k][m] -> [m][k] and B stored [k][n] -> [n][k], in one launch
@@ -361,14 +343,15 @@ int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const v
         const int kbs = (kb + want - 1) / want;
         args.splits = (kb + kbs - 1) / kbs;
         if (args.splits > 1) {
-            Workspace *w = nullptr;
-            if ((rc = get_workspace(s, &w)) != DG_OK)
+            void *w = nullptr;
+            const size_t need = (size_t)tiles * args.splits * 64 * 64 * sizeof(float);
+            if ((rc = stream_workspace(WS_SPLITK, s, need, &w)) != DG_OK)
                 return rc;
-            if (w && (size_t)tiles * args.splits * 64 * 64 <= w->partial_floats) {
-                args.ws = w->partials;
+            if (w) {
+                args.ws = (float *)w;
             } else {
-                // no workspace (first call made under graph capture) or too little: the
-                // pipelined kernel without split-K is slower here but needs none
+                // no workspace for this stream (a call made under graph capture before any
+                // outside it): the pipelined kernel without split-K is slower here but needs none
                 cfg = dg::CFG_64x32;
                 args.splits = 1;
             }
@@ -469,10 +452,17 @@ int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, 
     int cus = 0;
     if ((rc = device_cus(&cus)) != DG_OK)
         return rc;
-    (void)expected_m;
-    // 256-row tiles cover a group's m_max rows at once (the rows past masked_m skip their
-    // MFMAs and read zeros); of the two widths, the one with less column padding, the wider
-    // on a tie (each N-tile re-reads the group's A from L2, so fewer, wider tiles read less)
+    // The valid rows per group are known only on the device; the caller's expected count (<= 0:
+    // half of m_max) is the pages' hint for the tile choice.  Measured on the MI355X (16 groups,
+    // N = 7168, K = 2048, masked_m uniform in [0, 2e]), 256-row tiles are the fastest at every
+    // expected count from e = 8 to 128, ahead of 128-row tiles by 25-50%: a group's rows past
+    // masked_m skip their MFMAs and read zeros, so the taller tile costs little, and it reads
+    // each B column block once where two 128-row tiles may read it twice.  So the choice depends
+    // on m_max (one 256-row tile per N tile when the groups can exceed 128 rows) and not on the
+    // hint, which is printed with the choice.  Of the two 256-row widths, the one with less
+    // column padding, the wider on a tie (each N tile re-reads the group's A from L2, so fewer,
+    // wider tiles read less).
+    const int e = expected_m > 0 ? (expected_m < m_max ? expected_m : m_max) : (m_max + 1) / 2;
     int cfg = forced_config();
     if (cfg < 0 || cfg == dg::CFG_STREAM64) {
         if (m_max > 128) {
@@ -498,7 +488,7 @@ int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, 
     args.splits = 1;
     args.max_wgs = persistent_wgs(cus);
     args.sf_fmt = sf_fmt;
-    print_config("m_grouped_masked", m_max, n, k, num_groups, cfg, 1);
+    print_config("m_grouped_masked", m_max, n, k, num_groups, cfg, 1, e);
     return launch(dg::MODE_MASKED, cfg, args, (hipStream_t)stream);
 }
 

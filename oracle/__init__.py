@@ -43,6 +43,7 @@ def _load():
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.dgo_e4m3_table.argtypes = [p]
     lib.dgo_num_threads.restype = ctypes.c_int
+    lib.dgo_set_num_threads.argtypes = [ctypes.c_int]
     lib.dgo_block_partials.argtypes = [p, p, p, i64, i64, i64]
     lib.dgo_fp8_gemm_nt.argtypes = [p, p, i64, p, p, p, p, i64, i64, i64]
     lib.dgo_fp8_gemm_nt.restype = ctypes.c_int
@@ -64,6 +65,11 @@ def _c(x, dtype):
 
 def num_threads() -> int:
     return int(_load().dgo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (timing only; results do not depend on it)."""
+    _load().dgo_set_num_threads(int(n))
 
 
 def e4m3_table() -> np.ndarray:
@@ -239,7 +245,12 @@ def bf16_decode(bits) -> np.ndarray:
 
 def swiglu(x_bits) -> np.ndarray:
     """float64 h [M, I] of a bf16 [M, 2I] input (gate first, then up)."""
-    x = bf16_decode(x_bits)
+    return swiglu_values(bf16_decode(x_bits))
+
+
+def swiglu_values(x) -> np.ndarray:
+    """float64 h [M, I] of float64 first-GEMM results x [M, 2I] (gate first, then up)."""
+    x = np.asarray(x, dtype=np.float64)
     i = x.shape[1] // 2
     g, u = x[:, :i], x[:, i:]
     return g * u / (1.0 + np.exp(-g))
@@ -265,7 +276,12 @@ def e4m3_nearest(y) -> np.ndarray:
 
 def swiglu_quant(x_bits, ld: Optional[int] = None):
     """(h float64 [M, I], scales float64 [I/128, ld], codes uint8 [M, I]) by the definition."""
-    h = swiglu(x_bits)
+    return quant_1x128(swiglu(x_bits), ld)
+
+
+def quant_1x128(h, ld: Optional[int] = None):
+    """The 1x128 FP8 cast of float64 h [M, I]: (h, scales [I/128, ld], codes [M, I])."""
+    h = np.asarray(h, dtype=np.float64)
     m, i = h.shape
     if i % 128:
         raise ValueError("oracle: I must be a multiple of 128")
@@ -276,3 +292,33 @@ def swiglu_quant(x_bits, ld: Optional[int] = None):
     sf = np.zeros((i // 128, ld), dtype=np.float64)
     sf[:, :m] = scale.T
     return h, sf, e4m3_nearest(y)
+
+
+# ---------------------------------------------------------------------------------------------
+# The first GEMM of an expert with the activation step fused behind it (the single-GPU part of
+# the MoE block that pt.news.hada.io's "Mega MoE" section describes as linear 1 -> SwiGLU ->
+# linear 2 in one pass; "Interface GEMM e restrições de layout" leaves the FP8 cast of the next
+# GEMM's input to the caller).  Reading taken: the activation applies to the first GEMM's
+# unrounded result (no bf16 rounding in between): for every computed row m of the contiguous
+# layout, D1[m] = the plain definition above (float64), gate = D1[m, :I], up = D1[m, I:],
+# h = gate * up / (1 + exp(-gate)), and the 1x128 cast of h as in quant_1x128.
+
+def m_grouped_contiguous_swiglu(a, sfa, b, sfb, m_indices, ld: Optional[int] = None):
+    """(d1 [M, 2I], h [M, I], scales [I/128, ld], codes [M, I]) for the contiguous layout; rows
+    the method does not compute (index outside [0, G)) are NaN in d1 and h, 0 in the scales and
+    the codes."""
+    d1 = m_grouped_contiguous(a, sfa, b, sfb, m_indices)
+    m, n2 = d1.shape
+    if n2 % 256:
+        raise ValueError("oracle: N = 2I with I a multiple of 128")
+    valid = ~np.isnan(d1).any(axis=1)
+    ld = (m + 3) // 4 * 4 if ld is None else ld
+    h = np.full((m, n2 // 2), np.nan)
+    sf = np.zeros((n2 // 256, ld))
+    q = np.zeros((m, n2 // 2), dtype=np.uint8)
+    if valid.any():
+        hv, sfv, qv = quant_1x128(swiglu_values(d1[valid]))
+        h[valid] = hv
+        sf[:, np.nonzero(valid)[0]] = sfv[:, :int(valid.sum())]
+        q[valid] = qv
+    return d1, h, sf, q

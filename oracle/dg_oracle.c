@@ -71,6 +71,17 @@ void dgo_e4m3_table(double *out)
         out[i] = g_table[i];
 }
 
+/* Threads of the OpenMP loops below (the CPU baseline times the oracle on one thread too). */
+void dgo_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int dgo_num_threads(void)
 {
 #ifdef _OPENMP

@@ -87,6 +87,17 @@ def fp32_scales(p):
     return oracle.ue8m0_decode(p.sfa, ka, kb), oracle.ue8m0_decode(p.sfb, p.sfb.ndim - 1, kb)
 
 
+_REF_CACHE = {}
+
+
+def cached_ref(key, compute):
+    """The oracle's result for a full-size workload, computed once per test session (several
+    tests and variants run the same seeded inputs)."""
+    if key not in _REF_CACHE:
+        _REF_CACHE[key] = compute()
+    return _REF_CACHE[key]
+
+
 def dense_rows_ref(p: W.Dense, rows):
     rows = np.asarray(rows)
     sfa, sfb = fp32_scales(p)

@@ -74,6 +74,9 @@ def dense(lib, a=P, sfa=P, ld=128, b=P, sfb=P, c=None, d=P, m=128, n=256, k=512)
     (dict(b=P + 4), DG_ERR_MISALIGNED),
     (dict(d=P + 2), DG_ERR_MISALIGNED),
     (dict(sfa=P + 2), DG_ERR_MISALIGNED),
+    (dict(sfa=P + 4), DG_ERR_MISALIGNED),
+    (dict(sfa=P + 8), DG_ERR_MISALIGNED),
+    (dict(sfb=P + 2), DG_ERR_MISALIGNED),
     (dict(c=P + 8), DG_ERR_MISALIGNED),
     (dict(c=P, d=P), DG_ERR_INVALID_ARG),
 ])

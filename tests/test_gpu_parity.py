@@ -1,7 +1,7 @@
 """Parity of the HIP path (called through the C ABI binding) with the CPU oracle, on the
 same seeded inputs: small problems compared element by element across several tiles and
-ragged tails, the full-size workloads on sampled rows, edge cases, and the masked call
-replayed from a captured graph with masked_m rewritten on the device."""
+ragged tails, the full-size workloads compared element by element in full, edge cases, and
+the masked call replayed from a captured graph with masked_m rewritten on the device."""
 import os
 import sys
 
@@ -12,7 +12,7 @@ import torch
 import moe_grouped_gemm_fp8_amd as dg
 import oracle
 import workloads as W
-from gpu_util import (DEV, assert_parity, bits, dense_rows_ref, dev, run_contiguous, run_dense,
+from gpu_util import (DEV, assert_parity, bits, cached_ref, dev, run_contiguous, run_dense,
                       run_masked, sentinel_like)
 from tolerance import bf16_bits_to_f64
 
@@ -171,6 +171,24 @@ def test_dense_forced_split_k_with_ragged_tiles(splits, monkeypatch):
     assert_parity(run_dense(p), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"split{splits}")
 
 
+def test_split_k_on_two_streams_at_once():
+    # split-K calls on two streams, launched back to back with no synchronization between
+    # them: each stream's partial tiles go to its own workspace
+    ps = [W.make_dense(64, 1024, 4096, seed=55 + i, with_c=True) for i in range(2)]
+    ins = [[dev(x) for x in (p.a, p.sfa, p.b, p.sfb, p.c)] for p in ps]
+    outs = [sentinel_like((64, 1024)) for _ in ps]
+    streams = [torch.cuda.Stream() for _ in ps]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(10):
+        for s, (a, sfa, b, sfb, c), d in zip(streams, ins, outs):
+            with torch.cuda.stream(s):
+                dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)
+    torch.cuda.synchronize()
+    for p, d in zip(ps, outs):
+        assert_parity(bits(d), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "two streams")
+
+
 def test_dense_skinny_workload_full_and_deterministic():
     p = W.make_config("dense_skinny", seed=0)                  # 64 x 2112 x 7168, split K
     ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
@@ -180,14 +198,12 @@ def test_dense_skinny_workload_full_and_deterministic():
     assert np.array_equal(d1, d2), "split-K reduction is not deterministic"
 
 
-def test_dense_prefill_workload_sampled_rows():
+def test_dense_prefill_workload_full():
     p = W.make_config("dense_prefill", seed=0)                 # 4096 x 7168 x 2048 with C
     got = run_dense(p)
     assert not np.any(got == W.BF16_SENTINEL), "some outputs were never written"
-    rng = np.random.default_rng(100)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(p.m - 8, p.m),
-                                     rng.choice(p.m, 48, replace=False)]))
-    assert_parity(got[rows], dense_rows_ref(p, rows), "dense_prefill")
+    ref = cached_ref("dense_prefill", lambda: oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+    assert_parity(got, ref, "dense_prefill")
 
 
 # ------------------------------------------------------------------------------ contiguous
@@ -279,7 +295,7 @@ def test_contiguous_all_padding_writes_nothing():
 
 
 @pytest.mark.parametrize("served", [None, "0"])
-def test_contiguous_workload_sampled_rows(served, monkeypatch):
+def test_contiguous_workload_full(served, monkeypatch):
     # served=0: every straddling tile runs its second group inside its own workgroup
     if served is not None:
         monkeypatch.setenv("DG_STRADDLE_ROWS", served)
@@ -287,18 +303,10 @@ def test_contiguous_workload_sampled_rows(served, monkeypatch):
     got = run_contiguous(p)
     pad = p.m_indices < 0
     assert np.all(got[pad] == W.BF16_SENTINEL), "padding rows were written"
-    rng = np.random.default_rng(101)
-    rows = []
-    for g in range(p.num_groups):
-        idx = np.nonzero(p.m_indices == g)[0]
-        if idx.size:
-            rows += [idx[0], idx[-1]] + list(rng.choice(idx, min(6, idx.size), replace=False))
-    rows = np.unique(np.array(rows))
-    ref = np.stack([oracle.fp8_gemm_nt(p.a[r:r + 1], W.mn_major(p.sfa[:, r:r + 1].T),
-                                       p.b[p.m_indices[r]], p.sfb[p.m_indices[r]])[0]
-                    for r in rows])
-    assert_parity(got[rows], ref, "moe_contiguous")
     assert not np.any(got[~pad] == W.BF16_SENTINEL), "valid rows were left unwritten"
+    ref = cached_ref("moe_contiguous", lambda: oracle.m_grouped_contiguous(
+        p.a, p.sfa, p.b, p.sfb, p.m_indices))
+    assert_parity(got, ref, "moe_contiguous")
 
 
 # ------------------------------------------------------------------------------ masked
@@ -325,20 +333,15 @@ def test_masked_all_zero_writes_nothing():
     assert np.all(run_masked(p) == W.BF16_SENTINEL)
 
 
-def test_masked_workload_sampled_rows():
+def test_masked_workload_full():
     p = W.make_config("moe_masked", seed=0)                    # 16 x 256 x 7168 x 2048
     got = run_masked(p)
-    rng = np.random.default_rng(102)
     for g in range(p.num_groups):
         valid = int(p.masked_m[g])
         assert np.all(got[g, valid:] == W.BF16_SENTINEL), f"group {g}: tail written"
-        if valid == 0:
-            continue
-        rows = np.unique(np.concatenate([[0, valid - 1], rng.choice(valid, min(4, valid),
-                                                                      replace=False)]))
-        ref = oracle.fp8_gemm_nt(p.a[g, rows], W.mn_major(p.sfa[g][:, rows].T), p.b[g], p.sfb[g])
-        assert_parity(got[g, rows], ref, f"moe_masked group {g}")
-        assert not np.any(got[g, :valid] == W.BF16_SENTINEL)
+        assert not np.any(got[g, :valid] == W.BF16_SENTINEL), f"group {g}: rows unwritten"
+    ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(got, ref, "moe_masked")
 
 
 def test_masked_graph_replays_follow_device_masked_m():
@@ -369,3 +372,41 @@ def test_masked_graph_replays_follow_device_masked_m():
         assert_parity(got, ref, f"graph replay {r}")
         eager = run_masked(p, mm)
         assert np.array_equal(got, eager), f"replay {r} differs from the eager call"
+
+
+@pytest.mark.parametrize("expected_m", [16, 64, 200, 0])
+def test_masked_expected_m_is_reported_with_the_tile(expected_m, monkeypatch, capfd):
+    # the host hint is printed with the tile choice (DG_PRINT_CONFIGS); 256-row tiles were
+    # measured fastest at every expected count, so the choice stays 256x224 for this shape
+    tile = "256x224w8"
+    monkeypatch.setenv("DG_PRINT_CONFIGS", "1")
+    mm = [0, 3, 17, 64, 100, 130, 255, 256]
+    # N = 1792 = 8 x 224 = 7 x 256: no column padding for either width
+    p = W.make_masked(8, 256, 1792, 256, seed=45, masked_m=mm, tail_nan=True)
+    d = sentinel_like((8, 256, 1792))
+    dg.m_grouped_fp8_gemm_nt_masked(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d,
+                                    dev(np.asarray(mm, np.int32)), expected_m=expected_m)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    want = f"expected_m={expected_m if expected_m > 0 else 128} -> tile {tile}"
+    assert want in err, err
+    assert_parity(bits(d), oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m),
+                  f"masked expected_m={expected_m}")
+
+
+@pytest.mark.parametrize("cfg,m,n", [("256x128w8", 16384, 131072), ("256x224w8", 16384, 262528)])
+def test_more_than_65536_tiles_of_one_workgroup_each(cfg, m, n, monkeypatch):
+    # 65536 and 75008 tiles, one workgroup each: the per-XCD tile ranges pass 2^32 in their
+    # products of tile count and grid size; every tile must be written exactly by its owner
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = W.make_dense(m, n, 128, seed=57)
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), d)
+    torch.cuda.synchronize()
+    sentinel = np.array([W.BF16_SENTINEL], np.uint16).view(np.int16)[0]
+    left = int((d.view(torch.int16) == int(sentinel)).sum().item())
+    assert left == 0, f"{left} outputs never written"
+    rows = np.arange(0, m, 256)
+    got = bits(d[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.fp8_gemm_nt(p.a[rows], W.mn_major(p.sfa[:, rows].T), p.b, p.sfb)
+    assert_parity(got, ref, f"{cfg} {m}x{n}")

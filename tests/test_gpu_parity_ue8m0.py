@@ -2,7 +2,7 @@
 applied by the block-scaled MFMA) with the CPU oracle on the same seeded inputs: every
 pipelined tile configuration on ragged shapes, K-block counts that leave the last packed
 word partly used, persistent workgroups looping over tiles, NaN scales, the grouped forms
-with their padding and clamps, and the full-size workloads on sampled rows."""
+with their padding and clamps, and the full-size workloads compared in full."""
 import sys
 
 import numpy as np
@@ -12,7 +12,7 @@ import moe_grouped_gemm_fp8_amd as dg
 
 import oracle
 import workloads as W
-from gpu_util import (assert_parity, dense_rows_ref, fp32_scales, run_contiguous, run_dense,
+from gpu_util import (assert_parity, fp32_scales, run_contiguous, run_dense,
                       run_masked)
 from tolerance import bf16_bits_to_f64
 
@@ -120,14 +120,11 @@ def test_dense_nan_scale_poisons_its_row_or_block():
     assert_parity(got_bits[keep][:, :128], ref[keep][:, :128], "finite part")
 
 
-def test_dense_prefill_workload_sampled_rows():
+def test_dense_prefill_workload_full():
     p = W.make_config("dense_prefill", seed=0, ue8m0=True)      # 4096 x 7168 x 2048 with C
     got = run_dense(p)
     assert not np.any(got == W.BF16_SENTINEL), "some outputs were never written"
-    rng = np.random.default_rng(110)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(p.m - 8, p.m),
-                                     rng.choice(p.m, 48, replace=False)]))
-    assert_parity(got[rows], dense_rows_ref(p, rows), "dense_prefill ue8m0")
+    assert_parity(got, oracle.fp8_gemm_nt_ue8m0(p.a, p.sfa, p.b, p.sfb, p.c), "dense_prefill ue8m0")
 
 
 # ------------------------------------------------------------------------------ contiguous
@@ -155,24 +152,14 @@ def test_contiguous_256_row_tiles_across_group_boundaries(counts, monkeypatch):
     assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
-def test_contiguous_workload_sampled_rows():
+def test_contiguous_workload_full():
     p = W.make_config("moe_contiguous", seed=0, ue8m0=True)    # 8 experts, 32768 x 4096 x 7168
     got = run_contiguous(p)
     pad = p.m_indices < 0
     assert np.all(got[pad] == W.BF16_SENTINEL), "padding rows were written"
-    sfa, sfb = fp32_scales(p)
-    rng = np.random.default_rng(111)
-    rows = []
-    for g in range(p.num_groups):
-        idx = np.nonzero(p.m_indices == g)[0]
-        if idx.size:
-            rows += [idx[0], idx[-1]] + list(rng.choice(idx, min(6, idx.size), replace=False))
-    rows = np.unique(np.array(rows))
-    ref = np.stack([oracle.fp8_gemm_nt(p.a[r:r + 1], W.mn_major(sfa[:, r:r + 1].T),
-                                       p.b[p.m_indices[r]], sfb[p.m_indices[r]])[0]
-                    for r in rows])
-    assert_parity(got[rows], ref, "moe_contiguous ue8m0")
     assert not np.any(got[~pad] == W.BF16_SENTINEL), "valid rows were left unwritten"
+    ref = oracle.m_grouped_contiguous_ue8m0(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(got, ref, "moe_contiguous ue8m0")
 
 
 # ------------------------------------------------------------------------------ masked
@@ -188,21 +175,15 @@ def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     assert_parity(run_masked(p), ref, f"masked ue8m0 {cfg}")
 
 
-def test_masked_workload_sampled_rows():
+def test_masked_workload_full():
     p = W.make_config("moe_masked", seed=0, ue8m0=True)        # 16 x 256 x 7168 x 2048
     got = run_masked(p)
-    sfa, sfb = fp32_scales(p)
-    rng = np.random.default_rng(112)
     for g in range(p.num_groups):
         valid = int(p.masked_m[g])
         assert np.all(got[g, valid:] == W.BF16_SENTINEL), f"group {g}: tail written"
-        if valid == 0:
-            continue
-        rows = np.unique(np.concatenate([[0, valid - 1], rng.choice(valid, min(4, valid),
-                                                                      replace=False)]))
-        ref = oracle.fp8_gemm_nt(p.a[g, rows], W.mn_major(sfa[g][:, rows].T), p.b[g], sfb[g])
-        assert_parity(got[g, rows], ref, f"moe_masked ue8m0 group {g}")
-        assert not np.any(got[g, :valid] == W.BF16_SENTINEL)
+        assert not np.any(got[g, :valid] == W.BF16_SENTINEL), f"group {g}: rows unwritten"
+    ref = oracle.m_grouped_masked_ue8m0(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(got, ref, "moe_masked ue8m0")
 
 
 def test_masked_graph_replays_follow_device_masked_m():

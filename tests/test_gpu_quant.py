@@ -89,14 +89,11 @@ def test_scale_columns_past_m_are_not_written():
     check(x, q, sf, "ld=16")
 
 
-def test_workload_sampled_rows():
+def test_workload_full():
     x = W.make_config("moe_swiglu_quant", seed=0)                 # 32768 x 2048
     q, sf = run(x)
-    rows = np.unique(np.concatenate([[0, 1, x.shape[0] - 1],
-                                     np.random.default_rng(140).choice(x.shape[0], 61, replace=False)]))
-    sub_sf = np.zeros((sf.shape[0], (len(rows) + 3) // 4 * 4), np.float32)
-    sub_sf[:, :len(rows)] = sf[:, rows]
-    check(x[rows], q[rows], sub_sf, "moe_swiglu_quant")
+    near = check(x, q, sf, "moe_swiglu_quant")
+    _say(f"{near} of {q.size} codes within the error bound of a boundary")
 
 
 def test_cast_feeds_the_nt_gemm():
