@@ -67,6 +67,20 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
                    void *stream);
 
 /*
+ * dg_fp8_gemm_nt for callers that cannot allocate device memory: code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, result and errors as
+ * dg_fp8_gemm_nt, except that the split-K partial tiles of skinny shapes go to a static device
+ * array of the library (16 MiB, one per device, held until the process ends) instead of a
+ * workspace, so the call never allocates.  A shape whose partials would need more than that
+ * array returns DG_ERR_UNSUPPORTED (shapes that do not split K need none of it).  Every call of
+ * this entry point on one device shares the array: calls that overlap in time on one device
+ * (on any streams) race and must be ordered by the caller.
+ */
+int dg_fp8_gemm_nt_noalloc(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                           const float *sfb, const float *c, void *d, int m, int n, int k,
+                           void *stream);
+
+/*
  * M-grouped GEMM, contiguous layout (pt.news.hada.io, "GEMM denso e grouped": experts share
  * N and K; their token rows are concatenated along M; each expert segment is aligned to the
  * M block, whose size dg_get_mk_alignment_for_contiguous_layout() returns).

@@ -20,7 +20,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "DGError", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "DGError", "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "swiglu_fp8_quant",
     "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "m_grouped_fp8_gemm_nt_masked_ue8m0", "k_grouped_fp8_gemm_tn_contiguous",
@@ -62,7 +62,7 @@ def _load():
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_masked.restype = i32
-    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt", "dg_fp8_gemm_nt_noalloc"):
         getattr(lib, name).argtypes = lib.dg_fp8_gemm_nt.argtypes
         getattr(lib, name).restype = i32
     for name in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous",
@@ -149,6 +149,12 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None
     """D = C + A @ B.T.  a [M,K] e4m3, sfa [K/128, ld>=M] f32, b [N,K] e4m3,
     sfb [ceil(N/128), K/128] f32, d [M,N] bf16 (written), c [M,N] f32 or None."""
     return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False)
+
+
+def fp8_gemm_nt_noalloc(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):
+    """fp8_gemm_nt through the entry point that allocates nothing (split-K partials in the
+    library's static per-device scratch; overlapping calls on one device race)."""
+    return _fp8_gemm_nt(a, sfa, b, sfb, d, c, stream, False, "nt_noalloc")
 
 
 def fp8_gemm_nn(a, sfa, b, sfb, d, c: Optional[torch.Tensor] = None, stream=None):

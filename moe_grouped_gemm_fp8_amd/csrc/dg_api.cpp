@@ -201,7 +201,8 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 
 
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
-            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream);
+            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream,
+            bool noalloc = false);
 
 bool layout_native_forced()
 {
@@ -273,8 +274,11 @@ int gemm_layout(int layout, const void *a, const float *sfa, int64_t ld_sfa, con
 }
 
 // The three forms, for either scale format (UE8M0: the scale pointers hold int32 words).
+// noalloc: the split-K partials go to the static scratch array (dg_stream.hip) instead of a
+// per-stream workspace, and nothing is allocated.
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
-            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
+            const float *sfb, const float *c, void *d, int m, int n, int k, void *stream,
+            bool noalloc)
 {
     int rc = check_common(a, sfa, ld_sfa, b, sfb, d, m, n, k);
     if (rc != DG_OK)
@@ -345,8 +349,22 @@ int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const v
         if (args.splits > 1) {
             void *w = nullptr;
             const size_t need = (size_t)tiles * args.splits * 64 * 64 * sizeof(float);
-            if ((rc = stream_workspace(WS_SPLITK, s, need, &w)) != DG_OK)
+            if (noalloc) {
+                float *sp = nullptr;
+                size_t floats = 0;
+                const hipError_t e = dg::static_scratch(&sp, &floats);
+                if (e != hipSuccess)
+                    return fail(DG_ERR_HIP, "static scratch lookup failed: %s",
+                                hipGetErrorString(e));
+                if (need > floats * sizeof(float))
+                    return fail(DG_ERR_UNSUPPORTED,
+                                "split-K partials need %zu bytes, more than the %zu-byte static "
+                                "scratch of the no-allocation call",
+                                need, floats * sizeof(float));
+                w = sp;
+            } else if ((rc = stream_workspace(WS_SPLITK, s, need, &w)) != DG_OK) {
                 return rc;
+            }
             if (w) {
                 args.ws = (float *)w;
             } else {
@@ -500,6 +518,13 @@ int dg_fp8_gemm_nt(const void *a, const float *sfa, int64_t ld_sfa, const void *
                    const float *sfb, const float *c, void *d, int m, int n, int k, void *stream)
 {
     return gemm_nt(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream);
+}
+
+int dg_fp8_gemm_nt_noalloc(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                           const float *sfb, const float *c, void *d, int m, int n, int k,
+                           void *stream)
+{
+    return gemm_nt(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, c, d, m, n, k, stream, true);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t ld_sfa,

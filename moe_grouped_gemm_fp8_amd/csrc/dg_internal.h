@@ -107,5 +107,8 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &args, hipStream_t stre
 int64_t stream_grid_size(const GemmArgs &args);
 int stream_max_kblocks();
 hipError_t launch_stream(const GemmArgs &args, hipStream_t stream);
+// Device address (on the current device) and size in floats of the static split-K scratch
+// that the no-allocation entry point uses instead of a workspace.
+hipError_t static_scratch(float **out, size_t *floats);
 
 }  // namespace dg

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -264,6 +266,40 @@ int64_t stream_grid_size(const GemmArgs &a)
 }
 
 int stream_max_kblocks() { return ST_KSB; }
+
+// Split-K scratch of the entry point that allocates nothing (dg_fp8_gemm_nt_noalloc): the
+// FP32 partial tiles go to this file-scope array instead of a library-allocated workspace.
+// Every device that runs the library holds its own copy of it, at its own address, until the
+// process ends.  Host code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is passed to kernels.
+// Nothing in it has to start at zero: every split writes its whole partial tile before the
+// reduce kernel reads it.  Calls that overlap on one device share the array and race.
+constexpr size_t kScratchFloats = size_t(4) << 20;  // 16 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+hipError_t static_scratch(float **out, size_t *floats)
+{
+    static std::mutex mu;
+    static void *addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *out = (float *)addr[dev];
+    *floats = kScratchFloats;
+    return hipSuccess;
+}
 
 hipError_t launch_stream(const GemmArgs &a, hipStream_t stream)
 {
