@@ -210,6 +210,66 @@ def make_contiguous_case(torch, dg, W, ue8m0=False):
     return c
 
 
+def make_block_case(torch, dg, W, variant):
+    """The experts of an MoE block on the contiguous workload's routing: linear 1 (N = 2I =
+    4096 gate and up columns, K = 7168), SwiGLU and the 1x128 FP8 cast, linear 2 (N = 7168,
+    K = I = 2048).  variant: "fused" (linear 1 with the activation step in its epilogue, then
+    linear 2), "unfused" (linear 1 to bf16, the activation step kernel, linear 2), or
+    "linear1_fused" (the fused first GEMM alone)."""
+    blk = W.make_config("moe_block", seed=0)
+    p = blk.up
+    name = {"fused": "moe_block", "unfused": "moe_block_unfused",
+            "linear1_fused": "moe_contiguous_swiglu"}[variant]
+    c = Case(name)
+    i, n2, k = p.n // 2, blk.n2, p.k
+    ld = W.sf_aligned(p.m_total)
+    t = dict(a=_dev(torch, p.a), sfa=_dev(torch, p.sfa), b=_dev(torch, p.b), sfb=_dev(torch, p.sfb),
+             idx=_dev(torch, p.m_indices), b2=_dev(torch, blk.b2), sfb2=_dev(torch, blk.sfb2),
+             q=torch.empty(p.m_total, i, dtype=torch.uint8, device="cuda"),
+             sfq=torch.zeros(i // 128, ld, dtype=torch.float32, device="cuda"),
+             d1=(torch.empty(p.m_total, p.n, dtype=torch.bfloat16, device="cuda")
+                 if variant == "unfused" else None),
+             d2=(torch.empty(p.m_total, n2, dtype=torch.bfloat16, device="cuda")
+                 if variant != "linear1_fused" else None))
+    valid = int(p.counts.sum())
+    used = int((p.counts > 0).sum())
+    kb, nb = k // 128, p.n // 128
+    # algorithmic bytes: linear 1's A and B, the codes and scales (written by the activation,
+    # read by linear 2), linear 2's B and D; the unfused chain also writes and reads the bf16
+    # linear-1 result
+    l1 = valid * k + used * p.n * k + 4 * valid * kb + 4 * used * nb * kb + 4 * p.m_total
+    act = valid * i + 4 * valid * (i // 128)
+    l2 = used * n2 * i + 4 * used * ((n2 + 127) // 128) * (i // 128) + 2 * valid * n2
+    if variant == "linear1_fused":
+        nbytes, flops = l1 + act, 2.0 * valid * p.n * k
+    else:
+        nbytes = l1 + 2 * act + l2 + (2 * 2 * valid * p.n if variant == "unfused" else 0)
+        flops = 2.0 * valid * (p.n * k + n2 * i)
+    c.sets = _copies(torch, t, nbytes)
+    per_graph = _steps_per_graph(len(c.sets))
+
+    def call(s):
+        if variant == "unfused":
+            dg.m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], s["d1"],
+                                                s["idx"])
+            dg.swiglu_fp8_quant(s["d1"], s["q"], s["sfq"])
+        else:
+            dg.m_grouped_fp8_gemm_nt_contiguous_swiglu(s["a"], s["sfa"], s["b"], s["sfb"],
+                                                       s["q"], s["sfq"], s["idx"])
+        if variant != "linear1_fused":
+            dg.m_grouped_fp8_gemm_nt_contiguous(s["q"], s["sfq"], s["b2"], s["sfb2"], s["d2"],
+                                                s["idx"])
+
+    _graph_launcher(c, *_capture(torch, c.sets, call, per_graph), per_graph)
+    c.config = dict(workload=name, groups=p.num_groups, valid_rows=valid, padded_rows=p.m_total,
+                    hidden=k, intermediate=i, out=n2 if variant != "linear1_fused" else None,
+                    launched_as=f"captured graph replay, {c.cycle} steps per graph",
+                    rotating_copies=len(c.sets))
+    c.flops = lambda i_: flops
+    c.bytes = lambda i_: float(nbytes)
+    return c
+
+
 def make_masked_case(torch, dg, W, ue8m0=False):
     p = W.make_config("moe_masked", seed=0, ue8m0=ue8m0)
     c = Case("moe_masked" + ("_ue8m0" if ue8m0 else ""))
@@ -504,7 +564,8 @@ def main():
                              "moe_masked", "dense_prefill_ue8m0", "dense_skinny_ue8m0",
                              "moe_contiguous_ue8m0", "moe_masked_ue8m0", "moe_wgrad",
                              "dense_prefill_nn", "dense_prefill_tn", "dense_prefill_tt",
-                             "moe_swiglu_quant"])
+                             "moe_swiglu_quant", "moe_contiguous_swiglu", "moe_block",
+                             "moe_block_unfused"])
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -543,6 +604,9 @@ def main():
         "dense_prefill_tn": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tn"),
         "dense_prefill_tt": lambda: make_dense_case(torch, dg, W, "dense_prefill", layout="tt"),
         "moe_swiglu_quant": lambda: make_quant_case(torch, dg, W),
+        "moe_contiguous_swiglu": lambda: make_block_case(torch, dg, W, "linear1_fused"),
+        "moe_block": lambda: make_block_case(torch, dg, W, "fused"),
+        "moe_block_unfused": lambda: make_block_case(torch, dg, W, "unfused"),
     }
     order = [args.workload] + ([] if args.only else [w for w in makers if w != args.workload])
     results = {}

@@ -101,6 +101,28 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
                                         int num_groups, void *stream);
 
 /*
+ * The contiguous M-grouped GEMM with the activation step between an expert's two GEMMs fused
+ * into its epilogue (pt.news.hada.io, "Mega MoE": linear 1 -> SwiGLU -> linear 2 of an MoE
+ * block in one pass; "Interface GEMM e restrições de layout": the FP8 cast of the next GEMM's
+ * input is otherwise left to the caller).  For each computed row r (as in
+ * dg_m_grouped_fp8_gemm_nt_contiguous) the FP32 result D1[r, :] = A[r] @ B[g].T (scaled as
+ * there, not rounded) is split into gate = D1[r, :n/2] and up = D1[r, n/2:], and
+ *     h = gate * up / (1 + exp(-gate));  per 1x128 segment s of h:
+ *     scale = max(amax, 1e-4) / 448,  q = e4m3(h / scale) (nearest even, within +-448)
+ *   a, sfa, b, sfb, m_indices, m_total, k, num_groups   as in the contiguous call; n = 2I, the
+ *             gate rows of each B[g] first, then the up rows; n % 256 == 0
+ *   q         e4m3 [m_total, n/2], 16-byte aligned: the codes of h
+ *   sfq       FP32 [n/256][ld_sfq], 16-byte aligned, ld_sfq >= m_total, ld_sfq % 4 == 0: the
+ *             scales, MN-major (sfq[s * ld_sfq + r]), the layout of the next GEMM's sfa
+ * Padding rows are written in neither q nor sfq.  FP32 scales only.  Errors as above.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const void *a, const float *sfa,
+                                               int64_t ld_sfa, const void *b, const float *sfb,
+                                               void *q, float *sfq, int64_t ld_sfq,
+                                               const int32_t *m_indices, int m_total, int n,
+                                               int k, int num_groups, void *stream);
+
+/*
  * M-grouped GEMM, masked layout (pt.news.hada.io, "GEMM denso e grouped": for decoding under
  * graph capture, when the host does not know the per-expert token counts, a mask tensor
  * tells the kernel which region is valid and only that region is computed).

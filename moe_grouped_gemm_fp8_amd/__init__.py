@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "DGError", "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "m_grouped_fp8_gemm_nt_contiguous_swiglu",
     "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "swiglu_fp8_quant",
     "fp8_gemm_nt_ue8m0", "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "m_grouped_fp8_gemm_nt_masked_ue8m0", "k_grouped_fp8_gemm_tn_contiguous",
@@ -62,6 +63,9 @@ def _load():
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, vp]
     lib.dg_m_grouped_fp8_gemm_nt_masked.restype = i32
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu.argtypes = [vp, vp, i64, vp, vp, vp, vp, i64,
+                                                               vp, i32, i32, i32, i32, vp]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu.restype = i32
     for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt", "dg_fp8_gemm_nt_noalloc"):
         getattr(lib, name).argtypes = lib.dg_fp8_gemm_nt.argtypes
         getattr(lib, name).restype = i32
@@ -211,6 +215,33 @@ def m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, d, m_indices, stream=
     """m_grouped_fp8_gemm_nt_contiguous with packed UE8M0 scales: sfa int32
     [ceil(K/512), ld>=M_total], sfb int32 [G, ceil(N/128), ceil(K/512)]."""
     return _contiguous(a, sfa, b, sfb, d, m_indices, stream, True)
+
+
+def m_grouped_fp8_gemm_nt_contiguous_swiglu(a, sfa, b, sfb, q, sfq, m_indices, stream=None):
+    """The contiguous GEMM with SwiGLU and the 1x128 FP8 cast fused into its epilogue.
+    a [M_total, K], sfa [K/128, ld>=M_total], b [G, 2I, K] (gate rows first),
+    sfb [G, 2I/128, K/128], m_indices int32 [M_total]; writes q [M_total, I] (uint8 or
+    float8_e4m3fn) and sfq float32 [I/128, ld>=M_total] (MN-major) for the valid rows."""
+    pa = _dev(a, "a", _FP8_DTYPES, 2)
+    m_total, k = a.shape
+    pb = _dev(b, "b", _FP8_DTYPES, 3)
+    g, n, kb_ = b.shape
+    _need(kb_ == k, "a and b disagree on K")
+    _need(k % 128 == 0 and n % 256 == 0, "K must be a multiple of 128 and 2I of 256")
+    psfa = _dev(sfa, "sfa", torch.float32, 2)
+    _need(sfa.shape[0] == k // 128, "sfa must be [K/128, ld]")
+    psfb = _dev(sfb, "sfb", torch.float32, 3)
+    _need(tuple(sfb.shape) == (g, n // 128, k // 128), "sfb must be [G, 2I/128, K/128]")
+    pq = _dev(q, "q", _FP8_DTYPES, 2)
+    _need(tuple(q.shape) == (m_total, n // 2), "q must be [M_total, I]")
+    psq = _dev(sfq, "sfq", torch.float32, 2)
+    _need(sfq.shape[0] == n // 256, "sfq must be [I/128, ld]")
+    pi = _dev(m_indices, "m_indices", torch.int32, 1)
+    _need(m_indices.shape[0] == m_total, "m_indices must be [M_total]")
+    _check(_load().dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(
+        pa, psfa, sfa.shape[1], pb, psfb, pq, psq, sfq.shape[1], pi, m_total, n, k, g,
+        _stream(stream)))
+    return q, sfq
 
 
 def _masked(a, sfa, b, sfb, d, masked_m, expected_m, stream, ue8m0):

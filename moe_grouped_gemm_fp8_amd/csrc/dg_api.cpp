@@ -452,6 +452,62 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
     return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
 }
 
+// The contiguous form with the activation step fused into the epilogue: B is [G, 2I, K] with
+// the gate rows first; the tile writes the 1x128 FP8 cast of SwiGLU(gate, up) instead of D.
+int grouped_contiguous_swiglu(const void *a, const float *sfa, int64_t ld_sfa, const void *b,
+                              const float *sfb, void *q, float *sfq, int64_t ld_sfq,
+                              const int32_t *m_indices, int m_total, int n, int k,
+                              int num_groups, void *stream)
+{
+    int rc = check_common(a, sfa, ld_sfa, b, sfb, q, m_total, n, k);
+    if (rc != DG_OK)
+        return rc;
+    if (!m_indices)
+        return fail(DG_ERR_INVALID_ARG, "null m_indices");
+    if (num_groups <= 0)
+        return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be positive", num_groups);
+    if (m_total % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "m_total=%d is not a multiple of 128", m_total);
+    if (n % 256 != 0)
+        return fail(DG_ERR_UNSUPPORTED, "n=%d: the gate and up halves must be multiples of 128",
+                    n);
+    if (!aligned(m_indices, 4))
+        return fail(DG_ERR_MISALIGNED, "m_indices must be 4-byte aligned");
+    if (m_total > 0 && !sfq)
+        return fail(DG_ERR_INVALID_ARG, "null sfq");
+    if (ld_sfq < m_total)
+        return fail(DG_ERR_INVALID_ARG, "ld_sfq=%lld is smaller than m_total=%d",
+                    (long long)ld_sfq, m_total);
+    if (ld_sfq % 4 != 0 || !aligned(sfq, 16))
+        return fail(DG_ERR_MISALIGNED, "sfq must be 16-byte aligned with ld_sfq %% 4 == 0");
+    if (m_total == 0)
+        return ok();
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != DG_OK)
+        return rc;
+    dg::GemmArgs args{};
+    args.a = (const uint8_t *)a;
+    args.sfa = sfa;
+    args.ld_sfa = ld_sfa;
+    args.b = (const uint8_t *)b;
+    args.sfb = sfb;
+    args.grp = m_indices;
+    args.m = m_total;
+    args.n = n;
+    args.k = k;
+    args.num_groups = num_groups;
+    args.splits = 1;
+    args.max_wgs = persistent_wgs(cus);
+    args.sf_fmt = dg::SF_FP32;
+    args.q = (uint8_t *)q;
+    args.sfq = sfq;
+    args.ld_sfq = ld_sfq;
+    // one tile per 128-column segment of h: 128 rows x (128 gate + 128 up columns)
+    const int cfg = dg::CFG_128x256w8;
+    print_config("m_grouped_contiguous_swiglu", m_total, n, k, num_groups, cfg, 1);
+    return launch(dg::MODE_CONTIG_SWIGLU, cfg, args, (hipStream_t)stream);
+}
+
 int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
                    const float *sfb, void *d, const int32_t *masked_m, int num_groups, int m_max,
                    int n, int k, int expected_m, void *stream)
@@ -534,6 +590,16 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const void *a, const float *sfa, int64_t
 {
     return grouped_contiguous(dg::SF_FP32, a, sfa, ld_sfa, b, sfb, d, m_indices, m_total, n, k,
                               num_groups, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const void *a, const float *sfa,
+                                               int64_t ld_sfa, const void *b, const float *sfb,
+                                               void *q, float *sfq, int64_t ld_sfq,
+                                               const int32_t *m_indices, int m_total, int n,
+                                               int k, int num_groups, void *stream)
+{
+    return grouped_contiguous_swiglu(a, sfa, ld_sfa, b, sfb, q, sfq, ld_sfq, m_indices, m_total,
+                                     n, k, num_groups, stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked(const void *a, const float *sfa, int64_t ld_sfa,

@@ -35,6 +35,27 @@ __device__ __forceinline__ void lds_write8(uint32_t addr, uint32_t lo, uint32_t 
     asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(make_uint2(lo, hi)) : "memory");
 }
 
+// gate * up / (1 + exp(-gate)) (SwiGLU) with the hardware reciprocal (v_rcp_f32, 1 ulp) in
+// place of an IEEE division, whose expansion makes the activation step bound by the vector unit
+__device__ __forceinline__ float silu_times(float g, float u)
+{
+    return g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
+
+// two FP32 values (already within +-448) to e4m3 (round to nearest even), packed into bytes
+// 2 SEL .. 2 SEL + 1 of `old` (gfx950's v_cvt_pk_fp8_f32)
+template <bool SEL>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
+{
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, SEL);
+}
+
+// 4-byte LDS write at a byte address; completion is counted by lgkmcnt
+__device__ __forceinline__ void lds_write4(uint32_t addr, float v)
+{
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void store_bf16x4(uint16_t *dst, v4f v)
 {
     uint32_t lo = pack_bf16x2(v.x, v.y);

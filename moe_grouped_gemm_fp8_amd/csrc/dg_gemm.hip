@@ -104,6 +104,12 @@ __device__ __forceinline__ void store8_async(uint16_t *dst, uint32_t lo, uint32_
                  : "memory");
 }
 
+// 4-byte global store issued as inline asm, for the same reason as store8_async
+__device__ __forceinline__ void store4_async(void *dst, uint32_t v)
+{
+    asm volatile("global_store_dword %0, %1, off" ::"v"(dst), "v"(v) : "memory");
+}
+
 template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int SF>
 __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int tiles_n)
 {
@@ -119,6 +125,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // accumulators.
     constexpr bool UE8 = SF != SF_FP32;
     constexpr bool DIRECT = SF == SF_UE8M0;
+    // the activation step fused into the epilogue (contiguous form): see the SwiGLU notes below
+    constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU;
+    constexpr bool CONTIG = MODE == MODE_CONTIG || SWIGLU;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int SM = TM / 16, SN = TN / 16;
@@ -139,12 +148,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
-    constexpr bool ONE_BAR = (DEPTH + 1) * (A_SLOT + B_SLOT + 1024 + 256) <= 160 * 1024;
+    // (the fused activation step adds an area for the row maxima of its segments: BM x WN floats)
+    constexpr int AMX_BYTES = SWIGLU ? BM * WN * 4 : 0;
+    constexpr bool ONE_BAR =
+        (DEPTH + 1) * (A_SLOT + B_SLOT + 1024 + 256) + AMX_BYTES <= 160 * 1024;
     constexpr int NA = ONE_BAR ? DEPTH + 1 : DEPTH;  // A slots (and scale areas)
     constexpr int B_BASE = NA * A_SLOT;
     constexpr int SA_BASE = B_BASE + (DEPTH + 1) * B_SLOT;
     constexpr int SB_BASE = SA_BASE + NA * 1024;
-    constexpr int LDS_BYTES = SB_BASE + NA * 256;
+    constexpr int AMX_BASE = SB_BASE + NA * 256;
+    constexpr int LDS_BYTES = AMX_BASE + AMX_BYTES;
     static_assert(A_SLOT % 4096 == 0 && B_SLOT % 4096 == 0, "slots start on 4 KB boundaries");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
@@ -156,6 +169,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
+    // SwiGLU: one tile covers the gate and up columns of one 128-wide segment of h (BN = 256),
+    // its waves 4 across (WN = 4, TN = 64: two gate/up sub-tile pairs per wave), FP32 scales
+    static_assert(!SWIGLU || (PERSIST && BN == 256 && WN == 4 && SN == 4 && SF == SF_FP32),
+                  "fused activation step: persistent 256-column tiles, four waves across");
     // contiguous tiles that may straddle two groups (their last rows may also lie past M)
     constexpr bool TWO_GROUPS = MODE == MODE_CONTIG && BM > 128;
     static_assert(!TWO_GROUPS || (BM == 256 && !PERSIST), "straddling tiles: 256 rows, one per workgroup");
@@ -299,7 +316,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     auto load_meta = [&](const Tile &u) {
         if constexpr (MODE == MODE_MASKED) {
             raw_cnt = p.grp[u.g];
-        } else if constexpr (MODE == MODE_CONTIG) {
+        } else if constexpr (CONTIG) {
             // (rows past M: only a tile taller than the 128-row alignment reaches them)
 #pragma unroll
             for (int r = 0; r < BM / 64; ++r) {
@@ -319,7 +336,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             const int v = raw_cnt < 0 ? 0 : (raw_cnt > M ? M : raw_cnt);
             u.row_limit = __builtin_amdgcn_readfirstlane(v);
             u.empty = u.m0 >= u.row_limit;
-        } else if constexpr (MODE == MODE_CONTIG) {
+        } else if constexpr (CONTIG) {
             int best = -1;
 #pragma unroll
             for (int r = 0; r < BM / 64; ++r) {
@@ -357,10 +374,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const float *SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * KS * ld : 0);
         const uint8_t *B = p.b + (int64_t)u.g * N * K;
         const float *SFB = p.sfb + (int64_t)u.g * NB * KS;
-        const int nbf = u.n0 / KBLK;
+        // SwiGLU: the tile's B rows start at its segment's first gate row, n0 / 2 (the up rows
+        // follow I = N / 2 rows further on, inside the same range)
+        const int bn0 = SWIGLU ? u.n0 / 2 : u.n0;
+        const int nbf = bn0 / KBLK;
         CopySrc s;
         s.a = make_rsrc(A + (int64_t)u.m0 * K, u.empty ? 0 : (int64_t)(u.row_limit - u.m0) * K);
-        s.b = make_rsrc(B + (int64_t)u.n0 * K, u.empty ? 0 : (int64_t)(N - u.n0) * K);
+        s.b = make_rsrc(B + (int64_t)bn0 * K, u.empty ? 0 : (int64_t)(N - bn0) * K);
         s.sa = make_rsrc(SFA + u.m0, u.empty ? 0 : ((int64_t)KS * ld - u.m0) * 4);
         s.sb = make_rsrc(SFB + (int64_t)nbf * KS, u.empty ? 0 : (int64_t)(NB - nbf) * KS * 4);
         return s;
@@ -437,10 +457,21 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const uint32_t lane_even =
             (uint32_t)(l >> 3) * (uint32_t)K + (uint32_t)((((l & 7) ^ ((l >> 4) << 1))) << 4);
 #pragma unroll
-        for (int c = 0; c < MAXI; ++c)
-            voff[c] = (lane_even ^ (uint32_t)((cq[c] & 1) << 4)) + (uint32_t)(8 * cq[c]) * (uint32_t)K;
+        for (int c = 0; c < MAXI; ++c) {
+            // SwiGLU: LDS rows of B alternate 16 gate rows and the 16 up rows of the same
+            // columns, so sub-tile pair (2p, 2p + 1) of a wave holds gate and up of 16 columns
+            uint32_t row = (uint32_t)(8 * cq[c]);
+            if (SWIGLU && c >= CA)
+                row = (uint32_t)(16 * (cq[c] >> 2) + 8 * (cq[c] & 1)) +
+                      (((cq[c] >> 1) & 1) ? (uint32_t)(N >> 1) : 0u);
+            voff[c] = (lane_even ^ (uint32_t)((cq[c] & 1) << 4)) + row * (uint32_t)K;
+        }
         lane_sfa = (uint32_t)l * 16u;
-        lane_sfb = (uint32_t)l * (uint32_t)KS * 4u;
+        // B scales: lane l copies block nbf + l; SwiGLU: lane 0 the gate block, lane 1 the up
+        // block I / 128 further on, the rest nothing (outside the range: zeros)
+        lane_sfb = SWIGLU ? (l == 0 ? 0u : (l == 1 ? (uint32_t)(N >> 8) * (uint32_t)KS * 4u
+                                                    : 0x80000000u))
+                          : (uint32_t)l * (uint32_t)KS * 4u;
         const int h = ((r >> 3) & 1) | (r & 2) | (((r >> 2) & 1) << 2);  // h(r)
         const uint32_t f_lo = (uint32_t)(r * KBLK + (((2 * gq) ^ h) << 4));
         const uint32_t f_hi = (uint32_t)(r * KBLK + (((2 * gq + 1) ^ h) << 4));
@@ -463,6 +494,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     };
     auto scale_sel = [&](const Tile &u) {
         ScaleSel s;
+        if constexpr (SWIGLU) {
+            // gate sub-tiles (even jj) take the gate block's scale, up sub-tiles the up block's
+            s.lo = 0;
+            s.hi = 4;
+            s.hi_mask = 0;
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+                s.hi_mask |= (uint32_t)(j & 1) << j;
+            return s;
+        }
         const int nbf = u.n0 / KBLK;
         const int nb_lo = min(u.n0 + wn, N - 1) / KBLK;
         const int nb_hi = min(nb_lo + 1, NB - 1);
@@ -536,7 +577,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // When every wave's columns lie in one 128-column scale block (BN a multiple of 128 and
     // TN dividing 128), a row's promotion scale is the same for all of its sub-tiles in a
     // block: scb[i] = sa[i] * sb, formed once per block instead of once per MFMA.
-    constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0);
+    constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0) && !SWIGLU;
     float scb[SM];
     // UE8M0: the block's exponents, for the MFMA's scale operands: eb[jj] for the B block of
     // sub-tile column jj, ea[i] for this lane's row of sub-tile row i
@@ -1009,14 +1050,82 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             }
         }
         uint16_t *D = p.d + (MODE == MODE_MASKED ? (int64_t)cur.g * M * N : 0);
-        if constexpr (PERSIST) {
+        if constexpr (SWIGLU) {
+            // The activation step on the tile's FP32 results, with no rounding in between:
+            // lane (fr, fg) of sub-tile pair pp holds gate (jj = 2 pp) and up (jj = 2 pp + 1) of
+            // h columns c0 + 32 wave_n + 16 pp + 4 fg .. + 3 of row wm + 16 i + fr.  A row's
+            // segment (the tile's 128 h columns) lies on its four lane groups and the WN waves
+            // across: its maximum is a two-step butterfly over the lane groups, then a pass
+            // through a small LDS area of its own.  Then, as the unfused activation step does,
+            // scale = max(amax, 1e-4) / 448 and q = e4m3(h * 448 / max(amax, 1e-4)), stored for
+            // the rows of the tile's group only, with the scales MN-major.
+            if (!cur.empty) {
+                constexpr int SP = SN / 2;
+                const int wave_n = wave % WN;
+                const int half = N >> 1;
+                const int c0 = cur.n0 >> 1;
+                v4f hv[SM][SP];
+#pragma unroll
+                for (int i = 0; i < SM; ++i) {
+                    float rmax = 0.f;
+#pragma unroll
+                    for (int pp = 0; pp < SP; ++pp) {
+                        const v4f g = acc[i][2 * pp], u = acc[i][2 * pp + 1];
+                        hv[i][pp] = v4f{silu_times(g.x, u.x), silu_times(g.y, u.y),
+                                        silu_times(g.z, u.z), silu_times(g.w, u.w)};
+                        rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(hv[i][pp].x), fabsf(hv[i][pp].y)),
+                                                 fmaxf(fabsf(hv[i][pp].z), fabsf(hv[i][pp].w))));
+                    }
+                    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+                    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+                    if (fg == 0)
+                        lds_write4(lds_base + AMX_BASE +
+                                       (uint32_t)(((wm + 16 * i + fr) * WN + wave_n) * 4),
+                                   rmax);
+                }
+                lds_wait();
+                bare_barrier();  // every wave's maxima are in the LDS area
+                v4f am[SM];
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+                    am[i] = lds_read16f_at<0>(lds_base + AMX_BASE +
+                                              (uint32_t)((wm + 16 * i + fr) * WN * 4));
+                lds_wait();
+                uint8_t *Q = p.q + (int64_t)(c0 + 32 * wave_n + 4 * fg);
+#pragma unroll
+                for (int i = 0; i < SM; ++i) {
+                    tie(am[i]);
+                    const float amax = fmaxf(fmaxf(am[i].x, am[i].y), fmaxf(am[i].z, am[i].w));
+                    const float floor_amax = fmaxf(amax, 1e-4f);
+                    const float scale = floor_amax / 448.f;
+                    const float inv = 448.f / floor_amax;
+                    const int row = cur.m0 + wm + 16 * i + fr;
+                    const bool ok = row < cur.row_limit && rowg[i] == cur.g;
+#pragma unroll
+                    for (int pp = 0; pp < SP; ++pp) {
+                        const v4f hh = hv[i][pp];
+                        const float y0 = fminf(fmaxf(hh.x * inv, -448.f), 448.f);
+                        const float y1 = fminf(fmaxf(hh.y * inv, -448.f), 448.f);
+                        const float y2 = fminf(fmaxf(hh.z * inv, -448.f), 448.f);
+                        const float y3 = fminf(fmaxf(hh.w * inv, -448.f), 448.f);
+                        int w = cvt_pk_e4m3<false>(y0, y1, 0);
+                        w = cvt_pk_e4m3<true>(y2, y3, w);
+                        if (ok)
+                            store4_async(Q + (int64_t)row * half + 16 * pp, (uint32_t)w);
+                    }
+                    if (ok && wave_n == 0 && fg == 0)
+                        store4_async(p.sfq + (int64_t)(c0 / KBLK) * p.ld_sfq + row,
+                                     __float_as_uint(scale));
+                }
+            }
+        } else if constexpr (PERSIST) {
             // from registers: the LDS holds the next tile's first blocks
             if (!cur.empty) {
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
                     const int row = cur.m0 + wm + 16 * i + fr;
                     bool ok = row < cur.row_limit;
-                    if constexpr (MODE == MODE_CONTIG)
+                    if constexpr (CONTIG)
                         ok = ok && rowg[i] == cur.g;
 #pragma unroll
                     for (int j = 0; j < SN; ++j) {
@@ -1067,7 +1176,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 piece[t] = lds_read16(lds_base + (uint32_t)((q / CPR) * OS + (q % CPR) * 16));
             }
             int prow[PPT];
-            if constexpr (MODE == MODE_CONTIG) {
+            if constexpr (CONTIG) {
 #pragma unroll
                 for (int t = 0; t < PPT; ++t) {
                     const int row = cur.m0 + (et + t * NT) / CPR;
@@ -1082,7 +1191,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     const int row = cur.m0 + q / CPR;
                     const int col = cur.n0 + (q % CPR) * 8;
                     bool ok = row < cur.row_limit && col < N;
-                    if constexpr (MODE == MODE_CONTIG)
+                    if constexpr (CONTIG)
                         ok = ok && prow[t] == cur.g;
                     if (ok)
                         __builtin_nontemporal_store(
@@ -1166,7 +1275,7 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
 }
 
 template <int BM, int BN, int WM, int WN, int DEPTH, bool PERSIST, int SF>
-static void launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_m, int tiles_n,
+static bool launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_m, int tiles_n,
                          hipStream_t stream)
 {
     // (the UE8M0 variants are built for the forms that use them: direct accumulation for
@@ -1175,17 +1284,32 @@ static void launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_
     case MODE_DENSE:
         hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_DENSE, PERSIST, SF>), g, b, 0,
                            stream, a, tiles_m, tiles_n);
-        break;
+        return true;
     case MODE_CONTIG:
-        if constexpr (SF != SF_UE8M0_PARTIAL && !(BM > 128 && PERSIST))
+        if constexpr (SF != SF_UE8M0_PARTIAL && !(BM > 128 && PERSIST)) {
             hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG, PERSIST, SF>), g,
                                b, 0, stream, a, tiles_m, tiles_n);
-        break;
-    default:
-        if constexpr (SF != SF_UE8M0)
+            return true;
+        }
+        return false;
+    case MODE_MASKED:
+        if constexpr (SF != SF_UE8M0) {
             hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_MASKED, PERSIST, SF>), g,
                                b, 0, stream, a, tiles_m, tiles_n);
-        break;
+            return true;
+        }
+        return false;
+    case MODE_CONTIG_SWIGLU:
+        // (built for the one tile it runs on: 128 x 256, eight waves, FP32 scales)
+        if constexpr (SF == SF_FP32 && PERSIST && BM == 128 && BN == 256 && WN == 4) {
+            hipLaunchKernelGGL(
+                (dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG_SWIGLU, PERSIST, SF>), g, b, 0,
+                stream, a, tiles_m, tiles_n);
+            return true;
+        }
+        return false;
+    default:
+        return false;
     }
 }
 
@@ -1208,13 +1332,18 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     dim3 g((unsigned)grid), b(cfg_threads);
     // UE8M0: MFMAs accumulate directly unless C is added inside the K loop or masked rows
     // skip MFMAs
+    bool launched;
     if (a.sf_fmt == SF_UE8M0 && (mode == MODE_CONTIG || (mode == MODE_DENSE && !a.c)))
-        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0>(mode, g, b, a, tiles_m, tiles_n, stream);
+        launched = launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0>(mode, g, b, a, tiles_m,
+                                                                          tiles_n, stream);
     else if (a.sf_fmt == SF_UE8M0)
-        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0_PARTIAL>(mode, g, b, a, tiles_m,
-                                                                        tiles_n, stream);
+        launched = launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_UE8M0_PARTIAL>(
+            mode, g, b, a, tiles_m, tiles_n, stream);
     else
-        launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_FP32>(mode, g, b, a, tiles_m, tiles_n, stream);
+        launched = launch_modes<BM, BN, WM, WN, DEPTH, PERSIST, SF_FP32>(mode, g, b, a, tiles_m,
+                                                                         tiles_n, stream);
+    if (!launched)
+        return hipErrorInvalidConfiguration;  // no kernel of this form for this tile
     return hipGetLastError();
 }
 

@@ -6,7 +6,15 @@
 
 namespace dg {
 
-enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+enum Mode : int {
+    MODE_DENSE = 0,
+    MODE_CONTIG = 1,
+    MODE_MASKED = 2,
+    // the contiguous form with the activation step fused into its epilogue: B is [G, 2I, K] with
+    // the gate rows first, and instead of D the tile writes the 1x128 FP8 cast of
+    // h = gate * up / (1 + exp(-gate)) (codes q [M, I], MN-major FP32 scales sfq)
+    MODE_CONTIG_SWIGLU = 3
+};
 
 // Scale formats: FP32 (1x128 A segments, 128x128 B blocks), or the same granularity as packed
 // UE8M0 exponents (four K blocks per 32-bit word, least significant byte first).
@@ -61,6 +69,9 @@ struct GemmArgs {
     int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
     int straddle_rows;    // contiguous, 256-row tiles: listed straddling tile-rows whose second
                           // group runs on workgroups ahead of the tiles (0: none)
+    uint8_t *q;           // MODE_CONTIG_SWIGLU: e4m3 codes [m, n/2]
+    float *sfq;           // MODE_CONTIG_SWIGLU: FP32 scales [n/256][ld_sfq] (MN-major)
+    int64_t ld_sfq;
 };
 
 // The MN-major-operand kernel (dg_layout.hip): the dense NN, TN and TT layouts (A stored

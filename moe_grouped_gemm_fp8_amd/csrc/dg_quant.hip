@@ -24,21 +24,6 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// gate * up / (1 + exp(-gate)) with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
-// IEEE division, whose expansion made the step bound by the vector unit
-__device__ __forceinline__ float silu_times(float g, float u)
-{
-    return g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
-}
-
-// two FP32 values (already within +-448) to e4m3 (round to nearest even), packed into bytes
-// 2 sel .. 2 sel + 1 of `old`
-template <bool SEL>
-__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
-{
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, SEL);
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256) void dg_swiglu_quant_kernel(const uint16_t *__restrict__ x,

@@ -81,3 +81,65 @@ def test_padding_rows_are_not_computed():
     assert np.isnan(d1[pad]).all() and np.isnan(h[pad]).all()
     assert not q[pad].any() and not sf[:, :p.m_total][:, pad].any()
     assert not np.isnan(h[~pad]).any() and (sf[:, :p.m_total][:, ~pad] > 0).all()
+
+
+def _rule_inputs(p):
+    from tolerance import gemm_error_bound
+    d1, h, sf, q = oracle.m_grouped_contiguous_swiglu(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    rows = np.nonzero(p.m_indices >= 0)[0]
+    tab = oracle.e4m3_table()
+    err = gemm_error_bound(p.a[rows], p.sfa[:, rows].T, p.b, p.sfb, p.m_indices[rows], tab)
+    return rows, d1[rows], err, h[rows], sf[:, rows].T, q[rows], tab
+
+
+def test_fused_rule_accepts_the_oracle_and_rejects_planted_faults():
+    from tolerance import fused_cast_violations
+    p = W.make_contiguous(3, 400, 512, 384, seed=6, counts=[150, 0, 250], stress=True)
+    rows, d1, err, h, s, q, tab = _rule_inputs(p)
+    bad_s, bad_q, amb = fused_cast_violations(q, s, d1, err, h, s, tab, oracle.e4m3_nearest)
+    assert not bad_s.any() and not bad_q.any()
+    # the worst-case FP32 bound leaves codes of small |y| (where e4m3 steps are finer than it)
+    # undecided; most codes are still decided exactly (under a third without stress inputs,
+    # about half with these stress scales)
+    assert amb < 0.6 * q.size
+    # the rule is not vacuous: a scale off by 2^-10, codes of the neighbouring row, codes one
+    # step off and the gate/up halves swapped all fail it
+    faults = {
+        "scale": (q, s * (1 + 2.0 ** -10)),
+        "row_shift": (np.roll(q, 1, axis=0), s),
+        "codes_one_step_up": (np.where((q & 0x7F) < 0x7E, q + 1, q - 1).astype(np.uint8), s),
+    }
+    for name, (qq, ss) in faults.items():
+        bs, bq, _ = fused_cast_violations(qq, ss, d1, err, h, s, tab, oracle.e4m3_nearest)
+        assert bs.any() or bq.any(), name
+    sw = np.concatenate([p.b[:, 256:], p.b[:, :256]], axis=1)
+    _, h2, sf2, q2 = oracle.m_grouped_contiguous_swiglu(p.a, p.sfa, sw, p.sfb, p.m_indices)
+    bs, bq, _ = fused_cast_violations(q2[rows], sf2[:, rows].T, d1, err, h, s, tab,
+                                      oracle.e4m3_nearest)
+    assert bs.any() or bq.any(), "gate_up_swapped"
+
+
+def test_gemm_error_bound_covers_fp32_accumulation():
+    # the bound holds for an FP32 evaluation of the GEMM in the kernel's order (block sums
+    # accumulated one product at a time in FP32, promoted with an FP32 scale product)
+    from tolerance import gemm_error_bound
+    p = W.make_contiguous(2, 256, 256, 512, seed=7, counts=[128, 128])
+    tab = oracle.e4m3_table()
+    rows = np.arange(256)
+    d1 = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    err = gemm_error_bound(p.a, p.sfa[:, :256].T, p.b, p.sfb, p.m_indices, tab)
+    f32 = np.float32
+    got = np.zeros((256, 256), np.float32)
+    for r in rows[::17]:
+        g = p.m_indices[r]
+        a = tab[p.a[r]].astype(f32)
+        for n in range(0, 256, 13):
+            bvec = tab[p.b[g, n]].astype(f32)
+            acc = f32(0)
+            for kb in range(4):
+                part = f32(0)
+                for t in range(kb * 128, kb * 128 + 128):
+                    part = f32(part + f32(a[t] * bvec[t]))
+                sc = f32(f32(p.sfa[kb, r]) * f32(p.sfb[g, n // 128, kb]))
+                acc = f32(acc + f32(part * sc))
+            assert abs(float(acc) - d1[r, n]) <= err[r, n], (r, n)

@@ -406,6 +406,30 @@ def make_masked(num_groups: int, m_max: int, n: int, k: int, seed: int = 0,
                   m_max=m_max, n=n, k=k)
 
 
+@dataclasses.dataclass
+class MoEBlock:
+    up: Contiguous           # first GEMM: B [G, 2I, K], gate rows first (n = 2I)
+    b2: np.ndarray           # second GEMM's B [G, N2, I] e4m3
+    sfb2: np.ndarray         # [G, ceil(N2/128), I/128]
+    n2: int
+
+
+def make_moe_block(num_groups: int, total_rows: int, n: int, k: int, n2: int, seed: int = 0,
+                   counts=None) -> MoEBlock:
+    """The two GEMMs of an MoE block's experts on the contiguous layout: the first as
+    make_contiguous (n = 2I output columns, gate then up), then the second GEMM's weights,
+    N(0,1) drawn [G, n2, I] from a generator seeded (seed, 2), each cast per 128x128 block."""
+    up = make_contiguous(num_groups, total_rows, n, k, seed=seed, counts=counts)
+    rng = np.random.default_rng((seed, 2))
+    i = n // 2
+    x2 = rng.standard_normal((num_groups, n2, i), dtype=np.float32)
+    b2 = np.empty((num_groups, n2, i), dtype=np.uint8)
+    sfb2 = np.empty((num_groups, (n2 + BLOCK - 1) // BLOCK, i // BLOCK), dtype=np.float32)
+    for g in range(num_groups):
+        b2[g], sfb2[g] = quantize_blocks(x2[g])
+    return MoEBlock(up=up, b2=b2, sfb2=sfb2, n2=n2)
+
+
 # The five workloads the library is measured and checked on (sizes from the method's
 # DeepSeek-V3/R1 inference shapes: hidden 7168, MoE intermediate 2048/4096, 2112-wide
 # low-rank projections).
@@ -419,6 +443,10 @@ CONFIGS = {
     "moe_wgrad": dict(kind="k_grouped", num_groups=8, total_tokens=32768, m=4096, n=7168),
     # SwiGLU + 1x128 FP8 cast of moe_contiguous's 32768 routed rows, expert width I = 2048
     "moe_swiglu_quant": dict(kind="swiglu", m=32768, i=2048),
+    # the experts of an MoE block on moe_contiguous's routing: hidden 7168 -> 2 x 2048 (gate,
+    # up) -> SwiGLU and the 1x128 cast -> 7168
+    "moe_block": dict(kind="moe_block", num_groups=8, total_rows=32768, n=4096, k=7168,
+                      n2=7168),
 }
 
 
@@ -435,4 +463,6 @@ def make_config(name: str, seed: int = 0, **overrides):
         return make_k_grouped(seed=seed, **cfg)
     if kind == "swiglu":
         return make_swiglu_input(seed=seed, **cfg)
+    if kind == "moe_block":
+        return make_moe_block(seed=seed, **cfg)
     return make_masked(seed=seed, **cfg)
