@@ -358,6 +358,9 @@ def make_quant_case(torch, dg, W):
     return c
 
 
+MIN_WARMUP_S = 0.5   # the warm-up also runs until this much time has passed (--min-warmup-s)
+
+
 def time_case(torch, case, steps, warmup):
     """Warm up, then time exactly `steps` steps as one region bracketed by HIP events on the
     launch stream (the step time and, for cases without a per-step device update, the kernel's
@@ -379,7 +382,7 @@ def time_case(torch, case, steps, warmup):
     # and caches are in their steady state when the timed region starts
     t_w = time.perf_counter()
     done = 0
-    while done < warmup or time.perf_counter() - t_w < 0.5:
+    while done < warmup or time.perf_counter() - t_w < MIN_WARMUP_S:
         for i, n in chunks(done, max(cyc, 16)):
             if prep:
                 prep(i)
@@ -569,9 +572,12 @@ def main():
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
+                    help="warm-up time floor (0 under a profiler: warm-up steps only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device copy (reference for HBM-traffic counters)")
     args = ap.parse_args()
+    globals()["MIN_WARMUP_S"] = args.min_warmup_s
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this library"

@@ -348,7 +348,7 @@ int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const v
         args.splits = (kb + kbs - 1) / kbs;
         if (args.splits > 1) {
             void *w = nullptr;
-            const size_t need = (size_t)tiles * args.splits * 64 * 64 * sizeof(float);
+            const size_t need = (size_t)dg::stream_workspace_bytes(tiles, args.splits);
             if (noalloc) {
                 float *sp = nullptr;
                 size_t floats = 0;

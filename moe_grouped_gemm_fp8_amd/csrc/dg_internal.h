@@ -117,6 +117,8 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &args, hipStream_t stre
 // hold, and the launch (rejects a split count that leaves a split empty or too long).
 int64_t stream_grid_size(const GemmArgs &args);
 int stream_max_kblocks();
+// Workspace bytes of a split-K launch (0 without split-K).
+int64_t stream_workspace_bytes(int64_t tiles, int splits);
 hipError_t launch_stream(const GemmArgs &args, hipStream_t stream);
 // Device address (on the current device) and size in floats of the static split-K scratch
 // that the no-allocation entry point uses instead of a workspace.
