@@ -45,8 +45,7 @@ def kernel_source_hash() -> str:
     record stays valid across edits that cannot change the kernels."""
     h = hashlib.sha256()
     for f in ("dg_gemm.hip", "dg_stream.hip", "dg_layout.hip", "dg_quant.hip", "dg_api.cpp",
-              "dg_device.h",
-              "dg_internal.h"):
+              "dg_device.h", "dg_internal.h", "dg_tiles.h"):
         with open(os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"//[^\n]*|/\*.*?\*/", " ", src, flags=re.S)
