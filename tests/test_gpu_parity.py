@@ -189,6 +189,57 @@ def test_split_k_on_two_streams_at_once():
         assert_parity(bits(d), oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "two streams")
 
 
+@pytest.mark.parametrize("m,n,k,splits", [(64, 64, 128 * 30, 30), (64, 208, 128 * 9, 9),
+                                          (128, 576, 128 * 24, 12), (64, 1024, 128 * 40, 40)])
+def test_split_k_repeated_calls_and_graph_replays(m, n, k, splits, monkeypatch):
+    # split-K calls many times in a row, eager and from a captured graph (one tile with many
+    # splits; tile counts that are not multiples of 8), each bit-identical to the first and
+    # within the tolerance
+    monkeypatch.setenv("DG_FORCE_CONFIG", "stream64")
+    monkeypatch.setenv("DG_FORCE_SPLITS", str(splits))
+    p = W.make_dense(m, n, k, seed=57, with_c=True)
+    a, sfa, b, sfb, c = (dev(x) for x in (p.a, p.sfa, p.b, p.sfb, p.c))
+    ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    d = sentinel_like((m, n))
+    dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)      # eager first: allocates the workspace
+    torch.cuda.synchronize()
+    first = bits(d).copy()
+    assert_parity(first, ref, f"split{splits} eager")
+    for _ in range(5):
+        d.fill_(0)
+        dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d), first)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):             # the capture stream's own workspace
+        dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d), first)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)
+    torch.cuda.synchronize()
+    for r in range(4):
+        d.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), first), f"graph replay {r}"
+        dg.fp8_gemm_nt(a, sfa, b, sfb, d, c)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), first), f"eager call after replay {r}"
+
+
+def test_skinny_wide_n_split_k():
+    # M = 64 with a wide N: many column tiles, each split over K
+    p = W.make_dense(64, 8192, 7168, seed=58, with_c=False)
+    ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, None)
+    d1 = run_dense(p)
+    assert_parity(d1, ref, "64x8192x7168")
+    assert np.array_equal(d1, run_dense(p))
+
+
 def test_dense_skinny_workload_full_and_deterministic():
     p = W.make_config("dense_skinny", seed=0)                  # 64 x 2112 x 7168, split K
     ref = oracle.fp8_gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
