@@ -16,6 +16,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import re
 import json
@@ -116,8 +117,17 @@ def _capture(torch, sets, call, per_graph=1):
                 call(s)
         return gr
 
-    singles = [cap([s]) for s in sets]
-    multi = [cap(sets[g0:g0 + per_graph]) for g0 in range(0, len(sets) - per_graph + 1, per_graph)]
+    # graphs of earlier workloads are destroyed here, not by the cyclic garbage collector in the
+    # middle of a capture (destroying a graph while a stream captures is not permitted)
+    gc.collect()
+    torch.cuda.synchronize()
+    gc.disable()
+    try:
+        singles = [cap([s]) for s in sets]
+        multi = [cap(sets[g0:g0 + per_graph])
+                 for g0 in range(0, len(sets) - per_graph + 1, per_graph)]
+    finally:
+        gc.enable()
     torch.cuda.synchronize()
     return singles, multi
 
@@ -635,6 +645,7 @@ def main():
             head = (case, res, summ, steps)
         else:
             del case
+            gc.collect()
             torch.cuda.empty_cache()
 
     case, res, summ, _ = head

@@ -408,16 +408,23 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
                       (dg::kTiles[cfg].bm != 256 || dg::kTiles[cfg].persistent))))
         cfg = -1;
     if (cfg < 0) {
-        const int cands[] = {dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
+        // 256 x 256 (B copied one block ahead) with FP32 scales and N % 256 == 0: its cost is
+        // weighted by its measured per-tile efficiency against 256 x 224 (0.94: one scale
+        // product per row and block, fewer copy bytes per MFMA, less B latency hidden); with
+        // UE8M0 scales it measured slower
+        const int cands[] = {dg::CFG_256x256, dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
         double best = 0;
         for (int cnd : cands) {
             const dg::TileInfo &t = dg::kTiles[cnd];
-            if (cnd == dg::CFG_128x256w8 && n % 256 != 0)
+            if ((cnd == dg::CFG_128x256w8 || cnd == dg::CFG_256x256) && n % 256 != 0)
+                continue;
+            if (cnd == dg::CFG_256x256 && sf_fmt != dg::SF_FP32)
                 continue;
             int64_t rows = (m_total + t.bm - 1) / t.bm;
             if (t.bm > 128)
                 rows += (num_groups - 1) / 2;
-            const double cost = tile_cost(t.bm, t.bn, rows * ((n + t.bn - 1) / t.bn), cus);
+            const double cost = tile_cost(t.bm, t.bn, rows * ((n + t.bn - 1) / t.bn), cus) *
+                                (cnd == dg::CFG_256x256 ? 0.94 : 1.0);
             if (cfg < 0 || cost < best) {
                 best = cost;
                 cfg = cnd;
@@ -502,8 +509,24 @@ int grouped_contiguous_swiglu(const void *a, const float *sfa, int64_t ld_sfa, c
     args.q = (uint8_t *)q;
     args.sfq = sfq;
     args.ld_sfq = ld_sfq;
-    // one tile per 128-column segment of h: 128 rows x (128 gate + 128 up columns)
-    const int cfg = dg::CFG_128x256w8;
+    // one tile per 128-column segment of h, (128 gate + 128 up columns): 256 rows (straddling
+    // tiles run once per group, as in the contiguous form; weighted by the same measured
+    // per-tile efficiency) or 128 rows, persistent
+    int cfg = forced_config();
+    if (cfg != dg::CFG_128x256w8 && cfg != dg::CFG_256x256) {
+        const int64_t rows256 = (m_total + 255) / 256 + (num_groups - 1) / 2;
+        const int64_t rows128 = (m_total + 127) / 128;
+        const double c256 = tile_cost(256, 256, rows256 * (n / 256), cus) * 0.94;
+        const double c128 = tile_cost(128, 256, rows128 * (n / 256), cus);
+        cfg = c256 < c128 ? dg::CFG_256x256 : dg::CFG_128x256w8;
+    }
+    if (cfg == dg::CFG_256x256) {
+        const int tiles_m = (m_total + 255) / 256;
+        args.straddle_rows = tiles_m <= 256 ? (num_groups - 1 < tiles_m ? num_groups - 1 : tiles_m) : 0;
+        const char *e = getenv("DG_STRADDLE_ROWS");  // tests: fewer served slots
+        if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
+            args.straddle_rows = atoi(e);
+    }
     print_config("m_grouped_contiguous_swiglu", m_total, n, k, num_groups, cfg, 1);
     return launch(dg::MODE_CONTIG_SWIGLU, cfg, args, (hipStream_t)stream);
 }

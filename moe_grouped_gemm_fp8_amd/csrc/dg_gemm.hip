@@ -67,6 +67,8 @@ const TileInfo kTiles[CFG_COUNT] = {
     {128, 128, 512, "128x128w8d4", true},
     {128, 256, 512, "128x256w8", true},
     {256, 128, 512, "256x128w8p", true},
+    // B one block ahead (256 x 256 operands fill the LDS): contiguous MoE with N % 256 == 0
+    {256, 256, 512, "256x256w8", false},
 };
 
 // True when 8 consecutive rows `stride` bytes apart start in 8 distinct 32-byte bank groups
@@ -145,16 +147,27 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // the end-of-block barrier of block j - 1: one barrier per block.  Otherwise (NA = DEPTH)
     // the refill takes block j's own A slot, freed only once every wave holds block j's A
     // fragments, which takes a second barrier at the block's start.
+    //
+    // Where DEPTH + 1 B slots do not fit next to DEPTH A slots (256 x 256 tiles: 160 KB of
+    // operands alone), B is copied one block ahead instead (BA = 1, two B slots): block j + 1's
+    // B goes, at block j's start, into block j - 1's B slot, released at block j - 1's end; A
+    // and the scales stay DEPTH blocks ahead.
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
     // (the fused activation step adds an area for the row maxima of its segments: BM x WN floats)
     constexpr int AMX_BYTES = SWIGLU ? BM * WN * 4 : 0;
+    constexpr bool B_FULL =
+        DEPTH * (A_SLOT + 1024 + 256) + (DEPTH + 1) * B_SLOT + AMX_BYTES <= 160 * 1024;
+    constexpr int BA = B_FULL ? DEPTH : 1;  // B look-ahead in blocks
+    constexpr int NBS = BA + 1;             // B slots
+    static_assert(BA == DEPTH || (DEPTH == 2 && !PERSIST),
+                  "B one block ahead: two-block A look-ahead, one tile per workgroup");
     constexpr bool ONE_BAR =
-        (DEPTH + 1) * (A_SLOT + B_SLOT + 1024 + 256) + AMX_BYTES <= 160 * 1024;
+        (DEPTH + 1) * (A_SLOT + 1024 + 256) + NBS * B_SLOT + AMX_BYTES <= 160 * 1024;
     constexpr int NA = ONE_BAR ? DEPTH + 1 : DEPTH;  // A slots (and scale areas)
     constexpr int B_BASE = NA * A_SLOT;
-    constexpr int SA_BASE = B_BASE + (DEPTH + 1) * B_SLOT;
+    constexpr int SA_BASE = B_BASE + NBS * B_SLOT;
     constexpr int SB_BASE = SA_BASE + NA * 1024;
     constexpr int AMX_BASE = SB_BASE + NA * 256;
     constexpr int LDS_BYTES = AMX_BASE + AMX_BYTES;
@@ -167,14 +180,19 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     constexpr int MAXI = CA + CB;                 // + wave 0 copies the block's scales (2)
     static_assert(DEPTH * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    // the staged epilogue (one tile per workgroup) writes the bf16 output tile there, rows OS
+    // bytes apart: OS = 32 (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct banks
+    constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
+    constexpr int LDS_ALLOC = (!PERSIST && BM * OS > LDS_BYTES) ? BM * OS : LDS_BYTES;
+    static_assert(LDS_ALLOC <= 160 * 1024, "LDS budget (output tile)");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_ALLOC];
 
     // SwiGLU: one tile covers the gate and up columns of one 128-wide segment of h (BN = 256),
-    // its waves 4 across (WN = 4, TN = 64: two gate/up sub-tile pairs per wave), FP32 scales
-    static_assert(!SWIGLU || (PERSIST && BN == 256 && WN == 4 && SN == 4 && SF == SF_FP32),
-                  "fused activation step: persistent 256-column tiles, four waves across");
+    // each wave TN / 2 of its h columns (TN / 32 gate/up sub-tile pairs), FP32 scales
+    static_assert(!SWIGLU || (BN == 256 && SN % 2 == 0 && (WN == 2 || WN == 4) && SF == SF_FP32),
+                  "fused activation step: 256-column tiles, two or four waves across");
     // contiguous tiles that may straddle two groups (their last rows may also lie past M)
-    constexpr bool TWO_GROUPS = MODE == MODE_CONTIG && BM > 128;
+    constexpr bool TWO_GROUPS = CONTIG && BM > 128;
     static_assert(!TWO_GROUPS || (BM == 256 && !PERSIST), "straddling tiles: 256 rows, one per workgroup");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -439,12 +457,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         }
     };
     // wait until the next block's copies have landed (those of the DEPTH - 1 blocks after it
-    // may still be in flight)
+    // may still be in flight; with B one block ahead, the next block's B is issued at the
+    // current block's start, before the current block's scale and A copies, which may be)
     auto wait_older_copies = [&]() {
+        constexpr int LATER = BA == DEPTH ? (DEPTH - 1) * MAXI : CA;
         if (wave == 0)
-            wait_vm<(DEPTH - 1) * (MAXI + 2)>();
+            wait_vm<LATER + (DEPTH - 1) * 2>();
         else
-            wait_vm<(DEPTH - 1) * MAXI>();
+            wait_vm<LATER>();
     };
 
     // per-lane fragment offsets inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32) of
@@ -579,6 +599,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // block: scb[i] = sa[i] * sb, formed once per block instead of once per MFMA.
     constexpr bool ONE_NB = (BN % KBLK == 0) && (KBLK % TN == 0) && !SWIGLU;
     float scb[SM];
+    // SwiGLU: even sub-tile columns take the gate block's scale and odd ones the up block's,
+    // so a row has two promotion scales per block, scb[i] and scb2[i]
+    constexpr bool TWO_NB = SWIGLU;
+    float scb2[SM];
     // UE8M0: the block's exponents, for the MFMA's scale operands: eb[jj] for the B block of
     // sub-tile column jj, ea[i] for this lane's row of sub-tile row i
     int eb[SN], ea[SM];
@@ -771,9 +795,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             issue_scales(in ? d : 0, as, s);
 #pragma unroll
             for (int c = 0; c < MAXI; ++c)
-                issue_copy(c, in ? d : 0, as, bs, s);
+                if (c < CA || d < BA)  // B: the first BA blocks
+                    issue_copy(c, in ? d : 0, as, bs, s);
             as = as == NA - 1 ? 0 : as + 1;
-            bs = bs == DEPTH ? 0 : bs + 1;
+            bs = bs == NBS - 1 ? 0 : bs + 1;
         }
         wait_older_copies();
         bare_barrier();
@@ -816,9 +841,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const __amdgpu_buffer_rsrc_t rc = c_src(cur);
         // K block j of the tile, whose refill copies (block kb_fill of the tile behind fs) go
         // out during its steps
-        auto block = [&](int j, const CopySrc &fs, int kb_fill) {
-            const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
-            const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
+        // (B one block ahead: its refill, block kb_fill_b behind fs_b, at the block's start)
+        auto block = [&](int j, const CopySrc &fs, int kb_fill, const CopySrc &fs_b,
+                         int kb_fill_b) {
+            const int bslot_next = bslot == NBS - 1 ? 0 : bslot + 1;
+            const int bslot_fill = bslot == 0 ? NBS - 1 : bslot - 1;  // (j + BA) % (BA + 1)
             const int an = aslot == NA - 1 ? 0 : aslot + 1;
             // the refill's A slot (and scale areas): block j-1's with NA = DEPTH + 1, else
             // block j's own
@@ -847,6 +874,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 for (int i = 0; i < SM; ++i)
                     scb[i] = Sf[i] * sb_cur[0];
             }
+            if constexpr (TWO_NB) {
+#pragma unroll
+                for (int i = 0; i < SM; ++i) {
+                    scb[i] = Sf[i] * sb_cur[0];
+                    scb2[i] = Sf[i] * sb_cur[1];
+                }
+            }
             // two-barrier form: every wave holds this block's A, so its A slot may take block
             // j+DEPTH, whose B slot (block j-1's) was released at the previous block's end
             if constexpr (!ONE_BAR)
@@ -866,10 +900,19 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 if (j == 0 && has_next)
                     load_meta(nxt);
             }
+            // B one block ahead: all of block j + 1's B copies first (the end-of-block wait
+            // counts on their being older than the scale and A copies below)
+            if constexpr (BA < DEPTH) {
+#pragma unroll
+                for (int c = CA; c < MAXI; ++c)
+                    issue_copy(c, kb_fill_b, afill, bslot_fill, fs_b);
+            }
             issue_scales(kb_fill, afill, fs);
+            // the copies spread over the steps: all of them, or the A copies when B went first
+            constexpr int SPREAD = BA == DEPTH ? MAXI : CA;
             if constexpr (SN == 1)
 #pragma unroll
-                for (int c = 0; c < MAXI; ++c)
+                for (int c = 0; c < SPREAD; ++c)
                     issue_copy(c, kb_fill, afill, bslot_fill, fs);
             // steps 0 .. SN-2, with this block's refill copies spread over them
             static_for<SN - 1>([&](auto JJ) {
@@ -879,11 +922,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     if constexpr (i == 0 && jj + 2 < SN)
                         read_b(blo_c, bhi_c, std::integral_constant<int, jj + 2>{},
                                Bf[bbuf(jj + 2, SN)]);
-                    // copies c with c * (SN - 1) / MAXI == jj, after MFMAs 0, 2, ...
+                    // copies c with c * (SN - 1) / SPREAD == jj, after MFMAs 0, 2, ...
 #pragma unroll
-                    for (int c = 0; c < MAXI; ++c) {
-                        if ((c * (SN - 1)) / MAXI == jj) {
-                            const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
+                    for (int c = 0; c < SPREAD; ++c) {
+                        if ((c * (SN - 1)) / SPREAD == jj) {
+                            const int first = (jj * SPREAD + SN - 2) / (SN > 1 ? SN - 1 : 1);
                             const int pos = c - first;
                             if (i == (SM == 1 ? 0 : (pos * 2) % SM))
                                 issue_copy(c, kb_fill, afill, bslot_fill, fs);
@@ -901,7 +944,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     mfma_step(JJ, Bf[0], [&](int i) { return psc[i]; }, extra);
                 else
                     mfma_step(JJ, Bf[bbuf(jj, SN)],
-                              [&](int i) { return ONE_NB ? scb[i] : Sf[i] * sb_cur[jj - 1]; },
+                              [&](int i) {
+                                  if constexpr (TWO_NB)
+                                      return ((jj - 1) & 1) ? scb2[i] : scb[i];
+                                  return ONE_NB ? scb[i] : Sf[i] * sb_cur[jj - 1];
+                              },
                               extra);
             });
             // last step: the next block's copies have landed everywhere (past the last block
@@ -955,6 +1002,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             } else {
                 mfma_step(std::integral_constant<int, SN - 1>{}, Bf[bbuf(SN - 1, SN)],
                           [&](int i) {
+                              if constexpr (TWO_NB) {
+                                  psc[i] = ((SN - 1) & 1) ? scb2[i] : scb[i];
+                                  return ((SN - 2) & 1) ? scb2[i] : scb[i];
+                              }
                               psc[i] = ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 1];
                               return ONE_NB ? scb[i] : Sf[i] * sb_cur[SN - 2];
                           },
@@ -984,14 +1035,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             {
                 const CopySrc s1 = copy_src(cur);
                 for (int j = 0; j < j_sw; ++j)
-                    block(j, s1, j + DEPTH);
+                    block(j, s1, j + DEPTH, s1, j + DEPTH);
             }
             {
                 Tile u = nxt;
                 u.empty = u.empty || !prefetch;
                 const CopySrc s2 = copy_src(u);
                 for (int j = j_sw; j < nkb; ++j)
-                    block(j, s2, prefetch ? j + DEPTH - nkb : 0);
+                    block(j, s2, prefetch ? j + DEPTH - nkb : 0, s2,
+                          prefetch ? j + DEPTH - nkb : 0);
             }
         } else {
             const CopySrc s1 = copy_src(cur);
@@ -1000,7 +1052,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             const CopySrc s0 = copy_src(e);
             for (int j = 0; j < nkb; ++j) {
                 const bool own = j + DEPTH < nkb;
-                block(j, own ? s1 : s0, own ? j + DEPTH : 0);
+                const bool own_b = j + BA < nkb;
+                block(j, own ? s1 : s0, own ? j + DEPTH : 0, own_b ? s1 : s0, own_b ? j + BA : 0);
             }
         }
         // the fragments read during the last step land before their registers can be reused
@@ -1053,10 +1106,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if constexpr (SWIGLU) {
             // The activation step on the tile's FP32 results, with no rounding in between:
             // lane (fr, fg) of sub-tile pair pp holds gate (jj = 2 pp) and up (jj = 2 pp + 1) of
-            // h columns c0 + 32 wave_n + 16 pp + 4 fg .. + 3 of row wm + 16 i + fr.  A row's
-            // segment (the tile's 128 h columns) lies on its four lane groups and the WN waves
-            // across: its maximum is a two-step butterfly over the lane groups, then a pass
-            // through a small LDS area of its own.  Then, as the unfused activation step does,
+            // h columns c0 + (TN / 2) wave_n + 16 pp + 4 fg .. + 3 of row wm + 16 i + fr.  A
+            // row's segment (the tile's 128 h columns) lies on its four lane groups and the WN
+            // waves across: its maximum is a two-step butterfly over the lane groups, then a
+            // pass through a small LDS area of its own.  Then, as the unfused activation step does,
             // scale = max(amax, 1e-4) / 448 and q = e4m3(h * 448 / max(amax, 1e-4)), stored for
             // the rows of the tile's group only, with the scales MN-major.
             if (!cur.empty) {
@@ -1064,17 +1117,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 const int wave_n = wave % WN;
                 const int half = N >> 1;
                 const int c0 = cur.n0 >> 1;
-                v4f hv[SM][SP];
+                // h replaces the gate values in the accumulators (no registers of its own)
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
                     float rmax = 0.f;
 #pragma unroll
                     for (int pp = 0; pp < SP; ++pp) {
                         const v4f g = acc[i][2 * pp], u = acc[i][2 * pp + 1];
-                        hv[i][pp] = v4f{silu_times(g.x, u.x), silu_times(g.y, u.y),
-                                        silu_times(g.z, u.z), silu_times(g.w, u.w)};
-                        rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(hv[i][pp].x), fabsf(hv[i][pp].y)),
-                                                 fmaxf(fabsf(hv[i][pp].z), fabsf(hv[i][pp].w))));
+                        const v4f h = v4f{silu_times(g.x, u.x), silu_times(g.y, u.y),
+                                          silu_times(g.z, u.z), silu_times(g.w, u.w)};
+                        acc[i][2 * pp] = h;
+                        rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)),
+                                                 fmaxf(fabsf(h.z), fabsf(h.w))));
                     }
                     rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
                     rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
@@ -1085,17 +1139,25 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 }
                 lds_wait();
                 bare_barrier();  // every wave's maxima are in the LDS area
+                // the WN maxima of each row: four in one 16-byte read, or two
                 v4f am[SM];
 #pragma unroll
-                for (int i = 0; i < SM; ++i)
-                    am[i] = lds_read16f_at<0>(lds_base + AMX_BASE +
-                                              (uint32_t)((wm + 16 * i + fr) * WN * 4));
+                for (int i = 0; i < SM; ++i) {
+                    const uint32_t at = lds_base + AMX_BASE + (uint32_t)((wm + 16 * i + fr) * WN * 4);
+                    if constexpr (WN == 4) {
+                        am[i] = lds_read16f_at<0>(at);
+                    } else {
+                        am[i].x = lds_read4_at<0>(at);
+                        am[i].y = lds_read4_at<4>(at);
+                    }
+                }
                 lds_wait();
-                uint8_t *Q = p.q + (int64_t)(c0 + 32 * wave_n + 4 * fg);
+                uint8_t *Q = p.q + (int64_t)(c0 + (TN / 2) * wave_n + 4 * fg);
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
                     tie(am[i]);
-                    const float amax = fmaxf(fmaxf(am[i].x, am[i].y), fmaxf(am[i].z, am[i].w));
+                    const float amax = WN == 4 ? fmaxf(fmaxf(am[i].x, am[i].y), fmaxf(am[i].z, am[i].w))
+                                               : fmaxf(am[i].x, am[i].y);
                     const float floor_amax = fmaxf(amax, 1e-4f);
                     const float scale = floor_amax / 448.f;
                     const float inv = 448.f / floor_amax;
@@ -1103,7 +1165,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     const bool ok = row < cur.row_limit && rowg[i] == cur.g;
 #pragma unroll
                     for (int pp = 0; pp < SP; ++pp) {
-                        const v4f hh = hv[i][pp];
+                        const v4f hh = acc[i][2 * pp];
                         const float y0 = fminf(fmaxf(hh.x * inv, -448.f), 448.f);
                         const float y1 = fminf(fmaxf(hh.y * inv, -448.f), 448.f);
                         const float y2 = fminf(fmaxf(hh.z * inv, -448.f), 448.f);
@@ -1145,9 +1207,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             // stores are non-temporal, so they do not push A and B out of the L2.  Output rows are OS bytes apart in LDS; OS = 32
             // (mod 256) puts a fragment write's 16 rows x 32 bytes on distinct banks.
             constexpr int NT = 64 * NW;
-            constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
             static_assert(rows_on_distinct_banks(OS), "output row stride");
-            static_assert(BM * OS <= LDS_BYTES, "output tile fits the operand slots");
+            static_assert(BM * OS <= LDS_ALLOC, "output tile fits the LDS");
             constexpr int CPR = BN / 8;  // 16-byte pieces per output row
             static_assert((BM * CPR) % NT == 0, "output pieces split evenly over the threads");
             constexpr int PPT = BM * CPR / NT;  // pieces per thread
@@ -1256,7 +1317,8 @@ static int64_t workgroups(int64_t total, bool persistent, const GemmArgs &a)
 // 256-row tiles, one workgroup per tile), rounded up to whole rounds of the 8 XCDs
 static int64_t straddle_wgs(int mode, int bm, bool persistent, const GemmArgs &a, int tiles_n)
 {
-    if (mode != MODE_CONTIG || bm <= 128 || persistent || a.straddle_rows <= 0)
+    if ((mode != MODE_CONTIG && mode != MODE_CONTIG_SWIGLU) || bm <= 128 || persistent ||
+        a.straddle_rows <= 0)
         return 0;
     return ((int64_t)a.straddle_rows * tiles_n + 7) / 8 * 8;
 }
@@ -1300,8 +1362,10 @@ static bool launch_modes(int mode, dim3 g, dim3 b, const GemmArgs &a, int tiles_
         }
         return false;
     case MODE_CONTIG_SWIGLU:
-        // (built for the one tile it runs on: 128 x 256, eight waves, FP32 scales)
-        if constexpr (SF == SF_FP32 && PERSIST && BM == 128 && BN == 256 && WN == 4) {
+        // (built for the tiles it runs on: 128 x 256 persistent and 256 x 256, eight waves,
+        // FP32 scales)
+        if constexpr (SF == SF_FP32 && BN == 256 && WM * WN == 8 &&
+                      ((PERSIST && BM == 128 && WN == 4) || (!PERSIST && BM == 256 && WN == 2))) {
             hipLaunchKernelGGL(
                 (dg_gemm_kernel<BM, BN, WM, WN, DEPTH, MODE_CONTIG_SWIGLU, PERSIST, SF>), g, b, 0,
                 stream, a, tiles_m, tiles_n);
@@ -1360,6 +1424,8 @@ hipError_t launch_gemm(int mode, int cfg, const GemmArgs &a, hipStream_t stream)
         return launch_cfg<64, 32, 2, 2>(mode, a, stream);
     case CFG_256x128:
         return launch_cfg<256, 128, 4, 2, 2, false>(mode, a, stream);
+    case CFG_256x256:
+        return launch_cfg<256, 256, 4, 2, 2, false>(mode, a, stream);
     case CFG_256x128p:
         return launch_cfg<256, 128, 4, 2, 2, true>(mode, a, stream);
     case CFG_128x128d4:

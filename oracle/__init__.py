@@ -253,7 +253,8 @@ def swiglu_values(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     i = x.shape[1] // 2
     g, u = x[:, :i], x[:, i:]
-    return g * u / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):       # exp(-g) = inf for a very negative gate: h -> 0
+        return g * u / (1.0 + np.exp(-g))
 
 
 def e4m3_nearest(y) -> np.ndarray:

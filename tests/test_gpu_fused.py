@@ -79,12 +79,24 @@ def check_fused(p, q_dev, sfq_dev, d1=None, what=""):
     return q, sfq
 
 
+# 128 x 256 persistent tiles, and 256 x 256 tiles (B one block ahead), whose tiles can hold
+# two groups: [0,130,41,300,129] -> 128-row blocks 1 1 | 2 3 | 3 3 | 4 4 (one straddle),
+# [41,0,300,1,130] -> 0 2 | 2 2 | 3 4 | 4 - (two, the last tile half past m_total); the second
+# group of a straddle on a workgroup of its own, or (DG_STRADDLE_ROWS=0) in the tile's own
+@pytest.mark.parametrize("cfg,served", [(None, None), ("128x256w8", None), ("256x256w8", None),
+                                        ("256x256w8", "0")])
 @pytest.mark.parametrize("i,k,counts", [(128, 128, [0, 130, 41, 300, 129]),
                                         (256, 640, [0, 130, 41, 300, 129]),
-                                        (384, 384, [200, 0, 0, 57, 300])])
-def test_small_with_padding_and_empty_groups(i, k, counts):
-    p = W.make_contiguous(5, sum(counts), 2 * i, k, seed=200 + i, counts=counts, pad_nan=True)
-    check_fused(p, *run_fused(p), what=f"i={i} k={k}")
+                                        (384, 384, [200, 0, 0, 57, 300]),
+                                        (128, 256, [41, 0, 300, 1, 130])])
+def test_small_with_padding_and_empty_groups(cfg, served, i, k, counts, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
+    p = W.make_contiguous(5, sum(counts), 2 * i, k, seed=200 + i, counts=counts, pad_nan=True,
+                          stress=True)
+    check_fused(p, *run_fused(p), what=f"{cfg} i={i} k={k}")
 
 
 @pytest.mark.parametrize("wgs", ["3", "10"])
@@ -92,14 +104,17 @@ def test_small_with_padding_and_empty_groups(i, k, counts):
 def test_persistent_workgroups_walk_many_tiles(wgs, k, monkeypatch):
     # few workgroups: each walks a run of tiles, prefetching the next tile's first blocks (long
     # K) or restarting its pipeline per tile (short K); the segment maxima's LDS area is reused
+    monkeypatch.setenv("DG_FORCE_CONFIG", "128x256w8")
     monkeypatch.setenv("DG_PERSIST_WGS", wgs)
     p = W.make_contiguous(4, 900, 768, k, seed=210, counts=[300, 41, 0, 559], pad_nan=True)
     check_fused(p, *run_fused(p), what=f"wgs={wgs} k={k}")
 
 
-def test_stress_scales():
+@pytest.mark.parametrize("cfg", ["128x256w8", "256x256w8"])
+def test_stress_scales(cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = W.make_contiguous(4, 700, 512, 512, seed=211, stress=True, pad_nan=True)
-    check_fused(p, *run_fused(p), what="stress")
+    check_fused(p, *run_fused(p), what=f"stress {cfg}")
 
 
 def test_host_checks():

@@ -19,7 +19,7 @@ from tolerance import bf16_bits_to_f64
 pytestmark = pytest.mark.gpu
 
 TILE_CONFIGS = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "256x128w8p", "stream64",
-                "128x128w4d4", "128x128w8d4", "128x256w8"]
+                "128x128w4d4", "128x128w8d4", "128x256w8", "256x256w8"]
 DEEP_CONFIGS = ["128x128w4d4", "128x128w8d4"]
 
 
@@ -260,7 +260,7 @@ def test_dense_prefill_workload_full():
 # ------------------------------------------------------------------------------ contiguous
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
-                                 "128x256w8", "128x256w4"])
+                                 "128x256w8", "128x256w4", "256x256w8"])
 def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -277,7 +277,8 @@ def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
 # num_groups - 1 straddles (DG_STRADDLE_ROWS lowers that: 0 runs every second pass inside the
 # tile's own workgroup, 1 splits the two straddles of the second layout between both paths).
 @pytest.mark.parametrize("cfg,served", [("256x224w8", None), ("256x128w8", None),
-                                        (None, None), ("256x224w8", "0"), ("256x224w8", "1")])
+                                        (None, None), ("256x224w8", "0"), ("256x224w8", "1"),
+                                        ("256x256w8", None), ("256x256w8", "0")])
 @pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
 @pytest.mark.parametrize("n", [448, 400])
 def test_contiguous_256_row_tiles_across_group_boundaries(cfg, served, counts, n, monkeypatch):
@@ -295,7 +296,7 @@ def test_contiguous_256_row_tiles_across_group_boundaries(cfg, served, counts, n
     assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
-@pytest.mark.parametrize("cfg", ["256x224w8", "256x128w8"])
+@pytest.mark.parametrize("cfg", ["256x224w8", "256x128w8", "256x256w8"])
 def test_contiguous_256_row_tile_with_an_all_padding_half(cfg, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = W.make_contiguous(3, 600, 256, 384, seed=35, counts=[200, 250, 150], pad_nan=True)
@@ -306,6 +307,28 @@ def test_contiguous_256_row_tile_with_an_all_padding_half(cfg, monkeypatch):
     got = run_contiguous(p)
     assert_parity(got, ref, f"contiguous padding half {cfg}")
     assert np.all(got[p.m_indices < 0] == W.BF16_SENTINEL), "padding rows were written"
+
+
+# 256 x 256 tiles copy B one block ahead and A two (the LDS holds no third B block): every
+# short K (one to five blocks, where the prologue and the loop's last blocks meet) and a
+# longer one, with straddles and a ragged N
+@pytest.mark.parametrize("k", [128, 256, 384, 512, 640, 1152])
+def test_contiguous_b_one_block_ahead_k_sweep(k, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    p = W.make_contiguous(5, 600, 400, k, seed=38, counts=[0, 130, 41, 300, 129], stress=True,
+                          pad_nan=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"contiguous 256x256 k={k}")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
+@pytest.mark.parametrize("k", [128, 256, 384, 1152])
+def test_masked_b_one_block_ahead_k_sweep(k, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    p = W.make_masked(5, 256, 640, k, seed=42, masked_m=[0, 17, 128, 200, 256], tail_nan=True)
+    ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(run_masked(p), ref, f"masked 256x256 k={k}")
 
 
 @pytest.mark.parametrize("served", [None, "0"])
@@ -363,7 +386,7 @@ def test_contiguous_workload_full(served, monkeypatch):
 # ------------------------------------------------------------------------------ masked
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w4d4", "128x128w8d4",
-                                 "256x128w8", "256x128w8p", "256x224w8"])
+                                 "256x128w8", "256x128w8p", "256x224w8", "256x256w8"])
 def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

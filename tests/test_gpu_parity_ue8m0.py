@@ -19,7 +19,7 @@ from tolerance import bf16_bits_to_f64
 pytestmark = pytest.mark.gpu
 
 PIPELINED = ["256x224w8", "128x256w4", "128x128w4", "64x32w4", "256x128w8", "256x128w8p",
-             "128x128w4d4", "128x128w8d4", "128x256w8"]
+             "128x128w4d4", "128x128w8d4", "128x256w8", "256x256w8"]
 
 
 def _say(msg):
@@ -130,7 +130,7 @@ def test_dense_prefill_workload_full():
 # ------------------------------------------------------------------------------ contiguous
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "128x128w8d4", "128x256w8",
-                                 "256x224w8", "256x128w8"])
+                                 "256x224w8", "256x128w8", "256x256w8"])
 def test_contiguous_small_with_empty_group_and_nan_padding(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -165,7 +165,7 @@ def test_contiguous_workload_full():
 # ------------------------------------------------------------------------------ masked
 
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "64x32w4", "256x128w8", "256x128w8p",
-                                 "256x224w8"])
+                                 "256x224w8", "256x256w8"])
 def test_masked_small_with_clamps_and_nan_tails(cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

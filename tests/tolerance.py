@@ -97,7 +97,8 @@ def fused_cast_violations(q, sf, d1, d1_err, h, scale, table, nearest):
     i = n2 // 2
     g, u = d1[:, :i], d1[:, i:]
     eg, eu = d1_err[:, :i], d1_err[:, i:]
-    sig = 1.0 / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):       # exp(-g) = inf for a very negative gate: sig -> 0
+        sig = 1.0 / (1.0 + np.exp(-g))
     dh_dg = np.abs(u * (sig + g * sig * (1.0 - sig)))
     dh_du = np.abs(g * sig)
     dh = dh_dg * eg + dh_du * eu + (np.abs(u) + 1.0) * eg * (eg + eu) \
