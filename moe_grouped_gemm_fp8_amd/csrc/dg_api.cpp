@@ -408,23 +408,20 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
                       (dg::kTiles[cfg].bm != 256 || dg::kTiles[cfg].persistent))))
         cfg = -1;
     if (cfg < 0) {
-        // 256 x 256 (B copied one block ahead) with FP32 scales and N % 256 == 0: its cost is
-        // weighted by its measured per-tile efficiency against 256 x 224 (0.94: one scale
-        // product per row and block, fewer copy bytes per MFMA, less B latency hidden); with
-        // UE8M0 scales it measured slower
+        // 256 x 256 (scales in registers) when N % 256 == 0: its cost is weighted by its
+        // measured per-tile efficiency against 256 x 224 (0.92 with FP32 scales: one scale
+        // product per row and block, fewer copy bytes per MFMA; better still with UE8M0)
         const int cands[] = {dg::CFG_256x256, dg::CFG_256x224, dg::CFG_128x256w8, dg::CFG_128x128};
         double best = 0;
         for (int cnd : cands) {
             const dg::TileInfo &t = dg::kTiles[cnd];
             if ((cnd == dg::CFG_128x256w8 || cnd == dg::CFG_256x256) && n % 256 != 0)
                 continue;
-            if (cnd == dg::CFG_256x256 && sf_fmt != dg::SF_FP32)
-                continue;
             int64_t rows = (m_total + t.bm - 1) / t.bm;
             if (t.bm > 128)
                 rows += (num_groups - 1) / 2;
             const double cost = tile_cost(t.bm, t.bn, rows * ((n + t.bn - 1) / t.bn), cus) *
-                                (cnd == dg::CFG_256x256 ? 0.94 : 1.0);
+                                (cnd == dg::CFG_256x256 ? 0.92 : 1.0);
             if (cfg < 0 || cost < best) {
                 best = cost;
                 cfg = cnd;
@@ -556,9 +553,10 @@ int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, 
     // masked_m skip their MFMAs and read zeros, so the taller tile costs little, and it reads
     // each B column block once where two 128-row tiles may read it twice.  So the choice depends
     // on m_max (one 256-row tile per N tile when the groups can exceed 128 rows) and not on the
-    // hint, which is printed with the choice.  Of the two 256-row widths, the one with less
-    // column padding, the wider on a tie (each N tile re-reads the group's A from L2, so fewer,
-    // wider tiles read less).
+    // hint, which is printed with the choice.  Of the 256-row widths, the one with less column
+    // padding, the wider on a tie (each N tile re-reads the group's A from L2, so fewer, wider
+    // tiles read less); 256 columns with FP32 scales only (measured 67.0 against 68.0 us for
+    // 224 on the shape above).
     const int e = expected_m > 0 ? (expected_m < m_max ? expected_m : m_max) : (m_max + 1) / 2;
     int cfg = forced_config();
     if (cfg < 0 || cfg == dg::CFG_STREAM64) {
@@ -566,6 +564,8 @@ int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, 
             const int64_t pad224 = (int64_t)((n + 223) / 224) * 224 - n;
             const int64_t pad128 = (int64_t)((n + 127) / 128) * 128 - n;
             cfg = pad224 <= pad128 ? dg::CFG_256x224 : dg::CFG_256x128;
+            if (sf_fmt == dg::SF_FP32 && n % 256 == 0)
+                cfg = dg::CFG_256x256;  // no padding: as little as either, and the widest
         } else {
             cfg = dg::CFG_128x128;
         }

@@ -148,29 +148,45 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // the refill takes block j's own A slot, freed only once every wave holds block j's A
     // fragments, which takes a second barrier at the block's start.
     //
-    // Where DEPTH + 1 B slots do not fit next to DEPTH A slots (256 x 256 tiles: 160 KB of
-    // operands alone), B is copied one block ahead instead (BA = 1, two B slots): block j + 1's
-    // B goes, at block j's start, into block j - 1's B slot, released at block j - 1's end; A
-    // and the scales stay DEPTH blocks ahead.
+    // Where the scale areas do not fit next to DEPTH A and DEPTH + 1 B slots (256 x 256 tiles:
+    // 160 KB of operands alone), the scales go to registers instead (SREG): each wave loads
+    // its rows' A scales and its B scales for block j + 1 at block j's start, from the L2, and
+    // takes them at block j's end.  Where even the operands do not fit, B is copied one block
+    // ahead (BA = 1, two B slots): block j + 1's B goes, at block j's start, into block j - 1's
+    // B slot, released at block j - 1's end; A and the scales stay DEPTH blocks ahead.
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
-    // (the fused activation step adds an area for the row maxima of its segments: BM x WN floats)
+    // (the fused activation step adds an area for the row maxima of its segments: BM x WN
+    // floats; with one tile per workgroup it reuses the operand slots, free by then)
     constexpr int AMX_BYTES = SWIGLU ? BM * WN * 4 : 0;
+    constexpr bool AMX_ALIAS = !PERSIST;
+    constexpr int AMX_OWN = AMX_ALIAS ? 0 : AMX_BYTES;
+    constexpr int SCL = 1024 + 256;  // an A slot's scale areas (A scales, B scales)
     constexpr bool B_FULL =
-        DEPTH * (A_SLOT + 1024 + 256) + (DEPTH + 1) * B_SLOT + AMX_BYTES <= 160 * 1024;
-    constexpr int BA = B_FULL ? DEPTH : 1;  // B look-ahead in blocks
-    constexpr int NBS = BA + 1;             // B slots
+        DEPTH * (A_SLOT + SCL) + (DEPTH + 1) * B_SLOT + AMX_OWN <= 160 * 1024;
+    // (not for the fused activation step: at 256 x 256 its registers run out, and the
+    // compiler then waits for every copy at each block's start)
+    // (not for the fused activation step: at 256 x 256 its registers run out, and the
+    // compiler, reusing a scale load's register across the loop, then waits for every copy at
+    // each block's start; it copies B one block ahead instead)
+    constexpr bool SREG = !B_FULL && !PERSIST && !SWIGLU &&
+                          DEPTH * A_SLOT + (DEPTH + 1) * B_SLOT + AMX_OWN <= 160 * 1024;
+    constexpr int BA = (B_FULL || SREG) ? DEPTH : 1;  // B look-ahead in blocks
+    constexpr int NBS = BA + 1;                        // B slots
     static_assert(BA == DEPTH || (DEPTH == 2 && !PERSIST),
                   "B one block ahead: two-block A look-ahead, one tile per workgroup");
+    constexpr int SCL_LDS = SREG ? 0 : SCL;
     constexpr bool ONE_BAR =
-        (DEPTH + 1) * (A_SLOT + 1024 + 256) + NBS * B_SLOT + AMX_BYTES <= 160 * 1024;
+        (DEPTH + 1) * (A_SLOT + SCL_LDS) + NBS * B_SLOT + AMX_OWN <= 160 * 1024;
     constexpr int NA = ONE_BAR ? DEPTH + 1 : DEPTH;  // A slots (and scale areas)
     constexpr int B_BASE = NA * A_SLOT;
     constexpr int SA_BASE = B_BASE + NBS * B_SLOT;
-    constexpr int SB_BASE = SA_BASE + NA * 1024;
-    constexpr int AMX_BASE = SB_BASE + NA * 256;
-    constexpr int LDS_BYTES = AMX_BASE + AMX_BYTES;
+    constexpr int SB_BASE = SA_BASE + (SREG ? 0 : NA * 1024);
+    constexpr int OPS_END = SB_BASE + (SREG ? 0 : NA * 256);
+    constexpr int AMX_BASE = AMX_ALIAS ? 0 : OPS_END;
+    constexpr int LDS_BYTES = AMX_ALIAS ? (OPS_END > AMX_BYTES ? OPS_END : AMX_BYTES)
+                                        : OPS_END + AMX_BYTES;
     static_assert(A_SLOT % 4096 == 0 && B_SLOT % 4096 == 0, "slots start on 4 KB boundaries");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     constexpr int IA = BM / 8, IB = BN / 8;       // 1 KB copies (8 rows of 128 bytes)
@@ -440,7 +456,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 (uint32_t)kb * KBLK, 0, 0);
     };
     auto issue_scales = [&](int kb, int aslot, const CopySrc &s) {
-        if (wave == 0) {
+        if (!SREG && wave == 0) {
             // the K block's row offset goes into the range-checked lane offset: rows past the
             // last scale row read zeros
             uint32_t vo = lane_sfa;
@@ -459,12 +475,20 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // wait until the next block's copies have landed (those of the DEPTH - 1 blocks after it
     // may still be in flight; with B one block ahead, the next block's B is issued at the
     // current block's start, before the current block's scale and A copies, which may be)
-    auto wait_older_copies = [&]() {
+    // (SREG: no scale copies; inside the K loop each block's register loads of the next
+    // block's scales, SM + 2 per wave, precede its copies)
+    auto wait_older_copies = [&](bool in_loop) {
         constexpr int LATER = BA == DEPTH ? (DEPTH - 1) * MAXI : CA;
-        if (wave == 0)
+        if constexpr (SREG) {
+            if (in_loop)
+                wait_vm<LATER + (DEPTH - 1) * (SM + 2)>();
+            else
+                wait_vm<LATER>();
+        } else if (wave == 0) {
             wait_vm<LATER + (DEPTH - 1) * 2>();
-        else
+        } else {
             wait_vm<LATER>();
+        }
     };
 
     // per-lane fragment offsets inside a slot: lanes 16g..16g+15 hold K bytes [32g, 32g+32) of
@@ -536,9 +560,34 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         return s;
     };
     float vsb_lo, vsb_hi;  // this block's two B scales (all lanes equal)
+    // SREG: the next block's scales, loaded into registers at the current block's start: this
+    // lane's rows' A scales and the wave's two B scales (the offsets of the LDS form's lanes
+    // sel.lo / 4 and sel.hi / 4 in the B-scale copy)
+    float Sn[SM], vbn_lo, vbn_hi;
+    auto load_scales = [&](int kb, const CopySrc &s, const ScaleSel &sl) {
+        const int ks = UE8 ? kb >> 2 : kb;  // the scale column holding block kb
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+            Sn[i] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(
+                           s.sa, (uint32_t)(((int64_t)ks * ld + wm + 16 * i + fr) * 4), 0, 0));
+        const uint32_t blo = SWIGLU ? 0u : sl.lo * (uint32_t)KS;
+        const uint32_t bhi = SWIGLU ? (uint32_t)(N >> 8) * (uint32_t)KS * 4u : sl.hi * (uint32_t)KS;
+        vbn_lo = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(s.sb, blo + (uint32_t)ks * 4u, 0, 0));
+        vbn_hi = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(s.sb, bhi + (uint32_t)ks * 4u, 0, 0));
+    };
     auto read_sfb = [&](int aslot, const ScaleSel &s) {
-        vsb_lo = lds_read4(lds_base + SB_BASE + s.lo + (uint32_t)(aslot * 256));
-        vsb_hi = lds_read4(lds_base + SB_BASE + s.hi + (uint32_t)(aslot * 256));
+        if constexpr (SREG) {
+            tie(vbn_lo);
+            tie(vbn_hi);
+            vsb_lo = vbn_lo;
+            vsb_hi = vbn_hi;
+        } else {
+            vsb_lo = lds_read4(lds_base + SB_BASE + s.lo + (uint32_t)(aslot * 256));
+            vsb_hi = lds_read4(lds_base + SB_BASE + s.hi + (uint32_t)(aslot * 256));
+        }
     };
 
     // C, streamed into the accumulators (dense form).  Block c_j0 + 2 jj + h loads half h of
@@ -634,7 +683,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         constexpr int i = decltype(I)::value;
         Af[i][0] = lds_read16_at<i * 16 * KBLK>(alo);
         Af[i][1] = lds_read16_at<i * 16 * KBLK>(ahi);
-        Sf[i] = lds_read4_at<i * 64>(sa);
+        if constexpr (SREG) {
+            // loaded at the block's start; the use here makes the compiler's own wait for
+            // them fall inside this block (counting this block's copies after them), not at
+            // the next block's start, where it cannot count across the loop and waits for all
+            tie(Sn[i]);
+            Sf[i] = Sn[i];
+        } else
+            Sf[i] = lds_read4_at<i * 64>(sa);
     };
     auto read_b = [&](uint32_t blo, uint32_t bhi, auto JJ, v4i (&bf)[2]) {
         constexpr int jj = decltype(JJ)::value;
@@ -775,6 +831,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // barrier)
     auto read_first = [&]() {
         const uint32_t ao = (uint32_t)(aslot * A_SLOT), bo = (uint32_t)(bslot * B_SLOT);
+        if constexpr (SREG)
+            load_scales(0, copy_src(cur), sel);  // (one tile per workgroup)
         static_for<SM>(
             [&](auto I) { read_a(a_lo + ao, a_hi + ao, sa_lane + (uint32_t)(aslot * 1024), I); });
         read_sfb(aslot, sel);
@@ -800,7 +858,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             as = as == NA - 1 ? 0 : as + 1;
             bs = bs == NBS - 1 ? 0 : bs + 1;
         }
-        wait_older_copies();
+        wait_older_copies(false);
         bare_barrier();
         read_first();
     };
@@ -842,8 +900,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         // K block j of the tile, whose refill copies (block kb_fill of the tile behind fs) go
         // out during its steps
         // (B one block ahead: its refill, block kb_fill_b behind fs_b, at the block's start)
+        // (SREG: the tile's own source fsr for the next block's scales)
         auto block = [&](int j, const CopySrc &fs, int kb_fill, const CopySrc &fs_b,
-                         int kb_fill_b) {
+                         int kb_fill_b, const CopySrc &fsr) {
             const int bslot_next = bslot == NBS - 1 ? 0 : bslot + 1;
             const int bslot_fill = bslot == 0 ? NBS - 1 : bslot - 1;  // (j + BA) % (BA + 1)
             const int an = aslot == NA - 1 ? 0 : aslot + 1;
@@ -908,6 +967,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     issue_copy(c, kb_fill_b, afill, bslot_fill, fs_b);
             }
             issue_scales(kb_fill, afill, fs);
+            if constexpr (SREG)
+                load_scales(j + 1, fsr, sel);  // before the copies: the end-of-block wait counts
             // the copies spread over the steps: all of them, or the A copies when B went first
             constexpr int SPREAD = BA == DEPTH ? MAXI : CA;
             if constexpr (SN == 1)
@@ -955,7 +1016,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             // of the workgroup the reads below are harmless and unused); in the one-barrier
             // form every wave has also finished reading this block's slots, which the next
             // block's refill takes
-            wait_older_copies();
+            wait_older_copies(true);
             if constexpr (ONE_BAR)
                 lds_wait();
             bare_barrier();
@@ -1035,7 +1096,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             {
                 const CopySrc s1 = copy_src(cur);
                 for (int j = 0; j < j_sw; ++j)
-                    block(j, s1, j + DEPTH, s1, j + DEPTH);
+                    block(j, s1, j + DEPTH, s1, j + DEPTH, s1);
             }
             {
                 Tile u = nxt;
@@ -1043,7 +1104,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 const CopySrc s2 = copy_src(u);
                 for (int j = j_sw; j < nkb; ++j)
                     block(j, s2, prefetch ? j + DEPTH - nkb : 0, s2,
-                          prefetch ? j + DEPTH - nkb : 0);
+                          prefetch ? j + DEPTH - nkb : 0, s2);
             }
         } else {
             const CopySrc s1 = copy_src(cur);
@@ -1053,7 +1114,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             for (int j = 0; j < nkb; ++j) {
                 const bool own = j + DEPTH < nkb;
                 const bool own_b = j + BA < nkb;
-                block(j, own ? s1 : s0, own ? j + DEPTH : 0, own_b ? s1 : s0, own_b ? j + BA : 0);
+                block(j, own ? s1 : s0, own ? j + DEPTH : 0, own_b ? s1 : s0, own_b ? j + BA : 0,
+                      s1);
             }
         }
         // the fragments read during the last step land before their registers can be reused
@@ -1132,6 +1194,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     }
                     rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
                     rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+                    if constexpr (AMX_ALIAS) {
+                        // the area lies in the operand slots: every copy has landed (the last
+                        // blocks' refills write zeros there) and every wave is past its reads
+                        if (i == 0) {
+                            wait_vm<0>();
+                            bare_barrier();
+                        }
+                    }
                     if (fg == 0)
                         lds_write4(lds_base + AMX_BASE +
                                        (uint32_t)(((wm + 16 * i + fr) * WN + wave_n) * 4),

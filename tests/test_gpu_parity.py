@@ -451,8 +451,9 @@ def test_masked_graph_replays_follow_device_masked_m():
 @pytest.mark.parametrize("expected_m", [16, 64, 200, 0])
 def test_masked_expected_m_is_reported_with_the_tile(expected_m, monkeypatch, capfd):
     # the host hint is printed with the tile choice (DG_PRINT_CONFIGS); 256-row tiles were
-    # measured fastest at every expected count, so the choice stays 256x224 for this shape
-    tile = "256x224w8"
+    # measured fastest at every expected count, so the choice stays the widest unpadded one,
+    # 256x256, for this shape
+    tile = "256x256w8"
     monkeypatch.setenv("DG_PRINT_CONFIGS", "1")
     mm = [0, 3, 17, 64, 100, 130, 255, 256]
     # N = 1792 = 8 x 224 = 7 x 256: no column padding for either width
