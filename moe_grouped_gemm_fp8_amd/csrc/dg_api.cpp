@@ -513,7 +513,7 @@ int grouped_contiguous_swiglu(const void *a, const float *sfa, int64_t ld_sfa, c
     if (cfg != dg::CFG_128x256w8 && cfg != dg::CFG_256x256) {
         const int64_t rows256 = (m_total + 255) / 256 + (num_groups - 1) / 2;
         const int64_t rows128 = (m_total + 127) / 128;
-        const double c256 = tile_cost(256, 256, rows256 * (n / 256), cus) * 0.94;
+        const double c256 = tile_cost(256, 256, rows256 * (n / 256), cus) * 0.92;
         const double c128 = tile_cost(128, 256, rows128 * (n / 256), cus);
         cfg = c256 < c128 ? dg::CFG_256x256 : dg::CFG_128x256w8;
     }

@@ -67,7 +67,8 @@ const TileInfo kTiles[CFG_COUNT] = {
     {128, 128, 512, "128x128w8d4", true},
     {128, 256, 512, "128x256w8", true},
     {256, 128, 512, "256x128w8p", true},
-    // B one block ahead (256 x 256 operands fill the LDS): contiguous MoE with N % 256 == 0
+    // scales in registers (256 x 256 operands fill the LDS): contiguous MoE and masked with
+    // N % 256 == 0
     {256, 256, 512, "256x256w8", false},
 };
 
@@ -151,9 +152,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // Where the scale areas do not fit next to DEPTH A and DEPTH + 1 B slots (256 x 256 tiles:
     // 160 KB of operands alone), the scales go to registers instead (SREG): each wave loads
     // its rows' A scales and its B scales for block j + 1 at block j's start, from the L2, and
-    // takes them at block j's end.  Where even the operands do not fit, B is copied one block
-    // ahead (BA = 1, two B slots): block j + 1's B goes, at block j's start, into block j - 1's
-    // B slot, released at block j - 1's end; A and the scales stay DEPTH blocks ahead.
+    // takes them at block j's end.
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
@@ -163,25 +162,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     constexpr bool AMX_ALIAS = !PERSIST;
     constexpr int AMX_OWN = AMX_ALIAS ? 0 : AMX_BYTES;
     constexpr int SCL = 1024 + 256;  // an A slot's scale areas (A scales, B scales)
-    constexpr bool B_FULL =
-        DEPTH * (A_SLOT + SCL) + (DEPTH + 1) * B_SLOT + AMX_OWN <= 160 * 1024;
-    // (not for the fused activation step: at 256 x 256 its registers run out, and the
-    // compiler then waits for every copy at each block's start)
-    // (not for the fused activation step: at 256 x 256 its registers run out, and the
-    // compiler, reusing a scale load's register across the loop, then waits for every copy at
-    // each block's start; it copies B one block ahead instead)
-    constexpr bool SREG = !B_FULL && !PERSIST && !SWIGLU &&
-                          DEPTH * A_SLOT + (DEPTH + 1) * B_SLOT + AMX_OWN <= 160 * 1024;
-    constexpr int BA = (B_FULL || SREG) ? DEPTH : 1;  // B look-ahead in blocks
-    constexpr int NBS = BA + 1;                        // B slots
-    static_assert(BA == DEPTH || (DEPTH == 2 && !PERSIST),
-                  "B one block ahead: two-block A look-ahead, one tile per workgroup");
+    constexpr bool SREG =
+        DEPTH * (A_SLOT + SCL) + (DEPTH + 1) * B_SLOT + AMX_OWN > 160 * 1024;
+    static_assert(!SREG || (!PERSIST && DEPTH * A_SLOT + (DEPTH + 1) * B_SLOT <= 160 * 1024),
+                  "scales in registers: one tile per workgroup, operands within the LDS");
     constexpr int SCL_LDS = SREG ? 0 : SCL;
     constexpr bool ONE_BAR =
-        (DEPTH + 1) * (A_SLOT + SCL_LDS) + NBS * B_SLOT + AMX_OWN <= 160 * 1024;
+        (DEPTH + 1) * (A_SLOT + SCL_LDS + B_SLOT) + AMX_OWN <= 160 * 1024;
     constexpr int NA = ONE_BAR ? DEPTH + 1 : DEPTH;  // A slots (and scale areas)
     constexpr int B_BASE = NA * A_SLOT;
-    constexpr int SA_BASE = B_BASE + NBS * B_SLOT;
+    constexpr int SA_BASE = B_BASE + (DEPTH + 1) * B_SLOT;
     constexpr int SB_BASE = SA_BASE + (SREG ? 0 : NA * 1024);
     constexpr int OPS_END = SB_BASE + (SREG ? 0 : NA * 256);
     constexpr int AMX_BASE = AMX_ALIAS ? 0 : OPS_END;
@@ -473,12 +463,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         }
     };
     // wait until the next block's copies have landed (those of the DEPTH - 1 blocks after it
-    // may still be in flight; with B one block ahead, the next block's B is issued at the
-    // current block's start, before the current block's scale and A copies, which may be)
-    // (SREG: no scale copies; inside the K loop each block's register loads of the next
-    // block's scales, SM + 2 per wave, precede its copies)
+    // may still be in flight).  SREG: no scale copies; inside the K loop each block's register
+    // loads of the next block's scales, SM + 2 per wave, precede its copies and may still be
+    // in flight too (their own wait comes at the block's last step).
     auto wait_older_copies = [&](bool in_loop) {
-        constexpr int LATER = BA == DEPTH ? (DEPTH - 1) * MAXI : CA;
+        constexpr int LATER = (DEPTH - 1) * MAXI;
         if constexpr (SREG) {
             if (in_loop)
                 wait_vm<LATER + (DEPTH - 1) * (SM + 2)>();
@@ -853,10 +842,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             issue_scales(in ? d : 0, as, s);
 #pragma unroll
             for (int c = 0; c < MAXI; ++c)
-                if (c < CA || d < BA)  // B: the first BA blocks
-                    issue_copy(c, in ? d : 0, as, bs, s);
+                issue_copy(c, in ? d : 0, as, bs, s);
             as = as == NA - 1 ? 0 : as + 1;
-            bs = bs == NBS - 1 ? 0 : bs + 1;
+            bs = bs == DEPTH ? 0 : bs + 1;
         }
         wait_older_copies(false);
         bare_barrier();
@@ -899,12 +887,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const __amdgpu_buffer_rsrc_t rc = c_src(cur);
         // K block j of the tile, whose refill copies (block kb_fill of the tile behind fs) go
         // out during its steps
-        // (B one block ahead: its refill, block kb_fill_b behind fs_b, at the block's start)
         // (SREG: the tile's own source fsr for the next block's scales)
-        auto block = [&](int j, const CopySrc &fs, int kb_fill, const CopySrc &fs_b,
-                         int kb_fill_b, const CopySrc &fsr) {
-            const int bslot_next = bslot == NBS - 1 ? 0 : bslot + 1;
-            const int bslot_fill = bslot == 0 ? NBS - 1 : bslot - 1;  // (j + BA) % (BA + 1)
+        auto block = [&](int j, const CopySrc &fs, int kb_fill, const CopySrc &fsr) {
+            const int bslot_next = bslot == DEPTH ? 0 : bslot + 1;
+            const int bslot_fill = bslot == 0 ? DEPTH : bslot - 1;  // (j + DEPTH) % (DEPTH + 1)
             const int an = aslot == NA - 1 ? 0 : aslot + 1;
             // the refill's A slot (and scale areas): block j-1's with NA = DEPTH + 1, else
             // block j's own
@@ -959,21 +945,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 if (j == 0 && has_next)
                     load_meta(nxt);
             }
-            // B one block ahead: all of block j + 1's B copies first (the end-of-block wait
-            // counts on their being older than the scale and A copies below)
-            if constexpr (BA < DEPTH) {
-#pragma unroll
-                for (int c = CA; c < MAXI; ++c)
-                    issue_copy(c, kb_fill_b, afill, bslot_fill, fs_b);
-            }
             issue_scales(kb_fill, afill, fs);
             if constexpr (SREG)
                 load_scales(j + 1, fsr, sel);  // before the copies: the end-of-block wait counts
-            // the copies spread over the steps: all of them, or the A copies when B went first
-            constexpr int SPREAD = BA == DEPTH ? MAXI : CA;
             if constexpr (SN == 1)
 #pragma unroll
-                for (int c = 0; c < SPREAD; ++c)
+                for (int c = 0; c < MAXI; ++c)
                     issue_copy(c, kb_fill, afill, bslot_fill, fs);
             // steps 0 .. SN-2, with this block's refill copies spread over them
             static_for<SN - 1>([&](auto JJ) {
@@ -983,11 +960,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     if constexpr (i == 0 && jj + 2 < SN)
                         read_b(blo_c, bhi_c, std::integral_constant<int, jj + 2>{},
                                Bf[bbuf(jj + 2, SN)]);
-                    // copies c with c * (SN - 1) / SPREAD == jj, after MFMAs 0, 2, ...
+                    // copies c with c * (SN - 1) / MAXI == jj, after MFMAs 0, 2, ...
 #pragma unroll
-                    for (int c = 0; c < SPREAD; ++c) {
-                        if ((c * (SN - 1)) / SPREAD == jj) {
-                            const int first = (jj * SPREAD + SN - 2) / (SN > 1 ? SN - 1 : 1);
+                    for (int c = 0; c < MAXI; ++c) {
+                        if ((c * (SN - 1)) / MAXI == jj) {
+                            const int first = (jj * MAXI + SN - 2) / (SN > 1 ? SN - 1 : 1);
                             const int pos = c - first;
                             if (i == (SM == 1 ? 0 : (pos * 2) % SM))
                                 issue_copy(c, kb_fill, afill, bslot_fill, fs);
@@ -1096,15 +1073,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             {
                 const CopySrc s1 = copy_src(cur);
                 for (int j = 0; j < j_sw; ++j)
-                    block(j, s1, j + DEPTH, s1, j + DEPTH, s1);
+                    block(j, s1, j + DEPTH, s1);
             }
             {
                 Tile u = nxt;
                 u.empty = u.empty || !prefetch;
                 const CopySrc s2 = copy_src(u);
                 for (int j = j_sw; j < nkb; ++j)
-                    block(j, s2, prefetch ? j + DEPTH - nkb : 0, s2,
-                          prefetch ? j + DEPTH - nkb : 0, s2);
+                    block(j, s2, prefetch ? j + DEPTH - nkb : 0, s2);
             }
         } else {
             const CopySrc s1 = copy_src(cur);
@@ -1113,9 +1089,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             const CopySrc s0 = copy_src(e);
             for (int j = 0; j < nkb; ++j) {
                 const bool own = j + DEPTH < nkb;
-                const bool own_b = j + BA < nkb;
-                block(j, own ? s1 : s0, own ? j + DEPTH : 0, own_b ? s1 : s0, own_b ? j + BA : 0,
-                      s1);
+                block(j, own ? s1 : s0, own ? j + DEPTH : 0, s1);
             }
         }
         // the fragments read during the last step land before their registers can be reused
@@ -1179,6 +1153,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 const int wave_n = wave % WN;
                 const int half = N >> 1;
                 const int c0 = cur.n0 >> 1;
+                // lane coordinates from an opaque copy of the thread id, and the rows' groups
+                // loaded again here: nothing of the epilogue's is held through the K loop
+                int et = tid;
+                asm volatile("" : "+v"(et));
+                const int efr = et & 15, efg = (et >> 4) & 3;
                 // h replaces the gate values in the accumulators (no registers of its own)
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
@@ -1202,9 +1181,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                             bare_barrier();
                         }
                     }
-                    if (fg == 0)
+                    if (efg == 0)
                         lds_write4(lds_base + AMX_BASE +
-                                       (uint32_t)(((wm + 16 * i + fr) * WN + wave_n) * 4),
+                                       (uint32_t)(((wm + 16 * i + efr) * WN + wave_n) * 4),
                                    rmax);
                 }
                 lds_wait();
@@ -1213,7 +1192,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 v4f am[SM];
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
-                    const uint32_t at = lds_base + AMX_BASE + (uint32_t)((wm + 16 * i + fr) * WN * 4);
+                    const uint32_t at = lds_base + AMX_BASE + (uint32_t)((wm + 16 * i + efr) * WN * 4);
                     if constexpr (WN == 4) {
                         am[i] = lds_read16f_at<0>(at);
                     } else {
@@ -1222,7 +1201,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     }
                 }
                 lds_wait();
-                uint8_t *Q = p.q + (int64_t)(c0 + (TN / 2) * wave_n + 4 * fg);
+                uint8_t *Q = p.q + (int64_t)(c0 + (TN / 2) * wave_n + 4 * efg);
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
                     tie(am[i]);
@@ -1231,8 +1210,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     const float floor_amax = fmaxf(amax, 1e-4f);
                     const float scale = floor_amax / 448.f;
                     const float inv = 448.f / floor_amax;
-                    const int row = cur.m0 + wm + 16 * i + fr;
-                    const bool ok = row < cur.row_limit && rowg[i] == cur.g;
+                    const int row = cur.m0 + wm + 16 * i + efr;
+                    const bool ok = row < cur.row_limit && p.grp[row < M ? row : 0] == cur.g;
 #pragma unroll
                     for (int pp = 0; pp < SP; ++pp) {
                         const v4f hh = acc[i][2 * pp];
@@ -1245,7 +1224,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                         if (ok)
                             store4_async(Q + (int64_t)row * half + 16 * pp, (uint32_t)w);
                     }
-                    if (ok && wave_n == 0 && fg == 0)
+                    if (ok && wave_n == 0 && efg == 0)
                         store4_async(p.sfq + (int64_t)(c0 / KBLK) * p.ld_sfq + row,
                                      __float_as_uint(scale));
                 }

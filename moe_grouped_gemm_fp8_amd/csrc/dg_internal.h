@@ -40,7 +40,7 @@ enum TileCfg : int {
     CFG_128x128w8d4 = 7, // 8 waves (2x4), wave tile 64x32, copies four K blocks ahead
     CFG_128x256w8 = 8,   // 8 waves (2x4), wave tile 64x64: contiguous MoE, two waves per SIMD
     CFG_256x128p = 9,    // CFG_256x128 with workgroups looping over tiles
-    CFG_256x256 = 10,    // 8 waves (4x2), wave tile 64x128, B copied one block ahead
+    CFG_256x256 = 10,    // 8 waves (4x2), wave tile 64x128, scales loaded into registers
     CFG_COUNT
 };
 

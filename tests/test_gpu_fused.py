@@ -79,7 +79,7 @@ def check_fused(p, q_dev, sfq_dev, d1=None, what=""):
     return q, sfq
 
 
-# 128 x 256 persistent tiles, and 256 x 256 tiles (B one block ahead), whose tiles can hold
+# 128 x 256 persistent tiles, and 256 x 256 tiles (scales in registers), whose tiles can hold
 # two groups: [0,130,41,300,129] -> 128-row blocks 1 1 | 2 3 | 3 3 | 4 4 (one straddle),
 # [41,0,300,1,130] -> 0 2 | 2 2 | 3 4 | 4 - (two, the last tile half past m_total); the second
 # group of a straddle on a workgroup of its own, or (DG_STRADDLE_ROWS=0) in the tile's own

@@ -309,11 +309,11 @@ def test_contiguous_256_row_tile_with_an_all_padding_half(cfg, monkeypatch):
     assert np.all(got[p.m_indices < 0] == W.BF16_SENTINEL), "padding rows were written"
 
 
-# 256 x 256 tiles copy B one block ahead and A two (the LDS holds no third B block): every
-# short K (one to five blocks, where the prologue and the loop's last blocks meet) and a
-# longer one, with straddles and a ragged N
+# 256 x 256 tiles load their scales into registers (the operands fill the LDS): every short K
+# (one to five blocks, where the prologue and the loop's last blocks meet) and a longer one,
+# with straddles and a ragged N
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640, 1152])
-def test_contiguous_b_one_block_ahead_k_sweep(k, monkeypatch):
+def test_contiguous_scales_in_registers_k_sweep(k, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
     p = W.make_contiguous(5, 600, 400, k, seed=38, counts=[0, 130, 41, 300, 129], stress=True,
                           pad_nan=True)
@@ -324,7 +324,7 @@ def test_contiguous_b_one_block_ahead_k_sweep(k, monkeypatch):
 
 
 @pytest.mark.parametrize("k", [128, 256, 384, 1152])
-def test_masked_b_one_block_ahead_k_sweep(k, monkeypatch):
+def test_masked_scales_in_registers_k_sweep(k, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
     p = W.make_masked(5, 256, 640, k, seed=42, masked_m=[0, 17, 128, 200, 256], tail_nan=True)
     ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
