@@ -10,14 +10,17 @@
 //  * The MFMA is issued as D^T = B_tile x A_tile^T (B fragment as the first operand).  A lane
 //    of the 16x16 result then holds four consecutive columns of ONE output row, so the A
 //    row-segment scale is a single per-lane float and promoting a partial into the FP32
-//    accumulators costs one multiply (sa * sb) plus four FMAs per MFMA.
+//    accumulators costs four FMAs per MFMA, plus the product sa * sb: once per row and block
+//    where a wave's columns lie in one 128-column scale block, else once per MFMA.
 //  * Every global read of the main loop (A, B, the A scales and the tile's B scales) is a
-//    gfx950 direct-to-LDS copy through a buffer resource: nothing in flight targets
-//    registers, so the only waits are explicit ones.  A has two LDS slots and B three, each
-//    a whole 128-deep K block, so block j+1's copies are in flight while block j is
-//    multiplied, with one barrier per K block.  A wave holds its A fragments for the whole
-//    block and reads B fragments two sub-tile steps ahead of the MFMAs that use them.
-//    Barriers are bare s_barrier (a release fence would wait for every copy in flight).
+//    gfx950 direct-to-LDS copy through a buffer resource, copied two K blocks ahead of its
+//    MFMAs; the waits for them are explicit counts.  B has three LDS slots and A two or three
+//    (each a whole 128-deep K block): with three, one barrier per K block, with two, a second
+//    one at the block's start.  The 256 x 256 tile's operands fill the LDS, so there each
+//    wave loads its scales into registers instead, one block ahead, from the L2.  A wave
+//    holds its A fragments for the whole block and reads B fragments two sub-tile steps ahead
+//    of the MFMAs that use them.  Barriers are bare s_barrier (a release fence would wait for
+//    every copy in flight).
 //  * Dense with C: during the last K blocks each wave loads C for one half of an accumulator
 //    column at a time (16-byte buffer loads into registers, hidden behind the MFMAs) and adds
 //    it in, so that most of C's HBM read overlaps the main loop; the epilogue adds the rest.
@@ -33,9 +36,13 @@
 //    the in-flight copies and drains them.
 //  * Workgroup ids are mapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
 //    runs a contiguous range of tiles, rastered in groups of 4 M-tiles, so tiles that run
-//    together on one XCD share A rows and B columns in that XCD's L2.  Most tile shapes run
-//    persistent workgroups (one per CU) that walk their XCD's range; the next tile's first K
-//    blocks are copied while the current tile finishes, hiding the per-tile prologue.
+//    together on one XCD share A rows and B columns in that XCD's L2.  The smaller tile shapes
+//    run persistent workgroups (one per CU) that walk their XCD's range; the next tile's
+//    first K blocks are copied while the current tile finishes, hiding the per-tile prologue.
+//    The 256-row tiles run one workgroup per tile.
+//  * The contiguous form can instead write the 1x128 FP8 cast of SwiGLU(gate, up) of its
+//    FP32 result (the activation between an MoE block's two expert GEMMs), its tiles holding
+//    the gate and up columns of one 128-column segment of the activation.
 //  * Contiguous form: a tile takes the group of its rows from the per-row group indices.  The
 //    groups are aligned to 128 rows, so a 256-row tile (one workgroup per tile) can hold the
 //    rows of two groups; it then runs twice, once with each group's B, and each pass stores
