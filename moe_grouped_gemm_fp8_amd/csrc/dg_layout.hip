@@ -21,9 +21,10 @@
 //    group whatever the groups' K extents (one range over all groups gave one XCD the largest
 //    group's tiles).
 //  * Per K block a tile needs 128 x BM bytes of A and 128 x BN bytes of B.  They are staged
-//    whole by direct-to-LDS buffer copies (1 KB per wave instruction), two blocks ahead, into
-//    three slots: block j+2 refills block j-1's slot, which every wave has left once it is
-//    past block j-1's end barrier, so one barrier per block suffices.
+//    whole by direct-to-LDS buffer copies (1 KB per wave instruction), three blocks ahead,
+//    into four slots: block j starts with a wait for block j + 1 and one barrier, after which
+//    block j + 3 refills block j - 1's slot (every wave has read it into registers by then),
+//    and block j + 1's fragments are read into a second register set during block j's MFMAs.
 //  * A K-major operand's LDS rows are its rows (128 bytes of K each), read as two
 //    ds_read_b128 per MFMA operand lane, as in the NT kernels.  An MN-major operand's LDS
 //    rows are K indices; ds_read_b64_tr_b8 gives a lane 8 consecutive K values of one column
@@ -130,7 +131,7 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     static_assert(SM % 2 == 0, "partials alternate between two register sets");
     constexpr int A_SLOT = KBLK * BM, B_SLOT = KBLK * BN;
     constexpr int S_SLOT = 1024;  // a block's BM (or BN) scales, 16 bytes per lane of one copy
-    constexpr int NS = 3;
+    constexpr int NS = 4;  // slots: block j in use, j + 1 landed, j + 2 and j + 3 in flight
     constexpr int B_BASE = NS * A_SLOT;
     constexpr int SA_BASE = B_BASE + NS * B_SLOT;
     constexpr int SB_BASE = SA_BASE + NS * S_SLOT;
@@ -139,7 +140,7 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     constexpr int IA = A_SLOT / 1024, IB = B_SLOT / 1024;  // 1 KB copies per block
     static_assert(IA % NW == 0 && IB % NW == 0, "copies must split evenly over the waves");
     constexpr int CA = IA / NW, CB = IB / NW, MAXI = CA + CB;
-    static_assert(2 * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
+    static_assert((NS - 1) * (MAXI + 2) < 64, "outstanding copies must fit vmcnt");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     DG_LDS uint8_t *ldsp = (DG_LDS uint8_t *)lds;
@@ -275,6 +276,13 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         else
             wait_vm<MAXI>();
     };
+    // (prologue: the first block's, with the next two in flight)
+    auto wait_first_block = [&]() {
+        if (wave == 0)
+            wait_vm<2 * (MAXI + 2)>();
+        else
+            wait_vm<2 * MAXI>();
+    };
 
     // ---- fragment offsets.  MN-major: lane (fr, fg), read r, addresses K row
     // 32 fg + 8 r + fr / 2 at byte 8 (fr & 1) of the sub-tile's chunk and receives K rows
@@ -310,15 +318,17 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     float fsa[2][SM];
     v4f fsb[2][KG ? SN : 1];  // K-grouped: the lane's four columns
     float fsb1[2];            // dense: the tile's B scale
-    auto read_frags = [&](auto BUF, int s) {
+    // a block's fragments from slot s into register set BUF: the A row sub-tile I (and its
+    // scales), or all of B (and its scales)
+    auto read_frags_a = [&](auto BUF, int s, auto I) {
+        constexpr int bf = decltype(BUF)::value, i = decltype(I)::value;
+        const uint32_t ao = (uint32_t)(s * A_SLOT), so = (uint32_t)(s * S_SLOT);
+        read_frag<A_MN, BM, i>(fa[bf][i], fa_lo[A_MN ? i : 0] + ao, fa_hi + ao);
+        fsa[bf][i] = lds_read4_at<i * 64>(sa_off + so);
+    };
+    auto read_frags_b = [&](auto BUF, int s) {
         constexpr int bf = decltype(BUF)::value;
-        const uint32_t ao = (uint32_t)(s * A_SLOT), bo = (uint32_t)(s * B_SLOT);
-        const uint32_t so = (uint32_t)(s * S_SLOT);
-        static_for<SM>([&](auto I) {
-            constexpr int i = decltype(I)::value;
-            read_frag<A_MN, BM, i>(fa[bf][i], fa_lo[A_MN ? i : 0] + ao, fa_hi + ao);
-            fsa[bf][i] = lds_read4_at<i * 64>(sa_off + so);
-        });
+        const uint32_t bo = (uint32_t)(s * B_SLOT), so = (uint32_t)(s * S_SLOT);
         static_for<SN>([&](auto J) {
             constexpr int jj = decltype(J)::value;
             read_frag<B_MN, BN, jj>(fb[bf][jj], fb_lo[B_MN ? jj : 0] + bo, fb_hi + bo);
@@ -327,6 +337,10 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         });
         if constexpr (!KG)
             fsb1[bf] = lds_read4_at<0>(sb_off + so);
+    };
+    auto read_frags = [&](auto BUF, int s) {
+        static_for<SM>([&](auto I) { read_frags_a(BUF, s, I); });
+        read_frags_b(BUF, s);
     };
     auto tie_frags = [&](auto BUF) {
         constexpr int bf = decltype(BUF)::value;
@@ -373,13 +387,24 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         }
     };
 
-    // block j of the tile's K run: its fragments are in register set BUF (maybe in flight)
+    // block j of the tile's K run: its fragments are in register set BUF (read during block
+    // j - 1); block j + 1's are read into the other set during this block's MFMAs, so the
+    // LDS reads overlap them, which needs block j + 1 landed at this block's start: the
+    // copies run three blocks ahead, into four slots
     auto do_block = [&](auto BUF, int j) {
         constexpr int bf = decltype(BUF)::value;
         constexpr auto OTHER = std::integral_constant<int, 1 - bf>{};
-        issue_block(j + 2, (j + 2) % NS);
+        // block j + 1 has landed everywhere, and every wave is done with block j - 1's slot,
+        // which takes block j + 3
+        wait_next_block();
+        bare_barrier();
+        issue_block(j + 3, (j + 3) % NS);
         lds_wait();
         tie_frags(BUF);
+        const bool more = j + 1 < nkb;
+        const int sn = (j + 1) % NS;
+        if (more)
+            read_frags_b(OTHER, sn);
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
             const v8i av = fa[bf][i].op();
@@ -389,19 +414,17 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
                     fb[bf][jj].op(), av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
             if constexpr (i > 0)
                 promote(BUF, std::integral_constant<int, i - 1>{});
+            if (more)
+                read_frags_a(OTHER, sn, I);
         });
-        // block j + 1 has landed everywhere, and every wave is done reading block j
-        wait_next_block();
-        bare_barrier();
-        if (j + 1 < nkb)
-            read_frags(OTHER, (j + 1) % NS);
         promote(BUF, std::integral_constant<int, SM - 1>{});
     };
 
     // ---- prologue and K loop
     issue_block(0, 0);
     issue_block(1, 1);
-    wait_next_block();
+    issue_block(2, 2);
+    wait_first_block();
     bare_barrier();
     constexpr auto B0 = std::integral_constant<int, 0>{};
     constexpr auto B1 = std::integral_constant<int, 1>{};
