@@ -41,12 +41,36 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the library's code with comments and whitespace removed, so that a counter
-    record stays valid across edits that cannot change the kernels."""
+# the library files each workload's kernels (and their host-side dispatch) are built from
+_COMMON_SOURCES = ("dg_api.cpp", "dg_device.h", "dg_internal.h", "dg_tiles.h")
+_GEMM = ("dg_gemm.hip",)
+WORKLOAD_SOURCES = {
+    "dense_small": ("dg_stream.hip",),
+    "dense_skinny": ("dg_stream.hip",),
+    "dense_skinny_ue8m0": ("dg_stream.hip",),
+    "dense_prefill": _GEMM,
+    "dense_prefill_ue8m0": _GEMM,
+    "dense_prefill_nn": _GEMM + ("dg_layout.hip",),
+    "dense_prefill_tn": _GEMM + ("dg_layout.hip",),
+    "dense_prefill_tt": _GEMM + ("dg_layout.hip",),
+    "moe_contiguous": _GEMM,
+    "moe_contiguous_ue8m0": _GEMM,
+    "moe_contiguous_swiglu": _GEMM,
+    "moe_masked": _GEMM,
+    "moe_masked_ue8m0": _GEMM,
+    "moe_block": _GEMM,
+    "moe_block_unfused": _GEMM + ("dg_quant.hip",),
+    "moe_wgrad": ("dg_layout.hip",),
+    "moe_swiglu_quant": ("dg_quant.hip",),
+}
+
+
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the code of the library files that the workload's kernels are built from, with
+    comments and whitespace removed, so that a counter record stays valid across edits that
+    cannot change those kernels."""
     h = hashlib.sha256()
-    for f in ("dg_gemm.hip", "dg_stream.hip", "dg_layout.hip", "dg_quant.hip", "dg_api.cpp",
-              "dg_device.h", "dg_internal.h", "dg_tiles.h"):
+    for f in WORKLOAD_SOURCES[workload] + _COMMON_SOURCES:
         with open(os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"//[^\n]*|/\*.*?\*/", " ", src, flags=re.S)
@@ -62,7 +86,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
