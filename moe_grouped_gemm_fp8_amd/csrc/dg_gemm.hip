@@ -17,7 +17,9 @@
 //    MFMAs; the waits for them are explicit counts.  B has three LDS slots and A two or three
 //    (each a whole 128-deep K block): with three, one barrier per K block, with two, a second
 //    one at the block's start.  The 256 x 256 tile's operands fill the LDS, so there each
-//    wave loads its scales into registers instead, one block ahead, from the L2.  A wave
+//    wave loads its scales into registers instead, one block ahead, from the L2: two loads
+//    per wave (one A scale per lane of its 64 rows, the two B scales), spread to the lanes
+//    that use them by the gfx950 32- and 16-lane swaps and readlane.  A wave
 //    holds its A fragments for the whole block and reads B fragments two sub-tile steps ahead
 //    of the MFMAs that use them.  Barriers are bare s_barrier (a release fence would wait for
 //    every copy in flight).
@@ -158,8 +160,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     //
     // Where the scale areas do not fit next to DEPTH A and DEPTH + 1 B slots (256 x 256 tiles:
     // 160 KB of operands alone), the scales go to registers instead (SREG): each wave loads
-    // its rows' A scales and its B scales for block j + 1 at block j's start, from the L2, and
-    // takes them at block j's end.
+    // its 64 rows' A scales (one per lane) and its two B scales for block j + 1 at block j's
+    // start, from the L2, and takes them at block j's end.
     static_assert(DEPTH >= 2, "at least one block of look-ahead beyond the next");
     constexpr int A_SLOT = BM * KBLK;
     constexpr int B_SLOT = BN * KBLK;
@@ -173,6 +175,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         DEPTH * (A_SLOT + SCL) + (DEPTH + 1) * B_SLOT + AMX_OWN > 160 * 1024;
     static_assert(!SREG || (!PERSIST && DEPTH * A_SLOT + (DEPTH + 1) * B_SLOT <= 160 * 1024),
                   "scales in registers: one tile per workgroup, operands within the LDS");
+    static_assert(!SREG || TM == 64, "scales in registers: one A scale per lane of a 64-row band");
     constexpr int SCL_LDS = SREG ? 0 : SCL;
     constexpr bool ONE_BAR =
         (DEPTH + 1) * (A_SLOT + SCL_LDS + B_SLOT) + AMX_OWN <= 160 * 1024;
@@ -471,13 +474,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     };
     // wait until the next block's copies have landed (those of the DEPTH - 1 blocks after it
     // may still be in flight).  SREG: no scale copies; inside the K loop each block's register
-    // loads of the next block's scales, SM + 2 per wave, precede its copies and may still be
-    // in flight too (their own wait comes at the block's last step).
+    // loads of the next block's scales, two per wave, precede its copies and may still be in
+    // flight too (their own wait comes at the block's last step).
     auto wait_older_copies = [&](bool in_loop) {
         constexpr int LATER = (DEPTH - 1) * MAXI;
         if constexpr (SREG) {
             if (in_loop)
-                wait_vm<LATER + (DEPTH - 1) * (SM + 2)>();
+                wait_vm<LATER + (DEPTH - 1) * 2>();
             else
                 wait_vm<LATER>();
         } else if (wave == 0) {
@@ -556,30 +559,26 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         return s;
     };
     float vsb_lo, vsb_hi;  // this block's two B scales (all lanes equal)
-    // SREG: the next block's scales, loaded into registers at the current block's start: this
-    // lane's rows' A scales and the wave's two B scales (the offsets of the LDS form's lanes
+    // SREG: the next block's scales, loaded into registers at the current block's start, two
+    // loads per wave: lane l the A scale of the wave's row wm + l, and the wave's two B scales,
+    // lo in the even lanes and hi in the odd ones (the offsets of the LDS form's lanes
     // sel.lo / 4 and sel.hi / 4 in the B-scale copy)
-    float Sn[SM], vbn_lo, vbn_hi;
+    float Sn, vbn;
+    uint32_t sw_b, sw_hold;  // (lane moves of the A scales, during a block's last step)
     auto load_scales = [&](int kb, const CopySrc &s, const ScaleSel &sl) {
         const int ks = UE8 ? kb >> 2 : kb;  // the scale column holding block kb
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-            Sn[i] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(
-                           s.sa, (uint32_t)(((int64_t)ks * ld + wm + 16 * i + fr) * 4), 0, 0));
+        Sn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           s.sa, (uint32_t)(((int64_t)ks * ld + wm + lane) * 4), 0, 0));
         const uint32_t blo = SWIGLU ? 0u : sl.lo * (uint32_t)KS;
         const uint32_t bhi = SWIGLU ? (uint32_t)(N >> 8) * (uint32_t)KS * 4u : sl.hi * (uint32_t)KS;
-        vbn_lo = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(s.sb, blo + (uint32_t)ks * 4u, 0, 0));
-        vbn_hi = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(s.sb, bhi + (uint32_t)ks * 4u, 0, 0));
+        vbn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            s.sb, ((lane & 1) ? bhi : blo) + (uint32_t)ks * 4u, 0, 0));
     };
     auto read_sfb = [&](int aslot, const ScaleSel &s) {
         if constexpr (SREG) {
-            tie(vbn_lo);
-            tie(vbn_hi);
-            vsb_lo = vbn_lo;
-            vsb_hi = vbn_hi;
+            tie(vbn);
+            vsb_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vbn), 0));
+            vsb_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vbn), 1));
         } else {
             vsb_lo = lds_read4(lds_base + SB_BASE + s.lo + (uint32_t)(aslot * 256));
             vsb_hi = lds_read4(lds_base + SB_BASE + s.hi + (uint32_t)(aslot * 256));
@@ -682,9 +681,25 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if constexpr (SREG) {
             // loaded at the block's start; the use here makes the compiler's own wait for
             // them fall inside this block (counting this block's copies after them), not at
-            // the next block's start, where it cannot count across the loop and waits for all
-            tie(Sn[i]);
-            Sf[i] = Sn[i];
+            // the next block's start, where it cannot count across the loop and waits for all.
+            // Row wm + 16 i + fr's scale is in lane 16 i + fr: the 32- and 16-lane swaps give
+            // every lane the rows of lane group i (groups 0, 1 from the lower halves, 2, 3 from
+            // the upper), a sub-tile's value taken when its MFMAs no longer need the old one.
+            if constexpr (i == 0) {
+                tie(Sn);
+                const uint32_t v = __builtin_bit_cast(uint32_t, Sn);
+                const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+                const auto g = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+                sw_b = h[1];
+                Sf[0] = __builtin_bit_cast(float, g[0]);
+                sw_hold = g[1];
+            } else if constexpr (i == 2) {
+                const auto g = __builtin_amdgcn_permlane16_swap(sw_b, sw_b, false, false);
+                Sf[2] = __builtin_bit_cast(float, g[0]);
+                sw_hold = g[1];
+            } else {
+                Sf[i] = __builtin_bit_cast(float, sw_hold);
+            }
         } else
             Sf[i] = lds_read4_at<i * 64>(sa);
     };
