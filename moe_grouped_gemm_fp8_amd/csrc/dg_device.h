@@ -186,6 +186,11 @@ __device__ __forceinline__ int raster_index(int tm, int tn, int tiles_m, int til
     return first * tiles_n + tn * gsz + (tm - first);
 }
 
+// Cache-policy operand of a buffer load (gfx950): non-temporal, for data read once (a B
+// panel that only one tile reads, a skinny GEMM's B), so that it does not push reused lines
+// out of the caches.
+constexpr int CP_NT = 2;
+
 // 128-bit buffer resource for raw (unstrided) loads of `bytes` bytes from `base`: any lane
 // whose offset falls outside the range reads zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)

@@ -117,9 +117,10 @@ __global__ __launch_bounds__(64 * ST_WAVES) void dg_stream_kernel(GemmArgs p, in
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (DG_LDS void *)(ldsp + kb * A_SLOT + wave * 1024), 16, vo,
                 (uint32_t)(kb0 + kb) * KBLK, 0, 0);
+            // (B is read once: non-temporal)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (DG_LDS void *)(ldsp + B_BASE + kb * B_SLOT + wave * 1024), 16, vo,
-                (uint32_t)(kb0 + kb) * KBLK, 0, 0);
+                (uint32_t)(kb0 + kb) * KBLK, 0, CP_NT);
         }
     }
 
@@ -234,13 +235,17 @@ __global__ __launch_bounds__(64 * ST_WAVES) void dg_stream_kernel(GemmArgs p, in
         return;
     }
 
-    // ---- several splits: publish this split's partial tile (the reduce kernel finishes it)
+    // ---- several splits: publish this split's partial tile (the reduce kernel finishes it).
+    // Partials are written once and read once, by another workgroup on any XCD: non-temporal
+    // stores and loads (with both, the 64 x 2112 x 7168 step took 11.3 us against 12.1 us;
+    // non-temporal loads alone changed nothing)
     if (kh == 0) {
         float *ws_tile =
             p.ws + ((int64_t)(tm * tiles_n + tn) * p.splits + split) * (ST_BM * ST_BN);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<v4f *>(ws_tile + (i * 256 + cs * 64 + lane) * 4) = acc[i];
+            __builtin_nontemporal_store(acc[i],
+                                        reinterpret_cast<v4f *>(ws_tile + (i * 256 + cs * 64 + lane) * 4));
     }
 }
 
@@ -263,7 +268,8 @@ __global__ __launch_bounds__(256) void dg_stream_reduce_kernel(GemmArgs p, int t
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             if (s0 + u < p.splits)
-                part[u] = *reinterpret_cast<const v4f *>(src + (int64_t)(s0 + u) * ST_BM * ST_BN);
+                part[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4f *>(src + (int64_t)(s0 + u) * ST_BM * ST_BN));
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             if (s0 + u < p.splits)
