@@ -520,8 +520,8 @@ hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 // K-major, which the NT kernels take.  rows % 64 == 0 and cols % 16 == 0.  A workgroup moves
 // one 64 x 64 byte tile: 16-byte loads into a padded LDS tile (80-byte rows), then
 // ds_read_b64_tr_b8, whose 16-lane groups turn an 8 x 16 byte block into 16 lanes of 8
-// consecutive row bytes; wave w writes output rows 16 w .. 16 w + 15, 32 consecutive bytes
-// of each per instruction.
+// consecutive row bytes; two such reads give a lane 16 bytes, and wave w writes output rows
+// 16 w .. 16 w + 15, their whole 64 bytes, in one 16-byte store per lane.
 // One launch moves up to two operands (A and B of the TN layout): workgroups [0, p0.tiles)
 // transpose p0, the rest p1.
 struct U8Transpose {
@@ -552,19 +552,18 @@ __global__ __launch_bounds__(256) void dg_transpose_u8_kernel(U8Transpose p0, U8
     __syncthreads();
     const uint32_t base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)tile;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int inst = 0; inst < 2; ++inst) {
-        const int b = g + 4 * inst;  // K rows 8 b .. 8 b + 7 of the tile
-        const uint32_t addr =
-            base + (uint32_t)((8 * b + (j >> 1)) * PITCH + 16 * w + 8 * (j & 1));
-        v2i v = lds_read_tr8_at<0>(addr);
-        lds_wait();
-        tie(v);
-        const int c = c0 + 16 * w + j;  // output row
-        if (c < cols)
-            *reinterpret_cast<uint2 *>(y + (int64_t)c * rows + r0 + 8 * b) =
-                make_uint2((uint32_t)v.x, (uint32_t)v.y);
-    }
+    // lane group g: tile rows 16 g .. 16 g + 15 (two transposing reads of 8 rows), so lane j
+    // holds 16 consecutive bytes of output row c0 + 16 w + j
+    const uint32_t addr = base + (uint32_t)((16 * g + (j >> 1)) * PITCH + 16 * w + 8 * (j & 1));
+    v2i lo = lds_read_tr8_at<0>(addr);
+    v2i hi = lds_read_tr8_at<8 * PITCH>(addr);
+    lds_wait();
+    tie(lo);
+    tie(hi);
+    const int c = c0 + 16 * w + j;  // output row
+    if (c < cols)
+        *reinterpret_cast<uint4 *>(y + (int64_t)c * rows + r0 + 16 * g) =
+            make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y);
 }
 
 hipError_t launch_transpose_u8(const void *x0, void *y0, int rows0, int cols0, const void *x1,
