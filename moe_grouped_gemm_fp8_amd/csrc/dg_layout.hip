@@ -15,16 +15,21 @@
 // K-major, and use this template under graph capture before their workspace exists).
 //
 // Design:
-//  * One workgroup per 128 x 128 tile (of one group); eight waves (2 x 4), wave tile 64 x 32.
-//    Dense tiles go to the XCDs in 8 raster-order chunks (neighbours share A and B panels in
-//    an XCD's L2); K-grouped tiles go round-robin, so each XCD gets an equal share of every
-//    group whatever the groups' K extents (one range over all groups gave one XCD the largest
-//    group's tiles).
+//  * One workgroup per tile (of one group); eight waves (2 x 4).  Dense tiles are 128 x 128
+//    (wave tile 64 x 32); K-grouped tiles 128 x 256 (wave tile 64 x 64: per MFMA, three
+//    quarters of the copies and two thirds of the fragment reads of the 128 x 128 tile; the
+//    weight gradient of the routed 8-expert shape 1518 us against 1812 us).  Dense tiles go to
+//    the XCDs in 8 raster-order chunks (neighbours share A and B panels in an XCD's L2);
+//    K-grouped tiles go round-robin, so each XCD gets an equal share of every group whatever
+//    the groups' K extents (one range over all groups gave one XCD the largest group's tiles).
 //  * Per K block a tile needs 128 x BM bytes of A and 128 x BN bytes of B.  They are staged
-//    whole by direct-to-LDS buffer copies (1 KB per wave instruction), three blocks ahead,
-//    into four slots: block j starts with a wait for block j + 1 and one barrier, after which
-//    block j + 3 refills block j - 1's slot (every wave has read it into registers by then),
-//    and block j + 1's fragments are read into a second register set during block j's MFMAs.
+//    whole by direct-to-LDS buffer copies (1 KB per wave instruction) into NS slots, NS - 1
+//    blocks ahead: block j starts with a wait for block j + 1 and one barrier, after which
+//    block j + NS - 1 refills block j - 1's slot (every wave has read it into registers by
+//    then).  Four slots where they fit (128 x 128), three for 128 x 256, whose blocks take
+//    twice as long.  Block j + 1's A fragments are read into a second register set during
+//    block j's MFMAs; so are its B fragments on 128 x 128 tiles, while the wider tile (one B
+//    register set, to fit 256 VGPRs) reads them after block j's last MFMAs and promotions.
 //  * A K-major operand's LDS rows are its rows (128 bytes of K each), read as two
 //    ds_read_b128 per MFMA operand lane, as in the NT kernels.  An MN-major operand's LDS
 //    rows are K indices; ds_read_b64_tr_b8 gives a lane 8 consecutive K values of one column
@@ -39,6 +44,7 @@
 //    writes C, or zeros.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "dg_device.h"
 #include "dg_internal.h"
@@ -131,7 +137,9 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     static_assert(SM % 2 == 0, "partials alternate between two register sets");
     constexpr int A_SLOT = KBLK * BM, B_SLOT = KBLK * BN;
     constexpr int S_SLOT = 1024;  // a block's BM (or BN) scales, 16 bytes per lane of one copy
-    constexpr int NS = 4;  // slots: block j in use, j + 1 landed, j + 2 and j + 3 in flight
+    // slots: block j in use, j + 1 landed, the rest in flight (four where they fit, else three;
+    // a three-slot tile is twice as wide, so one block ahead covers as much time)
+    constexpr int NS = 4 * (KBLK * (BM + BN) + 2 * 1024) <= 160 * 1024 ? 4 : 3;
     constexpr int B_BASE = NS * A_SLOT;
     constexpr int SA_BASE = B_BASE + NS * B_SLOT;
     constexpr int SB_BASE = SA_BASE + NS * S_SLOT;
@@ -272,16 +280,16 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     // the next block's copies have landed (only those of the block after it may be in flight)
     auto wait_next_block = [&]() {
         if (wave == 0)
-            wait_vm<MAXI + 2>();
+            wait_vm<(NS - 3) * (MAXI + 2)>();
         else
-            wait_vm<MAXI>();
+            wait_vm<(NS - 3) * MAXI>();
     };
     // (prologue: the first block's, with the next two in flight)
     auto wait_first_block = [&]() {
         if (wave == 0)
-            wait_vm<2 * (MAXI + 2)>();
+            wait_vm<(NS - 2) * (MAXI + 2)>();
         else
-            wait_vm<2 * MAXI>();
+            wait_vm<(NS - 2) * MAXI>();
     };
 
     // ---- fragment offsets.  MN-major: lane (fr, fg), read r, addresses K row
@@ -313,10 +321,15 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
     const uint32_t sa_off = lds_base + SA_BASE + (uint32_t)(wm + fr) * 4;
     const uint32_t sb_off = lds_base + SB_BASE + (KG ? (uint32_t)(wn + 4 * fg) * 4 : 0u);
 
+    // Wide tiles (SN >= 4) hold one set of B fragments and scales: the next block's are read
+    // after the current block's last MFMA and promotion that use them (registers); narrower
+    // ones read the next block's B into a second set during the current block's MFMAs.
+    constexpr bool ONE_B = SN >= 4;
+    constexpr int NBB = ONE_B ? 1 : 2;
     Frag<A_MN> fa[2][SM];
-    Frag<B_MN> fb[2][SN];
+    Frag<B_MN> fb[NBB][SN];
     float fsa[2][SM];
-    v4f fsb[2][KG ? SN : 1];  // K-grouped: the lane's four columns
+    v4f fsb[NBB][KG ? SN : 1];  // K-grouped: the lane's four columns
     float fsb1[2];            // dense: the tile's B scale
     // a block's fragments from slot s into register set BUF: the A row sub-tile I (and its
     // scales), or all of B (and its scales)
@@ -327,7 +340,7 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         fsa[bf][i] = lds_read4_at<i * 64>(sa_off + so);
     };
     auto read_frags_b = [&](auto BUF, int s) {
-        constexpr int bf = decltype(BUF)::value;
+        constexpr int bf = ONE_B ? 0 : decltype(BUF)::value;
         const uint32_t bo = (uint32_t)(s * B_SLOT), so = (uint32_t)(s * S_SLOT);
         static_for<SN>([&](auto J) {
             constexpr int jj = decltype(J)::value;
@@ -336,14 +349,14 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
                 fsb[bf][jj] = lds_read16f_at<jj * 64>(sb_off + so);
         });
         if constexpr (!KG)
-            fsb1[bf] = lds_read4_at<0>(sb_off + so);
+            fsb1[decltype(BUF)::value] = lds_read4_at<0>(sb_off + so);
     };
     auto read_frags = [&](auto BUF, int s) {
         static_for<SM>([&](auto I) { read_frags_a(BUF, s, I); });
         read_frags_b(BUF, s);
     };
     auto tie_frags = [&](auto BUF) {
-        constexpr int bf = decltype(BUF)::value;
+        constexpr int bf = decltype(BUF)::value, bb = ONE_B ? 0 : bf;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
             fa[bf][i].tie_all();
@@ -351,11 +364,11 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         }
 #pragma unroll
         for (int jj = 0; jj < SN; ++jj)
-            fb[bf][jj].tie_all();
+            fb[bb][jj].tie_all();
         if constexpr (KG) {
 #pragma unroll
             for (int jj = 0; jj < SN; ++jj)
-                tie(fsb[bf][jj]);
+                tie(fsb[bb][jj]);
         } else {
             tie(fsb1[bf]);
         }
@@ -374,7 +387,7 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         if constexpr (KG) {
 #pragma unroll
             for (int jj = 0; jj < SN; ++jj) {
-                acc[i][jj] += pend[i % 2][jj] * (fsa[bf][i] * fsb[bf][jj]);
+                acc[i][jj] += pend[i % 2][jj] * (fsa[bf][i] * fsb[ONE_B ? 0 : bf][jj]);
                 asm volatile("" : "+v"(acc[i][jj]));
             }
         } else {
@@ -398,32 +411,39 @@ __device__ __forceinline__ void layout_tile(const LayoutArgs &p, int tiles_m, in
         // which takes block j + 3
         wait_next_block();
         bare_barrier();
-        issue_block(j + 3, (j + 3) % NS);
+        issue_block(j + NS - 1, (j + NS - 1) % NS);
         lds_wait();
         tie_frags(BUF);
         const bool more = j + 1 < nkb;
         const int sn = (j + 1) % NS;
-        if (more)
-            read_frags_b(OTHER, sn);
+        if constexpr (!ONE_B) {
+            if (more)
+                read_frags_b(OTHER, sn);
+        }
         static_for<SM>([&](auto I) {
             constexpr int i = decltype(I)::value;
             const v8i av = fa[bf][i].op();
 #pragma unroll
             for (int jj = 0; jj < SN; ++jj)
                 pend[i % 2][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fb[bf][jj].op(), av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    fb[ONE_B ? 0 : bf][jj].op(), av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
             if constexpr (i > 0)
                 promote(BUF, std::integral_constant<int, i - 1>{});
             if (more)
                 read_frags_a(OTHER, sn, I);
         });
         promote(BUF, std::integral_constant<int, SM - 1>{});
+        // one B set: the next block's B once this block's last MFMAs and promotions are issued
+        if constexpr (ONE_B) {
+            if (more)
+                read_frags_b(OTHER, sn);
+        }
     };
 
     // ---- prologue and K loop
-    issue_block(0, 0);
-    issue_block(1, 1);
-    issue_block(2, 2);
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d)
+        issue_block(d, d);
     wait_first_block();
     bare_barrier();
     constexpr auto B0 = std::integral_constant<int, 0>{};
@@ -469,11 +489,21 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_layout_kernel(LayoutArgs p, i
 
 namespace {
 constexpr int LY_BM = 128, LY_BN = 128, LY_WM = 2, LY_WN = 4;
+// K-grouped tiles are 128 x 256 (B in one register set; three slots): 256 columns per tile
+// halve the copies and LDS reads per MFMA of the 128 x 128 tile.  DG_KG_TILE_N=128 selects
+// the narrower tile (tests).
+int kg_tile_n()
+{
+    const char *e = getenv("DG_KG_TILE_N");
+    return (e && atoi(e) == 128) ? 128 : 256;
 }
+int tile_n(int layout) { return layout == LAYOUT_KGROUPED_TN ? kg_tile_n() : LY_BN; }
+}  // namespace
 
 int64_t layout_grid_size(int layout, const LayoutArgs &a)
 {
-    const int64_t tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
+    const int bn = tile_n(layout);
+    const int64_t tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + bn - 1) / bn;
     const int64_t per_g = tiles_m * tiles_n;
     if (layout == LAYOUT_KGROUPED_TN)
         return per_g * a.num_groups;  // one workgroup per tile of every group
@@ -484,7 +514,8 @@ int64_t layout_grid_size(int layout, const LayoutArgs &a)
 
 hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 {
-    const int tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + LY_BN - 1) / LY_BN;
+    const int bn = tile_n(layout);
+    const int tiles_m = (a.m + LY_BM - 1) / LY_BM, tiles_n = (a.n + bn - 1) / bn;
     const int64_t grid = layout_grid_size(layout, a);
     if (grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
@@ -494,7 +525,11 @@ hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
                        stream, a, tiles_m, tiles_n)
     switch (layout) {
     case LAYOUT_KGROUPED_TN:
-        DG_LAUNCH_LAYOUT(true, true, true);
+        if (bn == 256)
+            hipLaunchKernelGGL((dg_layout_kernel<LY_BM, 256, LY_WM, LY_WN, true, true, true>), g, b,
+                               0, stream, a, tiles_m, tiles_n);
+        else
+            DG_LAUNCH_LAYOUT(true, true, true);
         break;
     case LAYOUT_NN:
         DG_LAUNCH_LAYOUT(false, true, false);

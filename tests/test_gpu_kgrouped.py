@@ -73,6 +73,15 @@ def test_block_counts_around_the_pipeline_depth(blocks):
     check(run(p), oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c), f"{blocks} blocks")
 
 
+@pytest.mark.parametrize("blocks", [1, 3, 4])
+def test_narrow_tiles(blocks, monkeypatch):
+    # the 128 x 128 tile (four slots, two B register sets), which DG_KG_TILE_N=128 selects
+    monkeypatch.setenv("DG_KG_TILE_N", "128")
+    p = W.make_k_grouped(3, 128 * blocks + 200, 208, 336, seed=90 + blocks,
+                         counts=[128 * blocks, 0, 200], stress=True, with_c=True)
+    check(run(p), oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c), f"narrow {blocks}")
+
+
 def test_all_groups_empty_writes_c_or_zero():
     p = W.make_k_grouped(3, 0, 64, 48, seed=85, counts=[0, 0, 0], with_c=True)
     assert p.k_total == 0
