@@ -160,7 +160,7 @@ int forced_splits()
 }
 
 void print_config(const char *what, int m, int n, int k, int g, int cfg, int splits,
-                  int expected_m = -1)
+                  int expected_m = -1, int tail = 0)
 {
     static std::mutex mu;
     static std::set<std::tuple<std::string, int, int, int, int, int>> seen;
@@ -173,9 +173,13 @@ void print_config(const char *what, int m, int n, int k, int g, int cfg, int spl
     char hint[32] = "";
     if (expected_m >= 0)
         snprintf(hint, sizeof(hint), " expected_m=%d", expected_m);
-    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d%s -> tile %s (%dx%d), splits=%d\n", what,
+    char tl[64] = "";
+    if (tail > 0)
+        snprintf(tl, sizeof(tl), ", tail up to %d tiles as %s", tail,
+                 dg::kTiles[dg::CFG_128x128w8d4].name);
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d%s -> tile %s (%dx%d), splits=%d%s\n", what,
             m, n, k, g, hint, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn,
-            splits);
+            splits, tl);
 }
 
 // Estimated cost of a tile choice: waves of workgroups over the CUs times the work of one
@@ -455,8 +459,42 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
         if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
             args.straddle_rows = atoi(e);
     }
-    print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1);
-    return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
+    // The tail launch.  256 x 256 tiles run one workgroup each, and the last ones dispatched
+    // can form a last partial wave that leaves most CUs idle.  Where that wave could hold
+    // between an eighth and a quarter of the CUs' worth of busy workgroups (for some count of
+    // served straddles; the kernels count the actual ones from the group indices), a second
+    // launch of 128 x 128 tiles follows and runs the tiles of those workgroups over four times
+    // as many CUs.  DG_TAIL_TILES=n (tests) leaves n tiles to it whatever the wave, 0 never.
+    int tail_max = 0;
+    if (cfg == dg::CFG_256x256) {
+        const char *e = getenv("DG_TAIL_TILES");
+        const int force = (e && *e) ? atoi(e) : -1;
+        const int tm = (m_total + 255) / 256, tn = (n + 255) / 256;
+        const int64_t tiles = (int64_t)tm * tn;
+        if (force > 0) {
+            tail_max = (int)(force < tiles - 1 ? force : tiles - 1);
+            args.tail_force = force;
+        } else if (force < 0) {
+            for (int s = 0; s <= args.straddle_rows && tail_max == 0; ++s) {
+                const int64_t r = (tiles + (int64_t)s * tn) % cus;
+                if (8 * r >= cus && 4 * r <= cus && r < tiles)
+                    tail_max = cus / 4;
+            }
+        }
+        if (tail_max > 0) {
+            args.tail_cus = cus;
+            args.tail_tm = tm;
+            args.tail_tn = tn;
+            args.tail_max = tail_max;
+        } else {
+            args.tail_force = 0;
+        }
+    }
+    print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1, -1, tail_max);
+    rc = launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
+    if (rc != DG_OK || tail_max == 0)
+        return rc;
+    return launch(dg::MODE_CONTIG, dg::CFG_128x128w8d4, args, (hipStream_t)stream);
 }
 
 // The contiguous form with the activation step fused into the epilogue: B is [G, 2I, K] with

@@ -41,7 +41,9 @@
 //    together on one XCD share A rows and B columns in that XCD's L2.  The smaller tile shapes
 //    run persistent workgroups (one per CU) that walk their XCD's range; the next tile's
 //    first K blocks are copied while the current tile finishes, hiding the per-tile prologue.
-//    The 256-row tiles run one workgroup per tile.
+//    The 256-row tiles run one workgroup per tile.  The contiguous form's 256 x 256 launch can
+//    leave the tiles of its last-dispatched workgroups (a last partial wave) to a second launch
+//    of 128 x 128 tiles, which spreads them over four times as many CUs.
 //  * The contiguous form can instead write the 1x128 FP8 cast of SwiGLU(gate, up) of its
 //    FP32 result (the activation between an MoE block's two expert GEMMs), its tiles holding
 //    the gate and up columns of one 128-column segment of the activation.
@@ -250,35 +252,83 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // serve the first straddle_rows of them, one per N tile, and a tile's own workgroup runs
     // the second pass itself only for a straddle not served so (a straddle the first rows do
     // not show, or one past straddle_rows).  Both sides decide from the same loads.
-    const int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
+    //
+    // Tail launch (tail_cus > 0): the last workgroups of a launch of 256 x 256 tiles are
+    // dispatched last, one per XCD in turn, and where they form a last partial wave of whole
+    // tiles the launch ends with most CUs idle.  The workgroups of the last tail_tiles() ids
+    // then leave their tiles to a second launch of 128 x 128 tiles (TAIL below), which runs
+    // them over four times as many CUs; the straddle workgroups skip them too, since a
+    // 128-row tile holds one group.  Both launches count the same served straddles.
+    constexpr bool TAIL = CONTIG && !SWIGLU && PERSIST && BM == 128 && BN == 128;
+    constexpr int SUB = (256 / BM) * (256 / BN);  // TAIL: 128 x 128 tiles per 256 x 256 tile
+    int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
     const int E = TWO_GROUPS ? ((p.straddle_rows * tiles_n + 7) & ~7) : 0;
     const int bid = (int)blockIdx.x - E;  // < 0: a workgroup serving a listed straddle
     int tile_id, tile_end, tile_step;
-    // listed straddles among tile-rows 64 c + lane (c < 4; the host lists them only while
-    // tiles_m <= 256), and the groups of tile-row t's two block-leading rows
+    // listed straddles among 256-row tile-rows 64 c + lane (c < 4; the host lists them only
+    // while there are at most 256), and the groups of tile-row t's two block-leading rows
     auto leaders = [&](int t, int &la, int &lb) {
-        const int r0 = t * BM;
+        const int r0 = t * 256;
         la = p.grp[r0];
         lb = r0 + 128 < M ? p.grp[r0 + 128] : -1;
         la = (la >= 0 && la < p.num_groups) ? la : -1;
         lb = (lb >= 0 && lb < p.num_groups) ? lb : -1;
     };
     uint64_t listed[4];
-    auto scan_listed = [&]() {
+    auto scan_listed = [&](int rows256) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int t = 64 * c + lane;
             int la = -1, lb = -1;
-            if (t < tiles_m)
+            if (t < rows256)
                 leaders(t, la, lb);
             listed[c] = __ballot(la >= 0 && lb >= 0 && la != lb);
         }
     };
+    // tiles of a launch of `tiles` 256 x 256 tiles (tn256 across) left to the tail launch: the
+    // busy workgroups of its last partial wave over tail_cus CUs (every tile, and one workgroup
+    // per N tile for each served straddle) when they are between tail_cus / 8 and
+    // tail_cus / 4, else none; tail_force of them if set.  Needs scan_listed first where
+    // straddle_rows > 0.
+    auto tail_tiles = [&](int tiles, int tn256) {
+        if (p.tail_force > 0)
+            return min(p.tail_force, tiles - 1);
+        int served = 0;
+        if (p.straddle_rows > 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                served += __builtin_popcountll(listed[c]);
+            served = min(served, p.straddle_rows);
+        }
+        const int r = (tiles + served * tn256) % p.tail_cus;
+        return (8 * r >= p.tail_cus && 4 * r <= p.tail_cus && r < tiles) ? r : 0;
+    };
+    int tail_n = 0;  // TAIL: the 256 x 256 tiles this launch covers
+    if constexpr (TAIL) {
+        if (p.tail_cus > 0) {
+            if (p.straddle_rows > 0)
+                scan_listed(p.tail_tm);
+            tail_n = __builtin_amdgcn_readfirstlane(tail_tiles(p.tail_tm * p.tail_tn, p.tail_tn));
+            total = SUB * tail_n;
+            if (total == 0)
+                return;
+        }
+    }
+    if (TWO_GROUPS && p.tail_cus > 0 && bid >= 0) {
+        // (only the last workgroups can be left to the tail launch)
+        const int cap = p.tail_force > 0 ? total : p.tail_cus / 4;
+        if (bid >= total - cap) {
+            if (p.straddle_rows > 0)
+                scan_listed(tiles_m);
+            if (bid >= total - tail_tiles(total, tiles_n))
+                return;
+        }
+    }
     if (TWO_GROUPS && bid < 0) {
         const int b = (int)blockIdx.x / tiles_n, tn = (int)blockIdx.x - b * tiles_n;
         if (b >= p.straddle_rows)
             return;  // (E is rounded up to whole XCD rounds)
-        scan_listed();
+        scan_listed(tiles_m);
         int t = -1, left = b;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -294,6 +344,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if (t < 0)
             return;  // fewer listed straddles than served slots
         tile_id = raster_index(t, tn, tiles_m, tiles_n);
+        if (p.tail_cus > 0) {
+            // a tile left to the tail launch (its own workgroup is among the last ids)
+            const int left = tail_tiles(total, tiles_n);
+            if (left > 0 && xcd_tile_owner(total, E, tile_id) - E >= total - left)
+                return;
+        }
         tile_end = tile_id + 1;
         tile_step = 1;
     } else {
@@ -329,7 +385,21 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             tn = rem / tiles_m;
             tm = rem - tn * tiles_m;
         } else {
-            raster(t, tiles_m, tiles_n, tm, tn);
+            if (TAIL && tail_n > 0) {
+                // 128 x 128 tile q of the 256 x 256 tile of the launch's workgroup
+                // tiles - tail_n + u (the 256-row launch's own mapping)
+                const int u = t / SUB, q = t - u * SUB;
+                const int tiles = p.tail_tm * p.tail_tn;
+                const int lead = (p.straddle_rows * p.tail_tn + 7) & ~7;
+                const int big =
+                    xcd_tile_range(tiles, lead + tiles, lead, lead + tiles - tail_n + u).first;
+                int bm, bn;
+                raster(big, p.tail_tm, p.tail_tn, bm, bn);
+                tm = bm * (256 / BM) + q / (256 / BN);
+                tn = bn * (256 / BN) + q % (256 / BN);
+            } else {
+                raster(t, tiles_m, tiles_n, tm, tn);
+            }
             g = 0;
         }
     };
@@ -351,16 +421,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if constexpr (MODE == MODE_MASKED) {
             raw_cnt = p.grp[u.g];
         } else if constexpr (CONTIG) {
-            // (rows past M: only a tile taller than the 128-row alignment reaches them)
+            // (rows past M: only a tile taller than the 128-row alignment, or a tail launch's
+            // tile in the second half of a 256-row tile that ends past M, reaches them)
+            constexpr bool PAST_M = TWO_GROUPS || TAIL;
 #pragma unroll
             for (int r = 0; r < BM / 64; ++r) {
                 const int row = u.m0 + lane + 64 * r;
-                raw_max[r] = (!TWO_GROUPS || row < M) ? p.grp[row] : -1;
+                raw_max[r] = (!PAST_M || row < M) ? p.grp[row] : -1;
             }
 #pragma unroll
             for (int i = 0; i < SM; ++i) {
                 const int row = u.m0 + wm + 16 * i + fr;
-                raw_row[i] = (!TWO_GROUPS || row < M) ? p.grp[row] : -1;
+                raw_row[i] = (!PAST_M || row < M) ? p.grp[row] : -1;
             }
         }
     };
@@ -387,7 +459,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 }
                 u.g2 = __builtin_amdgcn_readfirstlane(wave_max(second));
             }
-            u.empty = u.g < 0;
+            // (a tail launch's tile in the second half of a ragged last 256-column tile can
+            // start past N)
+            u.empty = u.g < 0 || (TAIL && u.n0 >= N);
 #pragma unroll
             for (int i = 0; i < SM; ++i)
                 rowg_next[i] = raw_row[i];
@@ -732,7 +806,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                     cur.empty = true;  // the tile's own workgroup runs it
                 cur.g2 = -1;
             } else if (match && p.straddle_rows > 0) {
-                scan_listed();
+                scan_listed(tiles_m);
                 int rank = 0;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -1395,17 +1469,39 @@ static int64_t straddle_wgs(int mode, int bm, bool persistent, const GemmArgs &a
     return ((int64_t)a.straddle_rows * tiles_n + 7) / 8 * 8;
 }
 
+// Tiles a launch sizes its grid for: the tile grid (times the groups, masked), or for the
+// tail launch of the contiguous form (128 x 128 tiles, tail_cus > 0) the 128 x 128 tiles of
+// at most tail_max 256 x 256 tiles.  -1: tail fields on a launch that does not take them.
+static int64_t launch_tiles(int mode, int bm, int bn, bool persistent, const GemmArgs &a,
+                            int tiles_m, int tiles_n)
+{
+    if (a.tail_cus > 0) {
+        if (mode != MODE_CONTIG)
+            return -1;
+        if (bm == 256 && !persistent)
+            return (int64_t)tiles_m * tiles_n;
+        if (bm != 128 || bn != 128 || !persistent || a.tail_max <= 0 || a.tail_tm <= 0 ||
+            a.tail_tn <= 0)
+            return -1;
+        return (int64_t)4 * a.tail_max;
+    }
+    int64_t g = (int64_t)tiles_m * tiles_n;
+    if (mode == MODE_MASKED)
+        g *= a.num_groups;
+    return g;
+}
+
 int64_t grid_size(int mode, int cfg, const GemmArgs &a)
 {
     if (cfg == CFG_STREAM64)
         return mode == MODE_DENSE ? stream_grid_size(a) : -1;
     int tiles_m, tiles_n;
     tiles_for(cfg, a, tiles_m, tiles_n);
-    int64_t g = (int64_t)tiles_m * tiles_n;
-    if (mode == MODE_MASKED)
-        g *= a.num_groups;
-    return workgroups(g, kTiles[cfg].persistent, a) +
-           straddle_wgs(mode, kTiles[cfg].bm, kTiles[cfg].persistent, a, tiles_n);
+    const TileInfo &ti = kTiles[cfg];
+    const int64_t g = launch_tiles(mode, ti.bm, ti.bn, ti.persistent, a, tiles_m, tiles_n);
+    if (g <= 0)
+        return -1;
+    return workgroups(g, ti.persistent, a) + straddle_wgs(mode, ti.bm, ti.persistent, a, tiles_n);
 }
 
 template <int BM, int BN, int WM, int WN, int DEPTH, bool PERSIST, int SF>
@@ -1459,9 +1555,7 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     tiles_m = (a.m + BM - 1) / BM;
     if (mode == MODE_CONTIG && BM > 128 && PERSIST)
         return hipErrorInvalidConfiguration;  // straddling tiles need one workgroup per tile
-    int64_t total = (int64_t)tiles_m * tiles_n;
-    if (mode == MODE_MASKED)
-        total *= a.num_groups;
+    const int64_t total = launch_tiles(mode, BM, BN, PERSIST, a, tiles_m, tiles_n);
     if (total <= 0 || total > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const int64_t grid = workgroups(total, PERSIST, a) + straddle_wgs(mode, BM, PERSIST, a, tiles_n);

@@ -70,6 +70,15 @@ struct GemmArgs {
     int sf_fmt;           // ScaleFmt of sfa / sfb (UE8M0: int32 words behind the pointers)
     int straddle_rows;    // contiguous, 256-row tiles: listed straddling tile-rows whose second
                           // group runs on workgroups ahead of the tiles (0: none)
+    // Contiguous tail launch.  With tail_cus > 0, the launch of 256 x 256 tiles leaves the
+    // tiles of its last-dispatched workgroups (the busy ones of its last partial wave over
+    // tail_cus CUs, when they number between tail_cus / 8 and tail_cus / 4; tail_force of
+    // them, if set) to a second launch of 128 x 128 tiles, which is given tail_tm x tail_tn,
+    // the 256 x 256 tile grid, and at most tail_max of them.
+    int tail_cus;
+    int tail_force;
+    int tail_tm, tail_tn;
+    int tail_max;
     uint8_t *q;           // MODE_CONTIG_SWIGLU: e4m3 codes [m, n/2]
     float *sfq;           // MODE_CONTIG_SWIGLU: FP32 scales [n/256][ld_sfq] (MN-major)
     int64_t ld_sfq;

@@ -40,4 +40,22 @@ DG_HD inline TileRange xcd_tile_range(int64_t total, int grid, int lead, int id)
     return t;
 }
 
+// The inverse for one workgroup per tile (total == grid - lead): the id of the workgroup that
+// xcd_tile_range gives tile `tile` to.  XCD x's range starts at w_x and its workgroups take
+// one tile each in id order, so the tile w_x + j falls to workgroup lead + 8 j + x.
+// Preconditions: 0 < total == grid - lead, 0 <= tile < total.
+DG_HD inline int xcd_tile_owner(int total, int lead, int tile)
+{
+    const int q = total >> 3, r = total & 7;
+    int x, j;
+    if (tile < r * (q + 1)) {
+        x = tile / (q + 1);
+        j = tile - x * (q + 1);
+    } else {
+        x = r + (tile - r * (q + 1)) / q;
+        j = tile - (r * (q + 1) + (x - r) * q);
+    }
+    return lead + 8 * j + x;
+}
+
 }  // namespace dg

@@ -1,6 +1,7 @@
 // Host check of the XCD-aware tile mapping (dg_tiles.h): for each (tiles, workgroups, lead)
-// case on the command line, every tile id in [0, tiles) must fall to exactly one workgroup.
-// Prints "ok <tiles> <workgroups> <lead>" per case, or the first fault and exits non-zero.
+// case on the command line, every tile id in [0, tiles) must fall to exactly one workgroup,
+// and with one workgroup per tile xcd_tile_owner must name that workgroup.  Prints
+// "ok <tiles> <workgroups> <lead>" per case, or the first fault and exits non-zero.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -11,6 +12,7 @@
 static int check(long long total, int workgroups, int lead)
 {
     std::vector<unsigned char> hits((size_t)total, 0);
+    std::vector<int> owner((size_t)total, -1);
     const int grid = workgroups + lead;
     for (int id = lead; id < grid; ++id) {
         const dg::TileRange r = dg::xcd_tile_range(total, grid, lead, id);
@@ -28,6 +30,7 @@ static int check(long long total, int workgroups, int lead)
                 printf("tile %lld covered twice (id %d)\n", t, id);
                 return 1;
             }
+            owner[(size_t)t] = id;
         }
     }
     for (long long t = 0; t < total; ++t)
@@ -35,6 +38,13 @@ static int check(long long total, int workgroups, int lead)
             printf("tile %lld never covered\n", t);
             return 1;
         }
+    if (total == workgroups)
+        for (long long t = 0; t < total; ++t)
+            if (dg::xcd_tile_owner((int)total, lead, (int)t) != owner[(size_t)t]) {
+                printf("owner of tile %lld: %d, not %d\n", t,
+                       dg::xcd_tile_owner((int)total, lead, (int)t), owner[(size_t)t]);
+                return 1;
+            }
     printf("ok %lld %d %d\n", total, workgroups, lead);
     return 0;
 }

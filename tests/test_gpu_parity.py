@@ -355,6 +355,90 @@ def test_contiguous_256_row_tiles_unordered_groups(served, monkeypatch):
     assert not np.any(got[q.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
+# The tail launch: the tiles of the last-dispatched workgroups of a 256 x 256 launch run as
+# 128 x 128 tiles in a second launch (DG_TAIL_TILES forces how many; 9 is more than the 8
+# tiles there are, so all but one).  Straddling tiles among them (their second group then no
+# longer served ahead), tiles whose second 128-row half lies past m_total, and a ragged last N
+# tile whose second 128-column half lies wholly past N (n = 272) or partly (n = 400).
+@pytest.mark.parametrize("tail", ["1", "3", "5", "9"])
+@pytest.mark.parametrize("served", [None, "1"])
+@pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
+@pytest.mark.parametrize("n", [400, 272])
+def test_contiguous_tail_launch(tail, served, counts, n, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_TAIL_TILES", tail)
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
+    p = W.make_contiguous(5, sum(counts), n, 640, seed=34, counts=counts, stress=True,
+                          pad_nan=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"tail {tail} served={served} {counts} n={n}")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
+@pytest.mark.parametrize("wgs", ["1", "3"])
+def test_contiguous_tail_launch_with_few_workgroups(wgs, monkeypatch):
+    # the tail launch's persistent workgroups each loop over several 128 x 128 tiles
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_TAIL_TILES", "6")
+    monkeypatch.setenv("DG_PERSIST_WGS", wgs)
+    p = W.make_contiguous(4, 1100, 768, 384, seed=39, counts=[300, 0, 500, 300], stress=True,
+                          pad_nan=True)
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"tail, {wgs} workgroups")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
+def test_contiguous_tail_launch_chosen_by_the_wave(monkeypatch, capfd):
+    # 19 x 16 = 304 tiles of 256 x 256 and one group: on 256 CUs the last partial wave holds
+    # 48 tiles (between an eighth and a quarter of the CUs), which go to the tail launch
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_PRINT_CONFIGS", "1")
+    p = W.make_contiguous(1, 4864, 4096, 256, seed=40, counts=[4864])
+    cus = dg.get_num_cus()
+    r = 304 % cus
+    planned = 8 * r >= cus and 4 * r <= cus and r < 304
+    got = run_contiguous(p)
+    err = capfd.readouterr().err
+    assert (f"tail up to {cus // 4} tiles" in err) == planned, err
+    ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(got, ref, "tail chosen by the wave")
+    monkeypatch.setenv("DG_TAIL_TILES", "0")
+    assert_parity(run_contiguous(p), ref, "tail turned off")
+
+
+def test_contiguous_tail_launch_graph_replays(monkeypatch):
+    # both launches captured in one graph, replayed with eager calls in between
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_TAIL_TILES", "5")
+    p = W.make_contiguous(5, 472, 400, 640, seed=34, counts=[41, 0, 300, 1, 130], stress=True)
+    a, sfa, b, sfb, idx = (dev(x) for x in (p.a, p.sfa, p.b, p.sfb, p.m_indices))
+    d = sentinel_like((p.m_total, p.n))
+    dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, idx)
+    torch.cuda.synchronize()
+    first = bits(d).copy()
+    assert_parity(first, oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices),
+                  "tail eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, idx)
+    torch.cuda.synchronize()
+    blank = sentinel_like((p.m_total, p.n))  # (padding rows must keep it)
+    for r in range(3):
+        d.copy_(blank)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), first), f"graph replay {r}"
+        dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), first), f"eager call after replay {r}"
+
+
 def test_contiguous_stress_routing():
     p = W.make_contiguous(4, 700, 384, 256, seed=32, stress=True)
     ref = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.m_indices)

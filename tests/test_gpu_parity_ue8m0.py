@@ -152,6 +152,21 @@ def test_contiguous_256_row_tiles_across_group_boundaries(counts, monkeypatch):
     assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
+@pytest.mark.parametrize("tail", ["2", "7"])
+@pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
+def test_contiguous_tail_launch(tail, counts, monkeypatch):
+    # the tiles of the last-dispatched workgroups of the 256 x 256 launch as 128 x 128 tiles in
+    # a second launch, straddles and a tile half past m_total among them
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_TAIL_TILES", tail)
+    p = W.make_contiguous(5, sum(counts), 400, 640, seed=62, counts=counts, stress=True,
+                          pad_nan=True, ue8m0=True)
+    ref = oracle.m_grouped_contiguous_ue8m0(p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    got = run_contiguous(p)
+    assert_parity(got, ref, f"contiguous ue8m0 tail {tail} {counts}")
+    assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
+
+
 def test_contiguous_workload_full():
     p = W.make_config("moe_contiguous", seed=0, ue8m0=True)    # 8 experts, 32768 x 4096 x 7168
     got = run_contiguous(p)

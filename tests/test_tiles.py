@@ -1,7 +1,9 @@
 """The XCD-aware tile mapping (``dg_tiles.h``, used by the GEMM kernels) checked on the host:
 every tile id is assigned to exactly one workgroup, for persistent grids (fewer workgroups
 than tiles), one workgroup per tile (up to 75008 tiles, where 32-bit products of the tile
-count and the grid would wrap), and with straddle-serving workgroups ahead of the tiles.
+count and the grid would wrap), and with straddle-serving workgroups ahead of the tiles; with
+one workgroup per tile, the inverse (``xcd_tile_owner``, which the contiguous tail launch uses
+to find the tiles of the workgroups dispatched last) names the workgroup of every tile.
 CPU only: the header is plain C++ and is compiled here with g++."""
 import os
 import subprocess
@@ -32,7 +34,7 @@ def _run(exe, cases):
 def test_one_workgroup_per_tile(tile_cover, lead):
     # G == total: 46341 is the first count whose total * G passes 2^31, 65536 the first whose
     # product passes 2^32, 75008 the 256x224 tile count of a 65536 x 65536 output
-    _run(tile_cover, [(g, g, lead) for g in list(range(1, 10)) + [46341, 65536, 75008]])
+    _run(tile_cover, [(g, g, lead) for g in list(range(1, 41)) + [2080, 3640, 46341, 65536, 75008]])
 
 
 @pytest.mark.parametrize("lead", [0, 16])
@@ -41,3 +43,11 @@ def test_persistent_workgroups(tile_cover, lead):
     cases += [(t, g, lead) for g in (255, 256, 46341, 65536)
               for t in (g, g + 7, 3 * g + 5, 1 << 21)]
     _run(tile_cover, cases)
+
+
+@pytest.mark.parametrize("lead", [0, 8])
+def test_more_workgroups_than_tiles(tile_cover, lead):
+    # a persistent grid sized for more tiles than a launch finds (the contiguous tail launch
+    # sizes its grid for the most tiles it may get): the spare workgroups get no tile
+    _run(tile_cover, [(t, g, lead) for g in (2, 8, 9, 256, 1000) for t in (1, 3, g - 1, g // 2 + 1)
+                      if 0 < t < g])
