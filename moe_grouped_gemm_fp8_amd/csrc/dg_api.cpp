@@ -175,8 +175,7 @@ void print_config(const char *what, int m, int n, int k, int g, int cfg, int spl
         snprintf(hint, sizeof(hint), " expected_m=%d", expected_m);
     char tl[64] = "";
     if (tail > 0)
-        snprintf(tl, sizeof(tl), ", tail up to %d tiles as %s", tail,
-                 dg::kTiles[dg::CFG_128x128w8d4].name);
+        snprintf(tl, sizeof(tl), ", tail up to %d tiles as 128x128", tail);
     fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d%s -> tile %s (%dx%d), splits=%d%s\n", what,
             m, n, k, g, hint, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn,
             splits, tl);
@@ -459,12 +458,13 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
         if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
             args.straddle_rows = atoi(e);
     }
-    // The tail launch.  256 x 256 tiles run one workgroup each, and the last ones dispatched
-    // can form a last partial wave that leaves most CUs idle.  Where that wave could hold
-    // between an eighth and a quarter of the CUs' worth of busy workgroups (for some count of
-    // served straddles; the kernels count the actual ones from the group indices), a second
-    // launch of 128 x 128 tiles follows and runs the tiles of those workgroups over four times
-    // as many CUs.  DG_TAIL_TILES=n (tests) leaves n tiles to it whatever the wave, 0 never.
+    // The tail.  256 x 256 tiles run one workgroup each, and the last ones dispatched can
+    // form a last partial wave that leaves most CUs idle.  Where that wave could hold between
+    // an eighth and a quarter of the CUs' worth of busy workgroups (for some count of served
+    // straddles; the kernel counts the actual ones from the group indices), the launch gets
+    // workgroups of 128 x 128 tiles after the others, which run the tiles of those last
+    // workgroups over four times as many CUs.  DG_TAIL_TILES=n (tests) leaves n tiles to them
+    // whatever the wave, 0 never.
     int tail_max = 0;
     if (cfg == dg::CFG_256x256) {
         const char *e = getenv("DG_TAIL_TILES");
@@ -491,10 +491,16 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
         }
     }
     print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1, -1, tail_max);
-    rc = launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
-    if (rc != DG_OK || tail_max == 0)
-        return rc;
-    return launch(dg::MODE_CONTIG, dg::CFG_128x128w8d4, args, (hipStream_t)stream);
+    if (tail_max == 0)
+        return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
+    const int64_t grid = dg::contig_tail_grid(args);
+    if (grid <= 0 || grid > 0x7fffffff)
+        return fail(DG_ERR_UNSUPPORTED, "problem too large for one launch (%lld workgroups)",
+                    (long long)grid);
+    const hipError_t e = dg::launch_contig_tail(args, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 // The contiguous form with the activation step fused into the epilogue: B is [G, 2I, K] with

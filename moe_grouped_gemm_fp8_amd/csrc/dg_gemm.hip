@@ -41,9 +41,10 @@
 //    together on one XCD share A rows and B columns in that XCD's L2.  The smaller tile shapes
 //    run persistent workgroups (one per CU) that walk their XCD's range; the next tile's
 //    first K blocks are copied while the current tile finishes, hiding the per-tile prologue.
-//    The 256-row tiles run one workgroup per tile.  The contiguous form's 256 x 256 launch can
-//    leave the tiles of its last-dispatched workgroups (a last partial wave) to a second launch
-//    of 128 x 128 tiles, which spreads them over four times as many CUs.
+//    The 256-row tiles run one workgroup per tile.  The contiguous form's 256 x 256 tiles can
+//    leave the tiles of their last-dispatched workgroups (a last partial wave) to workgroups of
+//    128 x 128 tiles at the end of the same launch, which spread them over four times as many
+//    CUs.
 //  * The contiguous form can instead write the 1x128 FP8 cast of SwiGLU(gate, up) of its
 //    FP32 result (the activation between an MoE block's two expert GEMMs), its tiles holding
 //    the gate and up columns of one 128-column segment of the activation.
@@ -124,8 +125,20 @@ __device__ __forceinline__ void store4_async(void *dst, uint32_t v)
     asm volatile("global_store_dword %0, %1, off" ::"v"(dst), "v"(v) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int SF>
-__device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int tiles_n)
+// The LDS of a kernel that runs one tile shape (one static allocation per instantiation)
+template <int BYTES>
+__device__ __forceinline__ uint8_t *own_lds()
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[BYTES];
+    return lds;
+}
+
+// Tiles of workgroup wg of nwg (the kernel's grid, or its share of a grid that also runs another
+// tile shape: EXT, the LDS then given by the kernel).
+template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int SF,
+          bool EXT = false>
+__device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int tiles_n, int wg,
+                                           int nwg, uint8_t *ext_lds = nullptr)
 {
     // Scale format.  FP32 scales are applied on the vector unit: every MFMA result is one K
     // block's partial, promoted into the FP32 accumulators with sa * sb.  Packed UE8M0 scales
@@ -203,7 +216,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     constexpr int OS = BN * 2 + ((BN * 2) % 256 == 224 ? 0 : 32);
     constexpr int LDS_ALLOC = (!PERSIST && BM * OS > LDS_BYTES) ? BM * OS : LDS_BYTES;
     static_assert(LDS_ALLOC <= 160 * 1024, "LDS budget (output tile)");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_ALLOC];
+    uint8_t *lds;
+    if constexpr (EXT)
+        lds = ext_lds;  // (160 KB, shared with the other tile shape of the launch)
+    else
+        lds = own_lds<LDS_ALLOC>();
 
     // SwiGLU: one tile covers the gate and up columns of one 128-wide segment of h (BN = 256),
     // each wave TN / 2 of its h columns (TN / 32 gate/up sub-tile pairs), FP32 scales
@@ -253,17 +270,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // the second pass itself only for a straddle not served so (a straddle the first rows do
     // not show, or one past straddle_rows).  Both sides decide from the same loads.
     //
-    // Tail launch (tail_cus > 0): the last workgroups of a launch of 256 x 256 tiles are
-    // dispatched last, one per XCD in turn, and where they form a last partial wave of whole
-    // tiles the launch ends with most CUs idle.  The workgroups of the last tail_tiles() ids
-    // then leave their tiles to a second launch of 128 x 128 tiles (TAIL below), which runs
-    // them over four times as many CUs; the straddle workgroups skip them too, since a
-    // 128-row tile holds one group.  Both launches count the same served straddles.
-    constexpr bool TAIL = CONTIG && !SWIGLU && PERSIST && BM == 128 && BN == 128;
+    // Tail (dg_gemm_contig_tail_kernel, tail_cus > 0): the last workgroups of 256 x 256 tiles
+    // are dispatched last, one per XCD in turn, and where they form a last partial wave of
+    // whole tiles the launch ends with most CUs idle.  The workgroups of the last tail_tiles()
+    // ids (TAIL_MAIN) then leave their tiles to the launch's workgroups of 128 x 128 tiles
+    // (TAIL), which run them over four times as many CUs; the straddle workgroups skip them
+    // too, since a 128-row tile holds one group.  Both count the same served straddles.
+    constexpr bool TAIL_MAIN = EXT && MODE == MODE_CONTIG && TWO_GROUPS;
+    constexpr bool TAIL = EXT && MODE == MODE_CONTIG && PERSIST && BM == 128 && BN == 128;
     constexpr int SUB = (256 / BM) * (256 / BN);  // TAIL: 128 x 128 tiles per 256 x 256 tile
     int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
     const int E = TWO_GROUPS ? ((p.straddle_rows * tiles_n + 7) & ~7) : 0;
-    const int bid = (int)blockIdx.x - E;  // < 0: a workgroup serving a listed straddle
+    const int bid = wg - E;  // < 0: a workgroup serving a listed straddle
     int tile_id, tile_end, tile_step;
     // listed straddles among 256-row tile-rows 64 c + lane (c < 4; the host lists them only
     // while there are at most 256), and the groups of tile-row t's two block-leading rows
@@ -303,7 +321,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         const int r = (tiles + served * tn256) % p.tail_cus;
         return (8 * r >= p.tail_cus && 4 * r <= p.tail_cus && r < tiles) ? r : 0;
     };
-    int tail_n = 0;  // TAIL: the 256 x 256 tiles this launch covers
+    int tail_n = 0;  // TAIL: the 256 x 256 tiles these workgroups cover
     if constexpr (TAIL) {
         if (p.tail_cus > 0) {
             if (p.straddle_rows > 0)
@@ -314,7 +332,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 return;
         }
     }
-    if (TWO_GROUPS && p.tail_cus > 0 && bid >= 0) {
+    if (TAIL_MAIN && p.tail_cus > 0 && bid >= 0) {
         // (only the last workgroups can be left to the tail launch)
         const int cap = p.tail_force > 0 ? total : p.tail_cus / 4;
         if (bid >= total - cap) {
@@ -325,7 +343,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         }
     }
     if (TWO_GROUPS && bid < 0) {
-        const int b = (int)blockIdx.x / tiles_n, tn = (int)blockIdx.x - b * tiles_n;
+        const int b = wg / tiles_n, tn = wg - b * tiles_n;
         if (b >= p.straddle_rows)
             return;  // (E is rounded up to whole XCD rounds)
         scan_listed(tiles_m);
@@ -344,7 +362,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if (t < 0)
             return;  // fewer listed straddles than served slots
         tile_id = raster_index(t, tn, tiles_m, tiles_n);
-        if (p.tail_cus > 0) {
+        if (TAIL_MAIN && p.tail_cus > 0) {
             // a tile left to the tail launch (its own workgroup is among the last ids)
             const int left = tail_tiles(total, tiles_n);
             if (left > 0 && xcd_tile_owner(total, E, tile_id) - E >= total - left)
@@ -353,7 +371,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         tile_end = tile_id + 1;
         tile_step = 1;
     } else {
-        const TileRange tr = xcd_tile_range(total, (int)gridDim.x, E, (int)blockIdx.x);
+        const TileRange tr = xcd_tile_range(total, nwg, E, wg);
         tile_id = tr.first;
         tile_end = tr.end;
         tile_step = tr.step;
@@ -1438,7 +1456,29 @@ template <int BM, int BN, int WM, int WN, int DEPTH, int MODE, bool PERSIST, int
 __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n)
 {
-    gemm_tiles<BM, BN, WM, WN, DEPTH, MODE, PERSIST, SF>(p, tiles_m, tiles_n);
+    gemm_tiles<BM, BN, WM, WN, DEPTH, MODE, PERSIST, SF>(p, tiles_m, tiles_n, (int)blockIdx.x,
+                                                         (int)gridDim.x);
+}
+
+// The contiguous form's 256 x 256 tiles and their tail in one launch: workgroups below
+// main_wgs run the 256 x 256 tiles (straddle workgroups first), those from main_wgs rounded up
+// to a whole XCD round the tail's 128 x 128 tiles (persistent), in one LDS allocation both fit.
+// The tail workgroups come last in the grid, so they are dispatched as the 256 x 256 tiles'
+// CUs free up; where the kernels find no tail tiles they exit at once.
+constexpr int TAIL_BM = 128, TAIL_BN = 128, TAIL_WM = 2, TAIL_WN = 4, TAIL_DEPTH = 4;
+template <int SF>
+__global__ __launch_bounds__(512) void dg_gemm_contig_tail_kernel(GemmArgs p, int tiles_m,
+                                                                  int tiles_n, int main_wgs)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[160 * 1024];
+    const int wg = (int)blockIdx.x;
+    const int tail0 = (main_wgs + 7) & ~7;
+    if (wg < main_wgs)
+        gemm_tiles<256, 256, 4, 2, 2, MODE_CONTIG, false, SF, true>(p, tiles_m, tiles_n, wg,
+                                                                    main_wgs, lds);
+    else if (wg >= tail0)
+        gemm_tiles<TAIL_BM, TAIL_BN, TAIL_WM, TAIL_WN, TAIL_DEPTH, MODE_CONTIG, true, SF, true>(
+            p, 2 * tiles_m, 2 * tiles_n, wg - tail0, (int)gridDim.x - tail0, lds);
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -1469,22 +1509,12 @@ static int64_t straddle_wgs(int mode, int bm, bool persistent, const GemmArgs &a
     return ((int64_t)a.straddle_rows * tiles_n + 7) / 8 * 8;
 }
 
-// Tiles a launch sizes its grid for: the tile grid (times the groups, masked), or for the
-// tail launch of the contiguous form (128 x 128 tiles, tail_cus > 0) the 128 x 128 tiles of
-// at most tail_max 256 x 256 tiles.  -1: tail fields on a launch that does not take them.
-static int64_t launch_tiles(int mode, int bm, int bn, bool persistent, const GemmArgs &a,
-                            int tiles_m, int tiles_n)
+// Tiles a launch sizes its grid for: the tile grid (times the groups, masked).  -1: the tail
+// fields set (they go to launch_contig_tail only).
+static int64_t launch_tiles(int mode, const GemmArgs &a, int tiles_m, int tiles_n)
 {
-    if (a.tail_cus > 0) {
-        if (mode != MODE_CONTIG)
-            return -1;
-        if (bm == 256 && !persistent)
-            return (int64_t)tiles_m * tiles_n;
-        if (bm != 128 || bn != 128 || !persistent || a.tail_max <= 0 || a.tail_tm <= 0 ||
-            a.tail_tn <= 0)
-            return -1;
-        return (int64_t)4 * a.tail_max;
-    }
+    if (a.tail_cus > 0)
+        return -1;
     int64_t g = (int64_t)tiles_m * tiles_n;
     if (mode == MODE_MASKED)
         g *= a.num_groups;
@@ -1498,7 +1528,7 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &a)
     int tiles_m, tiles_n;
     tiles_for(cfg, a, tiles_m, tiles_n);
     const TileInfo &ti = kTiles[cfg];
-    const int64_t g = launch_tiles(mode, ti.bm, ti.bn, ti.persistent, a, tiles_m, tiles_n);
+    const int64_t g = launch_tiles(mode, a, tiles_m, tiles_n);
     if (g <= 0)
         return -1;
     return workgroups(g, ti.persistent, a) + straddle_wgs(mode, ti.bm, ti.persistent, a, tiles_n);
@@ -1555,7 +1585,7 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     tiles_m = (a.m + BM - 1) / BM;
     if (mode == MODE_CONTIG && BM > 128 && PERSIST)
         return hipErrorInvalidConfiguration;  // straddling tiles need one workgroup per tile
-    const int64_t total = launch_tiles(mode, BM, BN, PERSIST, a, tiles_m, tiles_n);
+    const int64_t total = launch_tiles(mode, a, tiles_m, tiles_n);
     if (total <= 0 || total > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const int64_t grid = workgroups(total, PERSIST, a) + straddle_wgs(mode, BM, PERSIST, a, tiles_n);
@@ -1574,6 +1604,34 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
                                                                          tiles_n, stream);
     if (!launched)
         return hipErrorInvalidConfiguration;  // no kernel of this form for this tile
+    return hipGetLastError();
+}
+
+int64_t contig_tail_grid(const GemmArgs &a)
+{
+    const int tiles_m = (a.m + 255) / 256, tiles_n = (a.n + 255) / 256;
+    const int64_t main_wgs =
+        (int64_t)tiles_m * tiles_n + straddle_wgs(MODE_CONTIG, 256, false, a, tiles_n);
+    return (main_wgs + 7) / 8 * 8 + workgroups((int64_t)4 * a.tail_max, true, a);
+}
+
+hipError_t launch_contig_tail(const GemmArgs &a, hipStream_t stream)
+{
+    if (a.tail_cus <= 0 || a.tail_max <= 0 || a.tail_tm <= 0 || a.tail_tn <= 0 ||
+        (a.sf_fmt != SF_FP32 && a.sf_fmt != SF_UE8M0))
+        return hipErrorInvalidConfiguration;
+    const int tiles_m = (a.m + 255) / 256, tiles_n = (a.n + 255) / 256;
+    const int64_t main_wgs =
+        (int64_t)tiles_m * tiles_n + straddle_wgs(MODE_CONTIG, 256, false, a, tiles_n);
+    const int64_t grid = contig_tail_grid(a);
+    if (tiles_m != a.tail_tm || tiles_n != a.tail_tn || grid <= 0 || grid > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    if (a.sf_fmt == SF_UE8M0)
+        hipLaunchKernelGGL(dg_gemm_contig_tail_kernel<SF_UE8M0>, dim3((unsigned)grid), dim3(512),
+                           0, stream, a, tiles_m, tiles_n, (int)main_wgs);
+    else
+        hipLaunchKernelGGL(dg_gemm_contig_tail_kernel<SF_FP32>, dim3((unsigned)grid), dim3(512),
+                           0, stream, a, tiles_m, tiles_n, (int)main_wgs);
     return hipGetLastError();
 }
 
