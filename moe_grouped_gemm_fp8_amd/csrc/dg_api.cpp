@@ -175,7 +175,7 @@ void print_config(const char *what, int m, int n, int k, int g, int cfg, int spl
         snprintf(hint, sizeof(hint), " expected_m=%d", expected_m);
     char tl[64] = "";
     if (tail > 0)
-        snprintf(tl, sizeof(tl), ", tail up to %d tiles as 128x128", tail);
+        snprintf(tl, sizeof(tl), ", tail up to %d tiles in 128-row tiles", tail);
     fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d%s -> tile %s (%dx%d), splits=%d%s\n", what,
             m, n, k, g, hint, dg::kTiles[cfg].name, dg::kTiles[cfg].bm, dg::kTiles[cfg].bn,
             splits, tl);
@@ -206,6 +206,52 @@ int launch(int mode, int cfg, dg::GemmArgs &args, hipStream_t stream)
 int gemm_nt(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,
             const float *sfb, const float *c, void *d, int m, int n, int k, void *stream,
             bool noalloc = false);
+
+// The tail of the contiguous forms' 256 x 256 tiles (args.straddle_rows already set).  These
+// tiles run one workgroup each, and the last ones dispatched can form a last partial wave that
+// leaves most CUs idle.  Where that wave could hold between an eighth and a quarter of the CUs'
+// worth of busy workgroups (for some count of served straddles; the kernel counts the actual
+// ones from the group indices), the launch gets workgroups of 128-row tiles after the others,
+// which run the tiles of those last workgroups over two or four times as many CUs.
+// DG_TAIL_TILES=n (tests) leaves n tiles to them whatever the wave, 0 never.  Sets the tail
+// fields of args; returns the most tiles the tail may take (0: no tail).
+int plan_contig_tail(dg::GemmArgs &args, int m_total, int n, int cus)
+{
+    const char *e = getenv("DG_TAIL_TILES");
+    const int force = (e && *e) ? atoi(e) : -1;
+    const int tm = (m_total + 255) / 256, tn = (n + 255) / 256;
+    const int64_t tiles = (int64_t)tm * tn;
+    int tail_max = 0;
+    if (force > 0) {
+        tail_max = (int)(force < tiles - 1 ? force : tiles - 1);
+    } else if (force < 0) {
+        for (int s = 0; s <= args.straddle_rows && tail_max == 0; ++s) {
+            const int64_t r = (tiles + (int64_t)s * tn) % cus;
+            if (8 * r >= cus && 4 * r <= cus && r < tiles)
+                tail_max = cus / 4;
+        }
+    }
+    if (tail_max > 0) {
+        args.tail_cus = cus;
+        args.tail_force = force > 0 ? force : 0;
+        args.tail_tm = tm;
+        args.tail_tn = tn;
+        args.tail_max = tail_max;
+    }
+    return tail_max;
+}
+
+int launch_with_tail(int mode, const dg::GemmArgs &args, hipStream_t stream)
+{
+    const int64_t grid = dg::contig_tail_grid(mode, args);
+    if (grid <= 0 || grid > 0x7fffffff)
+        return fail(DG_ERR_UNSUPPORTED, "problem too large for one launch (%lld workgroups)",
+                    (long long)grid);
+    const hipError_t e = dg::launch_contig_tail(mode, args, stream);
+    if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
 
 bool layout_native_forced()
 {
@@ -458,49 +504,11 @@ int grouped_contiguous(int sf_fmt, const void *a, const float *sfa, int64_t ld_s
         if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
             args.straddle_rows = atoi(e);
     }
-    // The tail.  256 x 256 tiles run one workgroup each, and the last ones dispatched can
-    // form a last partial wave that leaves most CUs idle.  Where that wave could hold between
-    // an eighth and a quarter of the CUs' worth of busy workgroups (for some count of served
-    // straddles; the kernel counts the actual ones from the group indices), the launch gets
-    // workgroups of 128 x 128 tiles after the others, which run the tiles of those last
-    // workgroups over four times as many CUs.  DG_TAIL_TILES=n (tests) leaves n tiles to them
-    // whatever the wave, 0 never.
-    int tail_max = 0;
-    if (cfg == dg::CFG_256x256) {
-        const char *e = getenv("DG_TAIL_TILES");
-        const int force = (e && *e) ? atoi(e) : -1;
-        const int tm = (m_total + 255) / 256, tn = (n + 255) / 256;
-        const int64_t tiles = (int64_t)tm * tn;
-        if (force > 0) {
-            tail_max = (int)(force < tiles - 1 ? force : tiles - 1);
-            args.tail_force = force;
-        } else if (force < 0) {
-            for (int s = 0; s <= args.straddle_rows && tail_max == 0; ++s) {
-                const int64_t r = (tiles + (int64_t)s * tn) % cus;
-                if (8 * r >= cus && 4 * r <= cus && r < tiles)
-                    tail_max = cus / 4;
-            }
-        }
-        if (tail_max > 0) {
-            args.tail_cus = cus;
-            args.tail_tm = tm;
-            args.tail_tn = tn;
-            args.tail_max = tail_max;
-        } else {
-            args.tail_force = 0;
-        }
-    }
+    const int tail_max = cfg == dg::CFG_256x256 ? plan_contig_tail(args, m_total, n, cus) : 0;
     print_config("m_grouped_contiguous", m_total, n, k, num_groups, cfg, 1, -1, tail_max);
     if (tail_max == 0)
         return launch(dg::MODE_CONTIG, cfg, args, (hipStream_t)stream);
-    const int64_t grid = dg::contig_tail_grid(args);
-    if (grid <= 0 || grid > 0x7fffffff)
-        return fail(DG_ERR_UNSUPPORTED, "problem too large for one launch (%lld workgroups)",
-                    (long long)grid);
-    const hipError_t e = dg::launch_contig_tail(args, (hipStream_t)stream);
-    if (e != hipSuccess)
-        return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return launch_with_tail(dg::MODE_CONTIG, args, (hipStream_t)stream);
 }
 
 // The contiguous form with the activation step fused into the epilogue: B is [G, 2I, K] with
@@ -571,8 +579,11 @@ int grouped_contiguous_swiglu(const void *a, const float *sfa, int64_t ld_sfa, c
         if (e && *e && atoi(e) >= 0 && atoi(e) < args.straddle_rows)
             args.straddle_rows = atoi(e);
     }
-    print_config("m_grouped_contiguous_swiglu", m_total, n, k, num_groups, cfg, 1);
-    return launch(dg::MODE_CONTIG_SWIGLU, cfg, args, (hipStream_t)stream);
+    const int tail_max = cfg == dg::CFG_256x256 ? plan_contig_tail(args, m_total, n, cus) : 0;
+    print_config("m_grouped_contiguous_swiglu", m_total, n, k, num_groups, cfg, 1, -1, tail_max);
+    if (tail_max == 0)
+        return launch(dg::MODE_CONTIG_SWIGLU, cfg, args, (hipStream_t)stream);
+    return launch_with_tail(dg::MODE_CONTIG_SWIGLU, args, (hipStream_t)stream);
 }
 
 int grouped_masked(int sf_fmt, const void *a, const float *sfa, int64_t ld_sfa, const void *b,

@@ -274,11 +274,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     // are dispatched last, one per XCD in turn, and where they form a last partial wave of
     // whole tiles the launch ends with most CUs idle.  The workgroups of the last tail_tiles()
     // ids (TAIL_MAIN) then leave their tiles to the launch's workgroups of 128 x 128 tiles
-    // (TAIL), which run them over four times as many CUs; the straddle workgroups skip them
-    // too, since a 128-row tile holds one group.  Both count the same served straddles.
-    constexpr bool TAIL_MAIN = EXT && MODE == MODE_CONTIG && TWO_GROUPS;
-    constexpr bool TAIL = EXT && MODE == MODE_CONTIG && PERSIST && BM == 128 && BN == 128;
-    constexpr int SUB = (256 / BM) * (256 / BN);  // TAIL: 128 x 128 tiles per 256 x 256 tile
+    // (TAIL; 128 x 256 for the fused activation step, whose tiles span 256 columns), which run
+    // them over four (two) times as many CUs; the straddle workgroups skip them too, since a
+    // 128-row tile holds one group.  Both count the same served straddles.
+    constexpr bool TAIL_MAIN = EXT && CONTIG && TWO_GROUPS;
+    constexpr bool TAIL = EXT && CONTIG && PERSIST && BM == 128 && (BN == 128 || BN == 256);
+    constexpr int SUB = (256 / BM) * (256 / BN);  // TAIL: its tiles per 256 x 256 tile
     int total = tiles_m * tiles_n * (MODE == MODE_MASKED ? p.num_groups : 1);
     const int E = TWO_GROUPS ? ((p.straddle_rows * tiles_n + 7) & ~7) : 0;
     const int bid = wg - E;  // < 0: a workgroup serving a listed straddle
@@ -404,8 +405,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             tm = rem - tn * tiles_m;
         } else {
             if (TAIL && tail_n > 0) {
-                // 128 x 128 tile q of the 256 x 256 tile of the launch's workgroup
-                // tiles - tail_n + u (the 256-row launch's own mapping)
+                // tile q of the 256 x 256 tile of the 256 x 256 workgroup tiles - tail_n + u
+                // (found with that shape's own mapping)
                 const int u = t / SUB, q = t - u * SUB;
                 const int tiles = p.tail_tm * p.tail_tn;
                 const int lead = (p.straddle_rows * p.tail_tn + 7) & ~7;
@@ -1462,23 +1463,30 @@ __global__ __launch_bounds__(64 * WM * WN) void dg_gemm_kernel(GemmArgs p, int t
 
 // The contiguous form's 256 x 256 tiles and their tail in one launch: workgroups below
 // main_wgs run the 256 x 256 tiles (straddle workgroups first), those from main_wgs rounded up
-// to a whole XCD round the tail's 128 x 128 tiles (persistent), in one LDS allocation both fit.
-// The tail workgroups come last in the grid, so they are dispatched as the 256 x 256 tiles'
-// CUs free up; where the kernels find no tail tiles they exit at once.
-constexpr int TAIL_BM = 128, TAIL_BN = 128, TAIL_WM = 2, TAIL_WN = 4, TAIL_DEPTH = 4;
-template <int SF>
+// to a whole XCD round the tail's tiles (persistent), in one LDS allocation both fit: 128 x 128
+// tiles (eight waves, copies four blocks ahead), or for the fused activation step 128 x 256
+// (eight waves, four across).  The tail workgroups come last in the grid, so they are
+// dispatched as the 256 x 256 tiles' CUs free up; where they find no tail tiles they exit at
+// once.
+constexpr int tail_sub_tiles(int mode) { return mode == MODE_CONTIG_SWIGLU ? 2 : 4; }
+template <int MODE, int SF>
 __global__ __launch_bounds__(512) void dg_gemm_contig_tail_kernel(GemmArgs p, int tiles_m,
                                                                   int tiles_n, int main_wgs)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[160 * 1024];
     const int wg = (int)blockIdx.x;
     const int tail0 = (main_wgs + 7) & ~7;
-    if (wg < main_wgs)
-        gemm_tiles<256, 256, 4, 2, 2, MODE_CONTIG, false, SF, true>(p, tiles_m, tiles_n, wg,
-                                                                    main_wgs, lds);
-    else if (wg >= tail0)
-        gemm_tiles<TAIL_BM, TAIL_BN, TAIL_WM, TAIL_WN, TAIL_DEPTH, MODE_CONTIG, true, SF, true>(
-            p, 2 * tiles_m, 2 * tiles_n, wg - tail0, (int)gridDim.x - tail0, lds);
+    if (wg < main_wgs) {
+        gemm_tiles<256, 256, 4, 2, 2, MODE, false, SF, true>(p, tiles_m, tiles_n, wg, main_wgs,
+                                                             lds);
+    } else if (wg >= tail0) {
+        if constexpr (MODE == MODE_CONTIG_SWIGLU)
+            gemm_tiles<128, 256, 2, 4, 2, MODE, true, SF, true>(
+                p, 2 * tiles_m, tiles_n, wg - tail0, (int)gridDim.x - tail0, lds);
+        else
+            gemm_tiles<128, 128, 2, 4, 4, MODE, true, SF, true>(
+                p, 2 * tiles_m, 2 * tiles_n, wg - tail0, (int)gridDim.x - tail0, lds);
+    }
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -1607,31 +1615,36 @@ static hipError_t launch_cfg(int mode, const GemmArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-int64_t contig_tail_grid(const GemmArgs &a)
+int64_t contig_tail_grid(int mode, const GemmArgs &a)
 {
     const int tiles_m = (a.m + 255) / 256, tiles_n = (a.n + 255) / 256;
     const int64_t main_wgs =
-        (int64_t)tiles_m * tiles_n + straddle_wgs(MODE_CONTIG, 256, false, a, tiles_n);
-    return (main_wgs + 7) / 8 * 8 + workgroups((int64_t)4 * a.tail_max, true, a);
+        (int64_t)tiles_m * tiles_n + straddle_wgs(mode, 256, false, a, tiles_n);
+    return (main_wgs + 7) / 8 * 8 + workgroups((int64_t)tail_sub_tiles(mode) * a.tail_max, true, a);
 }
 
-hipError_t launch_contig_tail(const GemmArgs &a, hipStream_t stream)
+hipError_t launch_contig_tail(int mode, const GemmArgs &a, hipStream_t stream)
 {
     if (a.tail_cus <= 0 || a.tail_max <= 0 || a.tail_tm <= 0 || a.tail_tn <= 0 ||
-        (a.sf_fmt != SF_FP32 && a.sf_fmt != SF_UE8M0))
+        (mode != MODE_CONTIG && mode != MODE_CONTIG_SWIGLU) ||
+        (a.sf_fmt != SF_FP32 && (mode != MODE_CONTIG || a.sf_fmt != SF_UE8M0)))
         return hipErrorInvalidConfiguration;
     const int tiles_m = (a.m + 255) / 256, tiles_n = (a.n + 255) / 256;
     const int64_t main_wgs =
-        (int64_t)tiles_m * tiles_n + straddle_wgs(MODE_CONTIG, 256, false, a, tiles_n);
-    const int64_t grid = contig_tail_grid(a);
+        (int64_t)tiles_m * tiles_n + straddle_wgs(mode, 256, false, a, tiles_n);
+    const int64_t grid = contig_tail_grid(mode, a);
     if (tiles_m != a.tail_tm || tiles_n != a.tail_tn || grid <= 0 || grid > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    if (a.sf_fmt == SF_UE8M0)
-        hipLaunchKernelGGL(dg_gemm_contig_tail_kernel<SF_UE8M0>, dim3((unsigned)grid), dim3(512),
-                           0, stream, a, tiles_m, tiles_n, (int)main_wgs);
+    const dim3 g((unsigned)grid), b(512);
+    if (mode == MODE_CONTIG_SWIGLU)
+        hipLaunchKernelGGL((dg_gemm_contig_tail_kernel<MODE_CONTIG_SWIGLU, SF_FP32>), g, b, 0,
+                           stream, a, tiles_m, tiles_n, (int)main_wgs);
+    else if (a.sf_fmt == SF_UE8M0)
+        hipLaunchKernelGGL((dg_gemm_contig_tail_kernel<MODE_CONTIG, SF_UE8M0>), g, b, 0, stream,
+                           a, tiles_m, tiles_n, (int)main_wgs);
     else
-        hipLaunchKernelGGL(dg_gemm_contig_tail_kernel<SF_FP32>, dim3((unsigned)grid), dim3(512),
-                           0, stream, a, tiles_m, tiles_n, (int)main_wgs);
+        hipLaunchKernelGGL((dg_gemm_contig_tail_kernel<MODE_CONTIG, SF_FP32>), g, b, 0, stream, a,
+                           tiles_m, tiles_n, (int)main_wgs);
     return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ struct GemmArgs {
     // Contiguous tail.  With tail_cus > 0, the workgroups of 256 x 256 tiles leave the tiles
     // of the last-dispatched ones (the busy ones of their last partial wave over tail_cus CUs,
     // when they number between tail_cus / 8 and tail_cus / 4; tail_force of them, if set) to
-    // workgroups of 128 x 128 tiles in the same launch, which are given tail_tm x tail_tn, the
+    // workgroups of 128-row tiles in the same launch, which are given tail_tm x tail_tn, the
     // 256 x 256 tile grid, and at most tail_max of them.
     int tail_cus;
     int tail_force;
@@ -123,10 +123,10 @@ int64_t grid_size(int mode, int cfg, const GemmArgs &args);
 // Launches the kernel for (mode, cfg) on `stream`; returns the HIP error of the launch.
 hipError_t launch_gemm(int mode, int cfg, const GemmArgs &args, hipStream_t stream);
 
-// The contiguous form (MODE_CONTIG) with 256 x 256 tiles and its tail of 128 x 128 tiles in
-// one launch (the tail fields of args set): grid size, and the launch.
-int64_t contig_tail_grid(const GemmArgs &args);
-hipError_t launch_contig_tail(const GemmArgs &args, hipStream_t stream);
+// The contiguous form (MODE_CONTIG, or MODE_CONTIG_SWIGLU) with 256 x 256 tiles and its tail
+// of 128-row tiles in one launch (the tail fields of args set): grid size, and the launch.
+int64_t contig_tail_grid(int mode, const GemmArgs &args);
+hipError_t launch_contig_tail(int mode, const GemmArgs &args, hipStream_t stream);
 
 // The split-K streaming kernel (dense form only): grid size, the most K blocks one split may
 // hold, and the launch (rejects a split count that leaves a split empty or too long).

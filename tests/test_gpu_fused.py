@@ -99,6 +99,25 @@ def test_small_with_padding_and_empty_groups(cfg, served, i, k, counts, monkeypa
     check_fused(p, *run_fused(p), what=f"{cfg} i={i} k={k}")
 
 
+# The tail: the tiles of the last-dispatched 256 x 256 workgroups run as 128 x 256 tiles at the
+# end of the same launch (DG_TAIL_TILES forces how many; 9 is more than there are, so all but
+# one), straddles and a tile half past m_total among them, and with few tail workgroups (each
+# then walks several tiles)
+@pytest.mark.parametrize("tail,wgs", [("1", None), ("3", None), ("9", None), ("5", "2")])
+@pytest.mark.parametrize("served", [None, "1"])
+@pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
+def test_tail_in_128_row_tiles(tail, wgs, served, counts, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    monkeypatch.setenv("DG_TAIL_TILES", tail)
+    if wgs is not None:
+        monkeypatch.setenv("DG_PERSIST_WGS", wgs)
+    if served is not None:
+        monkeypatch.setenv("DG_STRADDLE_ROWS", served)
+    p = W.make_contiguous(5, sum(counts), 512, 640, seed=213, counts=counts, pad_nan=True,
+                          stress=True)
+    check_fused(p, *run_fused(p), what=f"tail {tail} wgs={wgs} served={served} {counts}")
+
+
 @pytest.mark.parametrize("wgs", ["3", "10"])
 @pytest.mark.parametrize("k", [256, 1280])
 def test_persistent_workgroups_walk_many_tiles(wgs, k, monkeypatch):
