@@ -304,11 +304,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             listed[c] = __ballot(la >= 0 && lb >= 0 && la != lb);
         }
     };
-    // tiles of a launch of `tiles` 256 x 256 tiles (tn256 across) left to the tail launch: the
-    // busy workgroups of its last partial wave over tail_cus CUs (every tile, and one workgroup
-    // per N tile for each served straddle) when they are between tail_cus / 8 and
-    // tail_cus / 4, else none; tail_force of them if set.  Needs scan_listed first where
-    // straddle_rows > 0.
+    // of `tiles` 256 x 256 tiles (tn256 across), those left to the tail: the busy workgroups of
+    // their last partial wave over tail_cus CUs (every tile, and one workgroup per N tile for
+    // each served straddle) when they are between tail_cus / 8 and tail_cus / 4, else none;
+    // tail_force of them if set.  Needs scan_listed first where straddle_rows > 0.
     auto tail_tiles = [&](int tiles, int tn256) {
         if (p.tail_force > 0)
             return min(p.tail_force, tiles - 1);
@@ -334,7 +333,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         }
     }
     if (TAIL_MAIN && p.tail_cus > 0 && bid >= 0) {
-        // (only the last workgroups can be left to the tail launch)
+        // (only the last workgroups can be left to the tail)
         const int cap = p.tail_force > 0 ? total : p.tail_cus / 4;
         if (bid >= total - cap) {
             if (p.straddle_rows > 0)
@@ -364,7 +363,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             return;  // fewer listed straddles than served slots
         tile_id = raster_index(t, tn, tiles_m, tiles_n);
         if (TAIL_MAIN && p.tail_cus > 0) {
-            // a tile left to the tail launch (its own workgroup is among the last ids)
+            // a tile left to the tail (its own workgroup is among the last ids)
             const int left = tail_tiles(total, tiles_n);
             if (left > 0 && xcd_tile_owner(total, E, tile_id) - E >= total - left)
                 return;
