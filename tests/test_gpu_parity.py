@@ -377,6 +377,23 @@ def test_contiguous_tail_launch(tail, served, counts, n, monkeypatch):
     assert not np.any(got[p.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_contiguous_tail_changes_no_bits(ue8m0, monkeypatch):
+    # the 128 x 128 tiles sum the same 16 x 16 x 128 MFMA partials in the same K order with the
+    # same promotion as the 256 x 256 tiles, so every tail count gives the plain launch's bits
+    monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
+    p = W.make_contiguous(6, 1500, 512, 640, seed=44, counts=[300, 0, 257, 1, 642, 300],
+                          stress=True, pad_nan=True, ue8m0=ue8m0)
+    monkeypatch.setenv("DG_TAIL_TILES", "0")
+    plain = run_contiguous(p)
+    ref = (oracle.m_grouped_contiguous_ue8m0 if ue8m0 else oracle.m_grouped_contiguous)(
+        p.a, p.sfa, p.b, p.sfb, p.m_indices)
+    assert_parity(plain, ref, "plain launch")
+    for t in ("1", "4", "13"):
+        monkeypatch.setenv("DG_TAIL_TILES", t)
+        assert np.array_equal(run_contiguous(p), plain), f"tail {t}"
+
+
 @pytest.mark.parametrize("wgs", ["1", "3"])
 def test_contiguous_tail_launch_with_few_workgroups(wgs, monkeypatch):
     # the tail launch's persistent workgroups each loop over several 128 x 128 tiles
