@@ -15,6 +15,7 @@
 
 #include "../../include/dg.h"
 #include "dg_internal.h"
+#include "dg_tiles.h"
 
 namespace {
 
@@ -225,11 +226,9 @@ int plan_contig_tail(dg::GemmArgs &args, int m_total, int n, int cus)
     if (force > 0) {
         tail_max = (int)(force < tiles - 1 ? force : tiles - 1);
     } else if (force < 0) {
-        for (int s = 0; s <= args.straddle_rows && tail_max == 0; ++s) {
-            const int64_t r = (tiles + (int64_t)s * tn) % cus;
-            if (8 * r >= cus && 4 * r <= cus && r < tiles)
+        for (int s = 0; s <= args.straddle_rows && tail_max == 0; ++s)
+            if (dg::tail_count(tiles + (int64_t)s * tn, tiles, cus) > 0)
                 tail_max = cus / 4;
-        }
     }
     if (tail_max > 0) {
         args.tail_cus = cus;

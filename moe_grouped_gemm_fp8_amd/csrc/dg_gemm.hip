@@ -318,8 +318,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 served += __builtin_popcountll(listed[c]);
             served = min(served, p.straddle_rows);
         }
-        const int r = (tiles + served * tn256) % p.tail_cus;
-        return (8 * r >= p.tail_cus && 4 * r <= p.tail_cus && r < tiles) ? r : 0;
+        return tail_count((int64_t)tiles + (int64_t)served * tn256, tiles, p.tail_cus);
     };
     int tail_n = 0;  // TAIL: the 256 x 256 tiles these workgroups cover
     if constexpr (TAIL) {

@@ -40,6 +40,18 @@ DG_HD inline TileRange xcd_tile_range(int64_t total, int grid, int lead, int id)
     return t;
 }
 
+// The contiguous forms' tail: of `tiles` 256 x 256 tiles whose launch keeps `busy` workgroups
+// busy (the tiles, plus one per N tile for each served straddle), the tiles left to 128-row
+// tiles at the end of the launch: the busy workgroups of the last partial wave over `cus` CUs
+// when they number between cus / 8 and cus / 4 (and fewer than the tiles), else none.
+DG_HD inline int tail_count(int64_t busy, int64_t tiles, int cus)
+{
+    if (cus <= 0)
+        return 0;
+    const int64_t r = busy % cus;
+    return (8 * r >= cus && 4 * r <= cus && r < tiles) ? (int)r : 0;
+}
+
 // The inverse for one workgroup per tile (total == grid - lead): the id of the workgroup that
 // xcd_tile_range gives tile `tile` to.  XCD x's range starts at w_x and its workgroups take
 // one tile each in id order, so the tile w_x + j falls to workgroup lead + 8 j + x.

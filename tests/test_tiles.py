@@ -51,3 +51,11 @@ def test_more_workgroups_than_tiles(tile_cover, lead):
     # sizes its grid for the most tiles it may get): the spare workgroups get no tile
     _run(tile_cover, [(t, g, lead) for g in (2, 8, 9, 256, 1000) for t in (1, 3, g - 1, g // 2 + 1)
                       if 0 < t < g])
+
+
+def test_tail_rule(tile_cover):
+    # the contiguous forms leave the busy workgroups of a last partial wave to 128-row tiles
+    # when they fill between an eighth and a quarter of the CUs; worked cases and the rule's
+    # properties over every CU count to 320 (the kernel and the host both use tail_count)
+    out = subprocess.run([tile_cover, "tail"], capture_output=True, text=True)
+    assert out.returncode == 0 and "ok tail" in out.stdout, out.stdout + out.stderr
