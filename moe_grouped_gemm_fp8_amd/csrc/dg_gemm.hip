@@ -438,7 +438,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
         if constexpr (MODE == MODE_MASKED) {
             raw_cnt = p.grp[u.g];
         } else if constexpr (CONTIG) {
-            // (rows past M: only a tile taller than the 128-row alignment, or a tail launch's
+            // (rows past M: only a tile taller than the 128-row alignment, or a tail
             // tile in the second half of a 256-row tile that ends past M, reaches them)
             constexpr bool PAST_M = TWO_GROUPS || TAIL;
 #pragma unroll
@@ -476,7 +476,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
                 }
                 u.g2 = __builtin_amdgcn_readfirstlane(wave_max(second));
             }
-            // (a tail launch's tile in the second half of a ragged last 256-column tile can
+            // (a tail tile in the second half of a ragged last 256-column tile can
             // start past N)
             u.empty = u.g < 0 || (TAIL && u.n0 >= N);
 #pragma unroll

@@ -355,8 +355,8 @@ def test_contiguous_256_row_tiles_unordered_groups(served, monkeypatch):
     assert not np.any(got[q.m_indices >= 0] == W.BF16_SENTINEL), "valid rows left unwritten"
 
 
-# The tail launch: the tiles of the last-dispatched workgroups of a 256 x 256 launch run as
-# 128 x 128 tiles in a second launch (DG_TAIL_TILES forces how many; 9 is more than the 8
+# The tail: the tiles of the last-dispatched workgroups of 256 x 256 tiles run as 128 x 128
+# tiles at the end of the same launch (DG_TAIL_TILES forces how many; 9 is more than the 8
 # tiles there are, so all but one).  Straddling tiles among them (their second group then no
 # longer served ahead), tiles whose second 128-row half lies past m_total, and a ragged last N
 # tile whose second 128-column half lies wholly past N (n = 272) or partly (n = 400).
@@ -396,7 +396,7 @@ def test_contiguous_tail_changes_no_bits(ue8m0, monkeypatch):
 
 @pytest.mark.parametrize("wgs", ["1", "3"])
 def test_contiguous_tail_launch_with_few_workgroups(wgs, monkeypatch):
-    # the tail launch's persistent workgroups each loop over several 128 x 128 tiles
+    # the tail's persistent workgroups each loop over several 128 x 128 tiles
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
     monkeypatch.setenv("DG_TAIL_TILES", "6")
     monkeypatch.setenv("DG_PERSIST_WGS", wgs)
@@ -410,7 +410,7 @@ def test_contiguous_tail_launch_with_few_workgroups(wgs, monkeypatch):
 
 def test_contiguous_tail_launch_chosen_by_the_wave(monkeypatch, capfd):
     # 19 x 16 = 304 tiles of 256 x 256 and one group: on 256 CUs the last partial wave holds
-    # 48 tiles (between an eighth and a quarter of the CUs), which go to the tail launch
+    # 48 tiles (between an eighth and a quarter of the CUs), which go to the tail
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
     monkeypatch.setenv("DG_PRINT_CONFIGS", "1")
     p = W.make_contiguous(1, 4864, 4096, 256, seed=40, counts=[4864])

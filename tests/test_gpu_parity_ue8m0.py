@@ -156,7 +156,7 @@ def test_contiguous_256_row_tiles_across_group_boundaries(counts, monkeypatch):
 @pytest.mark.parametrize("counts", [[0, 130, 41, 300, 129], [41, 0, 300, 1, 130]])
 def test_contiguous_tail_launch(tail, counts, monkeypatch):
     # the tiles of the last-dispatched workgroups of the 256 x 256 launch as 128 x 128 tiles in
-    # a second launch, straddles and a tile half past m_total among them
+    # the same launch, straddles and a tile half past m_total among them
     monkeypatch.setenv("DG_FORCE_CONFIG", "256x256w8")
     monkeypatch.setenv("DG_TAIL_TILES", tail)
     p = W.make_contiguous(5, sum(counts), 400, 640, seed=62, counts=counts, stress=True,

@@ -2,7 +2,7 @@
 every tile id is assigned to exactly one workgroup, for persistent grids (fewer workgroups
 than tiles), one workgroup per tile (up to 75008 tiles, where 32-bit products of the tile
 count and the grid would wrap), and with straddle-serving workgroups ahead of the tiles; with
-one workgroup per tile, the inverse (``xcd_tile_owner``, which the contiguous tail launch uses
+one workgroup per tile, the inverse (``xcd_tile_owner``, which the contiguous tail uses
 to find the tiles of the workgroups dispatched last) names the workgroup of every tile.
 CPU only: the header is plain C++ and is compiled here with g++."""
 import os
@@ -47,7 +47,7 @@ def test_persistent_workgroups(tile_cover, lead):
 
 @pytest.mark.parametrize("lead", [0, 8])
 def test_more_workgroups_than_tiles(tile_cover, lead):
-    # a persistent grid sized for more tiles than a launch finds (the contiguous tail launch
+    # a persistent grid sized for more tiles than a launch finds (the contiguous tail
     # sizes its grid for the most tiles it may get): the spare workgroups get no tile
     _run(tile_cover, [(t, g, lead) for g in (2, 8, 9, 256, 1000) for t in (1, 3, g - 1, g // 2 + 1)
                       if 0 < t < g])
