@@ -106,7 +106,7 @@ struct LayoutArgs {
 };
 
 int64_t layout_grid_size(int layout, const LayoutArgs &args);
-// y[c][r] = x[r][c] for e4m3 bytes (rows % 64 == 0, cols % 16 == 0), for up to two operands
+// y[c][r] = x[r][c] for e4m3 bytes (rows % 128 == 0, cols % 16 == 0), for up to two operands
 // in one launch (a job with a null x is skipped)
 hipError_t launch_transpose_u8(const void *x0, void *y0, int rows0, int cols0, const void *x1,
                                void *y1, int rows1, int cols1, hipStream_t stream);

@@ -552,11 +552,14 @@ hipError_t launch_layout(int layout, const LayoutArgs &a, hipStream_t stream)
 
 // ---- byte transpose y[c][r] = x[r][c] (x: rows x cols, pitch cols; y: cols x rows, pitch
 // rows) of e4m3 operands, for the dense NN/TN/TT calls: their MN-major operands become
-// K-major, which the NT kernels take.  rows % 64 == 0 and cols % 16 == 0.  A workgroup moves
-// one 64 x 64 byte tile: 16-byte loads into a padded LDS tile (80-byte rows), then
-// ds_read_b64_tr_b8, whose 16-lane groups turn an 8 x 16 byte block into 16 lanes of 8
-// consecutive row bytes; two such reads give a lane 16 bytes, and wave w writes output rows
-// 16 w .. 16 w + 15, their whole 64 bytes, in one 16-byte store per lane.
+// K-major, which the NT kernels take.  rows % 128 == 0 and cols % 16 == 0.  A workgroup moves
+// one 128 x 128 byte tile: 16-byte loads of whole 128-byte row segments into a padded LDS
+// tile (144-byte rows), then ds_read_b64_tr_b8, whose 16-lane groups turn an 8 x 16 byte
+// block into 16 lanes of 8 consecutive row bytes; two such reads give a lane 16 bytes of one
+// output row.  Wave w writes output rows 32 w .. 32 w + 31, each row's 128 bytes as two
+// 64-byte halves in consecutive rounds.  So every 128-byte line of x and of y is read or
+// written by one workgroup: workgroups are dealt round-robin over the XCDs, whose L2s are
+// separate, and a line split between two workgroups is fetched twice.
 // One launch moves up to two operands (A and B of the TN layout): workgroups [0, p0.tiles)
 // transpose p0, the rest p1.
 struct U8Transpose {
@@ -565,10 +568,12 @@ struct U8Transpose {
     int rows, cols, tiles_c, tiles;
 };
 
+constexpr int TR_T = 128;  // tile side in bytes
+
 __global__ __launch_bounds__(256) void dg_transpose_u8_kernel(U8Transpose p0, U8Transpose p1)
 {
-    constexpr int PITCH = 80;
-    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
+    constexpr int PITCH = TR_T + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TR_T * PITCH];
     const bool second = (int)blockIdx.x >= p0.tiles;
     const int bid = (int)blockIdx.x - (second ? p0.tiles : 0);
     const uint8_t *__restrict__ x = second ? p1.x : p0.x;
@@ -576,29 +581,38 @@ __global__ __launch_bounds__(256) void dg_transpose_u8_kernel(U8Transpose p0, U8
     const int rows = second ? p1.rows : p0.rows, cols = second ? p1.cols : p0.cols;
     const int tiles_c = second ? p1.tiles_c : p0.tiles_c;
     const int tid = threadIdx.x;
-    const int r0 = (bid / tiles_c) * 64, c0 = (bid % tiles_c) * 64;
-    {
-        const int r = tid >> 2, c = (tid & 3) * 16;
-        uint4 v = make_uint4(0, 0, 0, 0);
+    const int r0 = (bid / tiles_c) * TR_T, c0 = (bid % tiles_c) * TR_T;
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // rows 32 q + tid / 8, 16-byte chunk tid % 8
+        const int r = 32 * q + (tid >> 3), c = (tid & 7) * 16;
+        v[q] = make_uint4(0, 0, 0, 0);
         if (c0 + c < cols)
-            v = *reinterpret_cast<const uint4 *>(x + (int64_t)(r0 + r) * cols + c0 + c);
-        *reinterpret_cast<uint4 *>(tile + r * PITCH + c) = v;
+            v[q] = *reinterpret_cast<const uint4 *>(x + (int64_t)(r0 + r) * cols + c0 + c);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4 *>(tile + (32 * q + (tid >> 3)) * PITCH + (tid & 7) * 16) = v[q];
     __syncthreads();
     const uint32_t base = (uint32_t)(uintptr_t)(DG_LDS uint8_t *)tile;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
-    // lane group g: tile rows 16 g .. 16 g + 15 (two transposing reads of 8 rows), so lane j
-    // holds 16 consecutive bytes of output row c0 + 16 w + j
-    const uint32_t addr = base + (uint32_t)((16 * g + (j >> 1)) * PITCH + 16 * w + 8 * (j & 1));
-    v2i lo = lds_read_tr8_at<0>(addr);
-    v2i hi = lds_read_tr8_at<8 * PITCH>(addr);
-    lds_wait();
-    tie(lo);
-    tie(hi);
-    const int c = c0 + 16 * w + j;  // output row
-    if (c < cols)
-        *reinterpret_cast<uint4 *>(y + (int64_t)c * rows + r0 + 16 * g) =
-            make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // 16-column block cb of the tile, 16-row chunk rc: lane j holds 16 consecutive bytes of
+        // output row c0 + 16 cb + j (the four lane groups: four consecutive chunks)
+        const int cb = 2 * w + (q >> 1), rc = 4 * (q & 1) + g;
+        const uint32_t addr =
+            base + (uint32_t)((16 * rc + (j >> 1)) * PITCH + 16 * cb + 8 * (j & 1));
+        v2i lo = lds_read_tr8_at<0>(addr);
+        v2i hi = lds_read_tr8_at<8 * PITCH>(addr);
+        lds_wait();
+        tie(lo);
+        tie(hi);
+        const int c = c0 + 16 * cb + j;  // output row
+        if (c < cols)
+            *reinterpret_cast<uint4 *>(y + (int64_t)c * rows + r0 + 16 * rc) =
+                make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y);
+    }
 }
 
 hipError_t launch_transpose_u8(const void *x0, void *y0, int rows0, int cols0, const void *x1,
@@ -610,10 +624,10 @@ hipError_t launch_transpose_u8(const void *x0, void *y0, int rows0, int cols0, c
     for (U8Transpose &t : p) {
         if (!t.x || t.rows <= 0 || t.cols <= 0)
             continue;  // no job
-        if (t.rows % 64 != 0 || t.cols % 16 != 0)
+        if (t.rows % TR_T != 0 || t.cols % 16 != 0)
             return hipErrorInvalidValue;
-        t.tiles_c = (t.cols + 63) / 64;
-        const int64_t tiles = (int64_t)(t.rows / 64) * t.tiles_c;
+        t.tiles_c = (t.cols + TR_T - 1) / TR_T;
+        const int64_t tiles = (int64_t)(t.rows / TR_T) * t.tiles_c;
         if (tiles > 0x3fffffff)
             return hipErrorInvalidConfiguration;
         t.tiles = (int)tiles;
