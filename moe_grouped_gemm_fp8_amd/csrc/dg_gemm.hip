@@ -394,6 +394,30 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     int raw_row[SM];
     const int fr = lane & 15;
     const int fg = lane >> 4;
+    // Masked form, up to 64 groups: the groups' tiles in an order that pairs the group with
+    // the most valid rows with the one with the fewest, the second with the second last, and
+    // so on.  Consecutive groups go to the same XCD (two per XCD at 16 groups), and a tile's
+    // time grows with its group's rows: in group order, the XCD that draws two large groups
+    // sets the launch's time.  Lane l holds masked_m of group l (clamped) and that group's
+    // rank (descending, ties by index), from one load per launch; the order changes with
+    // masked_m on the device, so graph replays follow it.
+    constexpr bool MASK_ORDER = MODE == MODE_MASKED;
+    int mcnt = 0, mrank = 0;
+    const bool ordered = MASK_ORDER && p.num_groups <= 64;
+    if constexpr (MASK_ORDER) {
+        if (ordered) {
+            const int G = p.num_groups;
+            int v = lane < G ? p.grp[lane] : -1;
+            v = lane < G ? (v < 0 ? 0 : (v > M ? M : v)) : -1;
+            int rk = 0;
+            for (int k = 0; k < G; ++k) {
+                const int vk = __shfl(v, k);
+                rk += (vk > v || (vk == v && k < lane)) ? 1 : 0;
+            }
+            mcnt = v;
+            mrank = rk;
+        }
+    }
     auto coords = [&](int t, int &tm, int &tn, int &g) {
         if constexpr (MODE == MODE_MASKED) {
             const int per_g = tiles_m * tiles_n;
@@ -401,6 +425,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
             const int rem = t - g * per_g;
             tn = rem / tiles_m;
             tm = rem - tn * tiles_m;
+            if (ordered) {
+                // slot g: ranks 0, G - 1, 1, G - 2, ...
+                const int r = (g & 1) ? p.num_groups - 1 - (g >> 1) : g >> 1;
+                const uint64_t at = __ballot(lane < p.num_groups && mrank == r);
+                g = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(at));
+            }
         } else {
             if (TAIL && tail_n > 0) {
                 // tile q of the 256 x 256 tile of the 256 x 256 workgroup tiles - tail_n + u
@@ -436,7 +466,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs &p, int tiles_m, int t
     };
     auto load_meta = [&](const Tile &u) {
         if constexpr (MODE == MODE_MASKED) {
-            raw_cnt = p.grp[u.g];
+            raw_cnt = ordered ? __builtin_amdgcn_readlane(mcnt, u.g) : p.grp[u.g];
         } else if constexpr (CONTIG) {
             // (rows past M: only a tile taller than the 128-row alignment, or a tail
             // tile in the second half of a 256-row tile that ends past M, reaches them)
