@@ -503,6 +503,21 @@ def test_masked_ragged_m_max_and_n():
     assert_parity(run_masked(p), ref, "masked ragged")
 
 
+# The kernel takes up to 64 groups in an order ranked by masked_m on the device (largest,
+# smallest, second largest, ...); ties keep the group order.  64 groups with many ties, 65
+# groups (group order), and every tile config, each group's rows written from its own B.
+@pytest.mark.parametrize("groups", [64, 65])
+@pytest.mark.parametrize("cfg", [None, "128x128w4", "256x128w8p", "256x256w8"])
+def test_masked_group_order(groups, cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    rng = np.random.default_rng(46 + groups)
+    mm = rng.choice([0, 1, 17, 64, 128, 128, 200, 256, 300], size=groups).tolist()
+    p = W.make_masked(groups, 256, 256, 128, seed=47, masked_m=mm, stress=True, tail_nan=True)
+    ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    assert_parity(run_masked(p), ref, f"masked {groups} groups {cfg}")
+
+
 def test_masked_all_zero_writes_nothing():
     p = W.make_masked(4, 64, 128, 256, seed=43, masked_m=[0, 0, 0, 0])
     assert np.all(run_masked(p) == W.BF16_SENTINEL)
