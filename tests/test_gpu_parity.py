@@ -505,7 +505,12 @@ def test_masked_ragged_m_max_and_n():
 
 # The kernel takes up to 64 groups in an order ranked by masked_m on the device (largest,
 # smallest, second largest, ...); ties keep the group order.  64 groups with many ties, 65
-# groups (group order), and every tile config, each group's rows written from its own B.
+# groups (group order), and every tile config, each group's rows written from its own B (a
+# row computed with another group's B, drawn independently, is wrong throughout).  Plain
+# N(0,1) inputs: with the per-segment 2^+-8 stress multipliers over 2.2 M outputs of one
+# K block, one element's block sum cancels 7900:1 (158.75 of terms whose magnitudes sum to
+# 1.25e6), and the FP8 MFMA's accumulation error there, 7 code units (5.6e-6 of that
+# magnitude sum), exceeds 1e-2 of the result; the stress tests elsewhere keep fewer outputs.
 @pytest.mark.parametrize("groups", [64, 65])
 @pytest.mark.parametrize("cfg", [None, "128x128w4", "256x128w8p", "256x256w8"])
 def test_masked_group_order(groups, cfg, monkeypatch):
@@ -513,7 +518,7 @@ def test_masked_group_order(groups, cfg, monkeypatch):
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     rng = np.random.default_rng(46 + groups)
     mm = rng.choice([0, 1, 17, 64, 128, 128, 200, 256, 300], size=groups).tolist()
-    p = W.make_masked(groups, 256, 256, 128, seed=47, masked_m=mm, stress=True, tail_nan=True)
+    p = W.make_masked(groups, 256, 256, 128, seed=47, masked_m=mm, tail_nan=True)
     ref = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
     assert_parity(run_masked(p), ref, f"masked {groups} groups {cfg}")
 
